@@ -1,0 +1,246 @@
+"""CPU oracle of one X-MoD sparse-depth layer and of a dense layer (test infrastructure only).
+
+Plain float64 NumPy written from the pages; see oracle/__init__.py for who may use it.
+
+Sources (cited by page title and section / equation):
+  [XMOD] "X-MoD: Practical Scaling Laws for Sparse-Depth Routing Beyond Mixture-of-Depths",
+         close-reading page. Sections "X-MoD: decoupling token sparsity K and anchor stride A"
+         (Eqs. (3)-(5), Fig. 1(b)), "three stabilisers" (Eqs. (6)-(8)), "training-time top-k",
+         "backbone configuration" (Table 4), "mechanism controls" (Table 7).
+  [MOD]  "Mixture-of-Depths explained" blog page, section "basic architecture" (the MoDLayer
+         sketch: scalar Linear(d, 1) router, top-k of int(T * ratio) tokens, RMSNorm before
+         attention and before the FFN, skipped rows passed through).
+  [MOE]  "Beyond dense Transformers: MoE, SSMs and hybrids" page, section on stored versus
+         evaluated parameters (bias-free SwiGLU with gate, value and down projections).
+  [MODA] "Mixture-of-Depths Attention" reading notes, section 2.1 (GQA: query head h reads
+         key/value head ceil(h/G), 1-based, G = Hq/Hkv).
+
+Readings taken where the pages are silent or ambiguous (all listed in the design doc):
+  * ell = s - tau*b, with the gate r = sigmoid(ell) taken from the biased logit (Eq. (8)).
+  * Selection ranks fp32 ell, ties to the lower position; -0 equals +0. k = floor(T/K).
+  * Selected rows are packed in ascending position; attention is causal over the selected
+    subset only, per sequence (Table 7: KV context "selected subset").
+  * FFN input is RMSNorm(X + a) (sequential pre-norm); output y = X + varsigma*r*(a + f).
+  * The bias update b[S] += delta happens after the gate is read.
+  * Softmax scale 1/sqrt(head_dim); GQA head h uses KV head floor(h*Hkv/Hq) (0-based).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import bf16_to_f64
+
+
+def _f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    return a.astype(np.float64)
+
+
+# --- router: [MOD] "basic architecture" (Linear(d, 1) score), [XMOD] Eq. (8) -------------------
+
+def router_logits(x, w_router, router_bias=0.0, bias=None, tau=1.0):
+    """Router logit s_t = w_r . x_t + beta_r and bias-adjusted logit ell_t = s_t - tau * b_t.
+
+    The dot product is taken in float64 and rounded once to fp32 ("the oracle's logit"). The
+    adjustment is fp32 arithmetic: tau*b rounded, then the subtraction rounded ([XMOD] Eq. (8)
+    subtracts tau*b_i before the top-1/K choice). Returns (s, ell), both float32 [B, T].
+    """
+    x = _f64(x)
+    w = _f64(w_router)
+    s = (x @ w + float(router_bias)).astype(np.float32)
+    if bias is None:
+        bias = np.zeros(s.shape, dtype=np.float32)
+    tb = np.float32(tau) * np.asarray(bias, dtype=np.float32)
+    ell = (s - tb).astype(np.float32)
+    return s, ell
+
+
+# --- selection: [XMOD] "training-time top-k", [MOD] "basic architecture" -----------------------
+
+def topk_select(ell, k):
+    """Per sequence, the k tokens with the largest fp32 ell; equal values go to the lower index.
+
+    Returns idx int64 [B, k] in ascending position order. [XMOD] Eq. (1): a Sparse(K) layer
+    processes only the top-1/K share of tokens; the ordering among equal logits is not fixed by
+    the pages and is taken as lower position first.
+    """
+    ell = np.asarray(ell, dtype=np.float32)
+    assert np.all(np.isfinite(ell)), "router logits must be finite"
+    B, T = ell.shape
+    assert 1 <= k <= T
+    out = np.empty((B, k), dtype=np.int64)
+    pos = np.arange(T)
+    for b in range(B):
+        # Primary key: -ell ascending (ell descending); secondary: position ascending.
+        order = np.lexsort((pos, -ell[b].astype(np.float64)))
+        out[b] = np.sort(order[:k])
+    return out
+
+
+def sigmoid(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+# --- layer pieces ------------------------------------------------------------------------------
+
+def rmsnorm(X, gain, eps):
+    """RMSNorm over the last axis: X / sqrt(mean(X^2) + eps) * gain ([MOD] norm1/norm2)."""
+    X = np.asarray(X, dtype=np.float64)
+    ms = np.mean(X * X, axis=-1, keepdims=True)
+    return X / np.sqrt(ms + float(eps)) * _f64(gain)
+
+
+def causal_attention(Q, Kt, Vt, q_pos, n_q_heads, n_kv_heads, head_dim):
+    """Causal multi-head attention with grouped KV heads, over one packed sequence.
+
+    Q: [n, Hq*hd] rows for queries at packed positions q_pos; Kt, Vt: [m, Hkv*hd] for packed
+    positions 0..m-1. Query i sees keys j <= q_pos[i]. Head h reads KV head floor(h*Hkv/Hq)
+    ([MODA] section 2.1, 0-based). Scores scaled by 1/sqrt(hd), softmax over visible keys.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    Kt = np.asarray(Kt, dtype=np.float64)
+    Vt = np.asarray(Vt, dtype=np.float64)
+    q_pos = np.asarray(q_pos)
+    n, m = Q.shape[0], Kt.shape[0]
+    assert np.all(q_pos < m)
+    visible = np.arange(m)[None, :] <= q_pos[:, None]          # [n, m]
+    out = np.empty((n, n_q_heads * head_dim), dtype=np.float64)
+    scale = 1.0 / np.sqrt(head_dim)
+    for h in range(n_q_heads):
+        g = (h * n_kv_heads) // n_q_heads
+        q = Q[:, h * head_dim:(h + 1) * head_dim]
+        kk = Kt[:, g * head_dim:(g + 1) * head_dim]
+        vv = Vt[:, g * head_dim:(g + 1) * head_dim]
+        S = (q @ kk.T) * scale
+        S = np.where(visible, S, -np.inf)
+        S = S - np.max(S, axis=1, keepdims=True)
+        P = np.exp(S)
+        P = P / np.sum(P, axis=1, keepdims=True)
+        out[:, h * head_dim:(h + 1) * head_dim] = P @ vv
+    return out
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z * sigmoid(z)
+
+
+def swiglu_ffn(v, w_gate, w_up, w_down):
+    """Bias-free SwiGLU: (SiLU(v Wg^T) * (v Wu^T)) Wd^T ([MOE] gate, value and down projections)."""
+    return (silu(v @ _f64(w_gate).T) * (v @ _f64(w_up).T)) @ _f64(w_down).T
+
+
+def _attn_ffn_on_rows(X, lay, dims, out_rows):
+    """Attention residual a and FFN residual f for rows out_rows of one packed sequence X.
+
+    u = RMSNorm(X; g_attn); [Q|K|V] = u W_qkv^T; O = causal attention over X's rows;
+    a = O W_o^T; v = RMSNorm(X + a; g_ffn); f = SwiGLU(v). Only rows 0..max(out_rows) of X
+    are needed (causality), so only those are projected to keys and values.
+    """
+    out_rows = np.asarray(out_rows)
+    m = int(out_rows.max()) + 1
+    Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    dq, dkv = Hq * hd, Hkv * hd
+    Wqkv = _f64(lay["w_qkv"])
+    u = rmsnorm(X[:m], lay["g_attn"], dims.rms_eps)
+    Q = u[out_rows] @ Wqkv[:dq].T
+    Kt = u @ Wqkv[dq:dq + dkv].T
+    Vt = u @ Wqkv[dq + dkv:dq + 2 * dkv].T
+    O = causal_attention(Q, Kt, Vt, out_rows, Hq, Hkv, hd)
+    a = O @ _f64(lay["w_o"]).T
+    v = rmsnorm(X[out_rows] + a, lay["g_ffn"], dims.rms_eps)
+    f = swiglu_ffn(v, lay["w_gate"], lay["w_up"], lay["w_down"])
+    return a, f
+
+
+# --- the Sparse(K) layer: [XMOD] Fig. 1(b), Eqs. (7)-(8) ---------------------------------------
+
+def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None, sample=None):
+    """Forward of one X-MoD Sparse(K) layer.
+
+    x: [B, T, d] bf16 bits or float64 values. lay: dict of layer weights (bf16 bits) plus
+    "router_bias" and "varsigma". bias: fp32 [B, T] carried bias or None (zeros).
+
+    Steps: router logit and bias adjustment (Eq. (8)); per sequence top-k with k = floor(T/K);
+    gate r = sigmoid(ell) on the selected tokens; attention and FFN over the packed selected
+    rows only; y_S = X + varsigma * r * (a + f) (Eq. (7)); unselected rows y = x (Fig. 1(b),
+    skip path); then b[S] += delta in fp32 (the bias grows when a token is chosen).
+
+    sample: None for the whole output, or {b: packed rows} to evaluate only those rows of those
+    sequences (each output row is computed exactly as in the full evaluation).
+
+    Returns a dict with s, ell (fp32), idx (int64 [B, k]), gate (float64 [B, k]), bias_out
+    (fp32), and either y (float64 [B, T, d]) or rows {b: (packed rows, positions, y rows)}.
+    """
+    x = _f64(x)
+    B, T, d = x.shape
+    k = T // K
+    assert k >= 1, "floor(T/K) must be at least 1"
+    if bias is None:
+        bias = np.zeros((B, T), dtype=np.float32)
+    bias = np.asarray(bias, dtype=np.float32)
+    s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
+    idx = topk_select(ell, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
+    bsel = np.arange(B)[:, None]
+    gate = sigmoid(ell[bsel, idx])
+    bias_out = bias.copy()
+    bias_out[bsel, idx] = (bias[bsel, idx] + np.float32(delta)).astype(np.float32)
+    vs = float(lay.get("varsigma", 1.0))
+
+    res = {"s": s, "ell": ell, "idx": idx, "gate": gate, "bias_out": bias_out}
+    seqs = range(B) if sample is None else sorted(sample)
+    if sample is None:
+        y = x.copy()
+    else:
+        rows = {}
+    for b in seqs:
+        X = x[b, idx[b]]                                       # packed, ascending position
+        out_rows = np.arange(k) if sample is None else np.asarray(sample[b])
+        a, f = _attn_ffn_on_rows(X, lay, dims, out_rows)
+        y_sel = X[out_rows] + (vs * gate[b, out_rows])[:, None] * (a + f)
+        if sample is None:
+            y[b, idx[b]] = y_sel
+        else:
+            rows[b] = (out_rows, idx[b, out_rows], y_sel)
+    if sample is None:
+        res["y"] = y
+    else:
+        res["rows"] = rows
+    return res
+
+
+# --- the dense layer: every token enters, no gate ---------------------------------------------
+
+def dense_layer(x, lay, dims, sample=None):
+    """Pre-norm dense layer over whole sequences: y = x + a + f.
+
+    a = Attn(RMSNorm(x)) causal over all T positions; f = SwiGLU(RMSNorm(x + a)). This is the
+    [Dense] layer of the stack in [XMOD] Eq. (3). Written independently of the routed path:
+    it never gathers, scatters or gates. sample: None or {b: positions}.
+    """
+    x = _f64(x)
+    B, T, d = x.shape
+    Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    dq, dkv = Hq * hd, Hkv * hd
+    Wqkv = _f64(lay["w_qkv"])
+    Wo = _f64(lay["w_o"])
+    out = x.copy() if sample is None else {}
+    for b in (range(B) if sample is None else sorted(sample)):
+        rows = np.arange(T) if sample is None else np.asarray(sample[b])
+        m = int(rows.max()) + 1
+        u = rmsnorm(x[b, :m], lay["g_attn"], dims.rms_eps)
+        Q = u[rows] @ Wqkv[:dq].T
+        Kt = u @ Wqkv[dq:dq + dkv].T
+        Vt = u @ Wqkv[dq + dkv:].T
+        a = causal_attention(Q, Kt, Vt, rows, Hq, Hkv, hd) @ Wo.T
+        h = x[b, rows] + a
+        f = swiglu_ffn(rmsnorm(h, lay["g_ffn"], dims.rms_eps), lay["w_gate"], lay["w_up"], lay["w_down"])
+        y = x[b, rows] + a + f
+        if sample is None:
+            out[b] = y
+        else:
+            out[b] = (rows, y)
+    return out
