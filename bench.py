@@ -1,0 +1,188 @@
+"""Throughput of one X-MoD Sparse(K) layer forward on one MI355X.
+
+Workload: the single Sparse(K=8) layer at B=8 x T=4096, d=2048, 16 heads x 128, SwiGLU hidden
+5632, bf16; 512 of 4096 tokens per sequence are routed (4096 routed rows per step). Weights
+N(0, 0.02), activations N(0, 1), carried bias N(0, 0.1), varsigma ~ U(0.5, 1.5), all seeded and
+synthetic. A step is one xmod_sparse_layer_fwd call (router, top-k, gather + RMSNorm, QKV GEMM,
+attention over the routed subset, O GEMM, residual + RMSNorm, gate/up GEMM with SwiGLU, down GEMM
+with the gated scatter back into x). Inputs are resident in HBM before timing starts; each step
+updates x and the carried bias in place, so consecutive steps act like a stack of layers that
+share weights (same shapes, same work per step).
+
+Prints one JSON line: routed tokens/s, the roofline of the dominant kernel (HIP events around
+each kernel of the timed steps), and the CPU oracle timed on a bounded sample on this host.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workload as wl  # noqa: E402
+
+METRIC = "routed tokens/s per sparse layer (bf16, 1 GPU); % MFMA peak; route/pack GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def algorithmic_work(w):
+    """Per-step algorithmic FLOPs and bytes of each kernel (what the method must do)."""
+    B, T, d, k = w.B, w.T, w.d, w.k
+    M = B * k
+    dq, dkv, F = w.d_q, w.d_kv, w.ffn_hidden
+    nqkv = dq + 2 * dkv
+    att_flops = 2.0 * B * w.n_q_heads * w.head_dim * k * (k + 1)   # causal QK^T and PV
+    return {
+        "router": {"bytes": 2.0 * B * T * d + 2 * d + 8.0 * B * T, "flops": 2.0 * B * T * d},
+        "topk": {"bytes": 4.0 * B * T + 8.0 * M + 8.0 * M, "flops": 0.0},
+        "gather_rmsnorm": {"bytes": 4.0 * M * d, "flops": 3.0 * M * d},
+        "qkv_gemm": {"flops": 2.0 * M * d * nqkv, "bytes": 2.0 * (M * d + nqkv * d + M * nqkv)},
+        "attention": {"flops": att_flops, "bytes": 2.0 * (M * nqkv + M * dq)},
+        "o_gemm": {"flops": 2.0 * M * dq * d, "bytes": 2.0 * (M * dq + d * dq + M * d)},
+        "residual_rmsnorm": {"bytes": 6.0 * M * d, "flops": 4.0 * M * d},
+        "gateup_swiglu_gemm": {"flops": 4.0 * M * d * F, "bytes": 2.0 * (M * d + 2 * F * d + M * F)},
+        "down_scatter_gemm": {"flops": 2.0 * M * F * d, "bytes": 2.0 * (M * F + d * F + 3 * M * d)},
+    }
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle (float64 NumPy) on a bounded sample of the same workload on this host."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    t0 = time.perf_counter()
+    oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
+                        sample={0: np.arange(w.k)})
+    t1 = time.perf_counter() - t0
+    n_seq = int(max(1, min(w.B, budget_s // max(t1, 1e-3))))
+    if n_seq > 1:
+        t0 = time.perf_counter()
+        oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
+                            sample={b: np.arange(w.k) for b in range(n_seq)})
+        t1 = time.perf_counter() - t0
+    routed = n_seq * w.k
+    return {"value": routed / t1, "unit": "routed tokens/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(t1, 3),
+            "sample": f"{n_seq} of {w.B} sequences (router and top-k over all {w.B}; attention and "
+                      f"FFN over the {w.k} routed tokens of each sampled sequence), float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_depth_token_amd import xmod
+
+    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    dev = "cuda"
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    dl = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in lay.items()}
+    L = xmod.make_layer(dl)
+    dims = xmod.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden,
+                          w.rms_eps)
+    x = up(xb)
+    bias = torch.from_numpy(wl.make_bias(w)).to(dev)
+    ws = xmod.alloc_workspace(dims, w.K, xmod.WS_SPARSE_LAYER)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        xmod.sparse_layer_fwd(x, L, dims, w.K, bias, w.tau, w.delta, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel events recorded by the library on the same stream
+    xmod.phase_timing(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    phase_ms, n_calls = xmod.phase_times()
+    xmod.phase_timing(False)
+    assert n_calls == args.steps
+    assert torch.isfinite(x.float()).all().item(), "non-finite hidden state"
+
+    ms_per_step = total_ms / args.steps
+    M = w.B * w.k
+    value = M / (ms_per_step * 1e-3)
+
+    work = algorithmic_work(w)
+    phases = {}
+    for name, ms in phase_ms.items():
+        avg = ms / args.steps
+        e = {"ms": round(avg, 5)}
+        if work[name]["flops"] > 0 and name.endswith(("gemm", "attention")):
+            e["tflops"] = round(work[name]["flops"] / (avg * 1e-3) / 1e12, 1)
+            e["frac_mfma_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        else:
+            e["gbs"] = round(work[name]["bytes"] / (avg * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        phases[name] = e
+    dom = max(phase_ms, key=phase_ms.get)
+    dom_avg_s = phase_ms[dom] / args.steps * 1e-3
+    if dom.endswith(("gemm", "attention")):
+        achieved = work[dom]["flops"] / dom_avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = work[dom]["bytes"] / dom_avg_s / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None}
+    layer_flops = sum(v["flops"] for k2, v in work.items())
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "routed tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "d": w.d, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_hidden": w.ffn_hidden,
+                   "K": w.K, "routed_tokens_per_step": M, "parallelism": "none (1 GPU)"},
+        "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "layer_frac_mfma_peak": round(layer_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+        "phases": phases,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * xmod.h - C ABI of the X-MoD sparse-depth layer forward on AMD MI355X (gfx950).
+ *
+ * What is computed (sources are cited by page title and section / equation):
+ *   [XMOD] "X-MoD: Practical Scaling Laws for Sparse-Depth Routing Beyond Mixture-of-Depths"
+ *          (close-reading page): Fig. 1(b) and Eq. (7) (gated residual of a sparse layer),
+ *          Eq. (8) (router logit adjusted by a carried per-token bias), section "training-time
+ *          top-k" (non-causal top-1/K selection per sequence), Eq. (3) (the stack
+ *          [Dense]xN0 + ([Sparse(K)]xAK + [Dense])xN1 and the bias reset at each anchor),
+ *          Table 7 (a sparse layer attends over the selected subset only).
+ *   [MOD]  "Mixture-of-Depths explained" (blog page), section "basic architecture": scalar
+ *          Linear(d, 1) router, top-k of floor(T * capacity) tokens, RMSNorm before attention
+ *          and before the FFN, unselected rows passed through.
+ *   [MOE]  "Beyond dense Transformers: MoE, SSMs and hybrids", bias-free SwiGLU FFN.
+ *   [MODA] "Mixture-of-Depths Attention" reading notes, section 2.1: GQA head mapping.
+ *
+ * One Sparse(K) layer, per sequence b of length T:
+ *   s_t   = w_r . x_t + beta_r                      (fp32 accumulate)
+ *   ell_t = s_t - tau * b_t                          (fp32, product rounded then difference)
+ *   S     = the k = floor(T/K) largest ell, ties to the lower position, packed ascending
+ *   r     = sigmoid(ell_S)                           (uses b before this layer's update)
+ *   X = x_S;  u = RMSNorm(X; g_attn);  [Q|K|V] = u W_qkv^T
+ *   O     = causal softmax(Q K^T / sqrt(hd)) V over the packed rows; query head h reads
+ *           KV head floor(h * Hkv / Hq)
+ *   a = O W_o^T;  v = RMSNorm(X + a; g_ffn);  f = (SiLU(v W_gate^T) * (v W_up^T)) W_down^T
+ *   y_S   = X + (varsigma * r) * (a + f)  written in place into x; unselected rows untouched
+ *   b_S  += delta                                     (fp32, when a bias buffer is given)
+ * A dense layer is the same with S = every position, no gate and no varsigma:
+ *   y = x + (a + f).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned (allocated by the caller, e.g. through PyTorch). The
+ *     library never allocates or frees device memory. Scratch space comes from a caller
+ *     workspace of at least xmod_workspace_bytes() bytes, 256-byte aligned.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the null stream) and
+ *     returns without synchronising. Pointers must stay valid until that work completes.
+ *     Calls are stateless; concurrent calls must not share output or workspace buffers.
+ *   - bf16 tensors are raw 16-bit bfloat16 arrays; fp32 tensors are float arrays.
+ *   - Activations are row-major [B, T, d]. Weights use the [out, in] layout of a Linear layer.
+ *     W_qkv rows are: Hq query heads, then Hkv key heads, then Hkv value heads, each head_dim
+ *     rows. idx lists positions within a sequence, ascending, [B, k]; packed row m = b*k + j.
+ *   - Arguments are validated before the first launch; on an error status nothing is written.
+ *     XMOD_ERR_INVALID_ARG: NULL required pointer, non-positive size, K < 1, floor(T/K) < 1,
+ *       Hq % Hkv != 0, A*K not an integer, wrong number of layers.
+ *     XMOD_ERR_UNSUPPORTED: head_dim not 64 or 128, d or ffn_hidden not a multiple of 64,
+ *       T > 65536 (top-k holds one sequence in one workgroup), d > 8192.
+ *     XMOD_ERR_WORKSPACE: workspace NULL or smaller than xmod_workspace_bytes().
+ *     XMOD_ERR_HIP: a kernel launch failed; xmod_last_hip_error() returns the hipError_t
+ *       (kept per calling thread). Faults inside kernels surface at the caller's next sync.
+ */
+#ifndef XMOD_H
+#define XMOD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XMOD_OK = 0,
+  XMOD_ERR_INVALID_ARG = 1,
+  XMOD_ERR_UNSUPPORTED = 2,
+  XMOD_ERR_WORKSPACE = 3,
+  XMOD_ERR_HIP = 4
+} xmod_status;
+
+/* Shapes shared by the layers of one model. */
+typedef struct {
+  int32_t B;            /* sequences */
+  int32_t T;            /* tokens per sequence */
+  int32_t d;            /* model width */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv, divides Hq */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t ffn_hidden;   /* F */
+  float rms_eps;        /* RMSNorm epsilon */
+} xmod_dims;
+
+/* Weights of one layer: device pointers to bf16 arrays, plus host scalars. */
+typedef struct {
+  const void *w_router;  /* [d]; unused by dense layers */
+  float router_bias;     /* beta_r (host scalar) */
+  float varsigma;        /* per-layer scale of the gated residual, Eq. (7) (host scalar) */
+  const void *g_attn;    /* [d] RMSNorm gain before attention */
+  const void *w_qkv;     /* [Hq*hd + 2*Hkv*hd, d] */
+  const void *w_o;       /* [d, Hq*hd] */
+  const void *g_ffn;     /* [d] RMSNorm gain before the FFN */
+  const void *w_gate;    /* [F, d] */
+  const void *w_up;      /* [F, d] */
+  const void *w_down;    /* [d, F] */
+} xmod_layer;
+
+/* Entry-point ids for xmod_workspace_bytes(). */
+enum {
+  XMOD_WS_ROUTE_TOPK = 0,
+  XMOD_WS_SPARSE_LAYER = 1,
+  XMOD_WS_DENSE_LAYER = 2,
+  XMOD_WS_BLOCK = 3
+};
+
+/* Workspace bytes an entry point needs for these shapes (0 if none). K is ignored for the
+ * dense layer. Returns 0 for invalid shapes as well; the entry point then reports the error. */
+size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_point);
+
+/* Router and top-k of one sparse layer ([XMOD] Eq. (8), "training-time top-k"; [MOD]).
+ *   x [B,T,d] bf16; w_router [d] bf16; bias [B,T] fp32 or NULL (zeros), read only.
+ *   logits [B,T] fp32 out: ell. idx [B,k] int32 out, ascending. gate [B,k] fp32 out:
+ *   sigmoid(ell) at idx. k = floor(T/K). No workspace is needed (ws may be NULL). */
+xmod_status xmod_route_topk(const void *x, const void *w_router, float router_bias,
+                            const float *bias, float tau, int32_t K, const xmod_dims *dims,
+                            float *logits, int32_t *idx, float *gate, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Top-k of given fp32 logits [B,T]: idx [B,k] int32 ascending; ties to the lower position,
+ * -0 equals +0, NaN ranks lowest. gate [B,k] fp32 = sigmoid(logit) at idx, or NULL.
+ * If bias is non-NULL, bias[b, idx] += delta (fp32). */
+xmod_status xmod_topk_from_logits(const float *logits, int32_t B, int32_t T, int32_t k,
+                                  int32_t *idx, float *gate, float *bias, float delta,
+                                  void *stream);
+
+/* Gather the selected rows: x_packed[b*k + j] = x[b, idx[b,j]] (bit copy). x [B,T,d] bf16,
+ * x_packed [B*k, d] bf16 out. ([MOD] "basic architecture": gather of the chosen tokens.) */
+xmod_status xmod_pack(const void *x, const int32_t *idx, int32_t B, int32_t T, int32_t d,
+                      int32_t k, void *x_packed, void *stream);
+
+/* Gated scatter of [XMOD] Eq. (7), in place: for every packed row m = b*k + j,
+ *   x[b, idx[b,j]] = bf16_rne(X + (varsigma * gate[m]) * (a[m] + f[m])), X = x[b, idx[b,j]],
+ * each operation rounded in fp32 in that order (no fused multiply-add). Other rows of x are
+ * not touched. a_packed, f_packed [B*k, d] bf16; gate [B*k] fp32. */
+xmod_status xmod_scatter_gated(void *x, const int32_t *idx, const float *gate, float varsigma,
+                               const void *a_packed, const void *f_packed, int32_t B, int32_t T,
+                               int32_t d, int32_t k, void *stream);
+
+/* Forward of one Sparse(K) layer ([XMOD] Fig. 1(b), Eqs. (7)-(8); Table 7), in place on x.
+ *   bias [B,T] fp32 in/out or NULL: read for ell, then bias[idx] += delta.
+ *   idx_out [B,k] int32 and gate_out [B,k] fp32: optional copies of the selection. */
+xmod_status xmod_sparse_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                  int32_t K, float *bias, float tau, float delta,
+                                  int32_t *idx_out, float *gate_out, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/* Forward of one dense layer (every token, no gate): y = x + (a + f), in place on x. */
+xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/* Forward of the stack [Dense]xN0 + ([Sparse(K)]xAK + [Dense])xN1 ([XMOD] Eq. (3)), in place.
+ * layers: host array of n_layers = N0 + N1*(A*K + 1) entries, in stack order. bias [B,T] fp32
+ * is scratch for the carried bias: zeroed at the start of every block (the reset at each dense
+ * anchor), grown by delta for each selection. A*K must be an integer (within 1e-6). */
+xmod_status xmod_block_fwd(void *x, const xmod_layer *layers, int32_t n_layers,
+                           const xmod_dims *dims, int32_t N0, int32_t N1, float A, int32_t K,
+                           float *bias, float tau, float delta, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* --- Stages of the path, exposed for stage-by-stage parity checks. ------------------------ */
+
+/* Row-wise RMSNorm of gathered rows: out[m] = bf16(X / sqrt(mean(X^2) + eps) * gain), with
+ * X = x[b, idx[b,j]] for m = b*k + j, or X = x[m] when idx is NULL (rows = B*k then). */
+xmod_status xmod_rmsnorm_rows(const void *x, const int32_t *idx, const void *gain, float eps,
+                              int32_t B, int32_t T, int32_t d, int32_t k, void *out, void *stream);
+
+/* C[M,N] = bf16(A[M,K] B[N,K]^T), fp32 accumulate; all row-major, leading dims in elements.
+ * K must be a multiple of 64. */
+xmod_status xmod_gemm_bf16_nt(const void *A, int32_t lda, const void *Bm, int32_t ldb, void *C,
+                              int32_t ldc, int32_t M, int32_t N, int32_t K, void *stream);
+
+/* Causal attention over packed sequences ([XMOD] Table 7 "selected subset"; [MODA] 2.1 GQA):
+ * qkv [B*k, ld_qkv] bf16 holds Q (Hq*hd columns), then K and V (Hkv*hd each) per row;
+ * o [B*k, ld_o] bf16 out (Hq*hd columns). Row j of a sequence attends to rows 0..j. */
+xmod_status xmod_attention_fwd(const void *qkv, int32_t ld_qkv, void *o, int32_t ld_o,
+                               int32_t B, int32_t k, int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, void *stream);
+
+/* --- Measurement hook. ------------------------------------------------------------------------
+ * While enabled, the layer and block entry points record a hipEvent on their stream before
+ * their first kernel and after every kernel they launch (events are created on first use and
+ * kept). xmod_phase_times() waits for the last recorded event, adds the time between
+ * consecutive events of every recorded call into ms[i] for kernel slot i (sparse layer slots:
+ * 0 router, 1 top-k, 2 gather+RMSNorm, 3 QKV GEMM, 4 attention, 5 O GEMM, 6 residual+RMSNorm,
+ * 7 gate/up GEMM with SwiGLU, 8 down GEMM with gated scatter; a dense layer fills slots 2-8),
+ * stores the number of recorded calls in *n_calls, and forgets the recorded events.
+ * Not thread safe; meant for benchmarks, not for production calls or graph capture. */
+void xmod_phase_timing_enable(int32_t on);
+xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls);
+
+const char *xmod_status_string(xmod_status st);
+int32_t xmod_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XMOD_H */

@@ -1,0 +1,263 @@
+// Router GEMV and per-sequence top-k of the X-MoD sparse layer (gfx950, wave64).
+//
+// Router: the scalar Linear(d, 1) score of the "Mixture-of-Depths explained" page ("basic
+// architecture"), adjusted by the carried per-token bias of the X-MoD review's Eq. (8):
+// ell_t = (w_r . x_t + beta_r) - tau * b_t, in fp32. One wave reduces one row; each wave keeps
+// several rows' loads in flight, which is what an HBM-bound pass over all B*T rows needs.
+//
+// Top-k: the X-MoD review's training-time rule (section "training-time top-k") keeps the
+// top-1/K share of each sequence, non-causally. One workgroup of 1024 threads owns one
+// sequence: 4 radix passes of 8 bits over order-preserving uint32 keys find the k-th largest
+// key, then a block-wide prefix sum over positions writes the winners in ascending position
+// order. Ties at the threshold go to the lowest positions; -0 equals +0; NaN ranks lowest.
+// All counting is integer, so the result does not depend on thread scheduling.
+#include "common.h"
+
+namespace xmod {
+
+// ---- router ---------------------------------------------------------------------------------
+
+template <int NI, int R>
+__global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict__ x,
+                                                     const uint16_t *__restrict__ w, float beta,
+                                                     const float *__restrict__ bias, float tau,
+                                                     float *__restrict__ logits, int64_t rows,
+                                                     int d) {
+  const int lane = threadIdx.x & 63;
+  const int nch = d >> 3;  // 8-element chunks per row
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (row0 >= rows) return;
+
+  float wf[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) {
+      unpack8(*(const uint4 *)(w + (size_t)c * 8), wf[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wf[i][e] = 0.f;
+    }
+  }
+  uint4 xv[R][NI];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = row0 + r < rows ? row0 + r : rows - 1;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = lane + 64 * i;
+      xv[r][i] = c < nch ? *(const uint4 *)(x + row * d + (size_t)c * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float xf[8];
+      unpack8(xv[r][i], xf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaf(xf[e], wf[i][e], a);
+    }
+    acc[r] = wave_sum(a);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r;
+      if (row < rows) {
+        const float s = __fadd_rn(acc[r], beta);
+        const float tb = bias ? __fmul_rn(tau, bias[row]) : 0.f;
+        logits[row] = __fsub_rn(s, tb);
+      }
+    }
+  }
+}
+
+template <int NI>
+static hipError_t router_ni(const uint16_t *x, const uint16_t *w, float beta, const float *bias,
+                            float tau, float *logits, int64_t rows, int d, hipStream_t s) {
+  constexpr int R = NI <= 2 ? 8 : (NI <= 4 ? 4 : (NI <= 8 ? 2 : 1));
+  const int64_t waves = (rows + R - 1) / R;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((router_kernel<NI, R>), dim3((unsigned)blocks), dim3(256), 0, s, x, w, beta,
+                     bias, tau, logits, rows, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t *x, const uint16_t *w, float beta, const float *bias,
+                         float tau, float *logits, int64_t rows, int d, hipStream_t s) {
+  const int ni = ((d >> 3) + 63) / 64;
+  switch (ni) {
+    case 1: return router_ni<1>(x, w, beta, bias, tau, logits, rows, d, s);
+    case 2: return router_ni<2>(x, w, beta, bias, tau, logits, rows, d, s);
+    case 3: return router_ni<3>(x, w, beta, bias, tau, logits, rows, d, s);
+    case 4: return router_ni<4>(x, w, beta, bias, tau, logits, rows, d, s);
+    case 5: case 6: return router_ni<6>(x, w, beta, bias, tau, logits, rows, d, s);
+    case 7: case 8: return router_ni<8>(x, w, beta, bias, tau, logits, rows, d, s);
+    default: return router_ni<16>(x, w, beta, bias, tau, logits, rows, d, s);
+  }
+}
+
+// ---- top-k ----------------------------------------------------------------------------------
+
+// Order-preserving map of fp32 to uint32: a > b (as floats) iff key(a) > key(b).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return 0u;  // NaN ranks lowest
+  if (mag == 0u) u = 0u;             // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Add each lane's digit to the LDS histogram, one atomic per distinct digit in the wave
+// (router logits share their top bits, so plain per-lane atomics would serialise).
+__device__ __forceinline__ void wave_hist_add(uint32_t *hist, uint32_t dg, bool cand) {
+  uint64_t active = __ballot(cand);
+  const int lane = threadIdx.x & 63;
+  while (active) {
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    const uint32_t dl = __shfl(dg, leader, 64);
+    const uint64_t same = __ballot(cand && dg == dl);
+    if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+    active &= ~same;
+  }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ logits, int T, int k,
+                                                    int32_t *__restrict__ idx,
+                                                    float *__restrict__ gate,
+                                                    float *__restrict__ bias, float delta) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_digit, s_remaining;
+  __shared__ unsigned long long s_wave_tot[16];
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const float *L = logits + (int64_t)b * T;
+  const int p0 = tid * KPT;
+
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int p = p0 + j;
+    key[j] = p < T ? order_key(L[p]) : 0u;
+  }
+
+  // Radix select of the k-th largest key, 8 bits per pass from the top.
+  uint32_t prefix = 0u, pmask = 0u, remaining = (uint32_t)k;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool cand = (p0 + j < T) && ((key[j] & pmask) == prefix);
+      wave_hist_add(hist, (key[j] >> shift) & 255u, cand);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane l owns bins 255-4l .. 252-4l, scanned from the top (largest digit first)
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        tot += c[q];
+      }
+      uint32_t incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const uint32_t excl = incl - tot;
+      if (excl < remaining && remaining <= incl) {
+        uint32_t above = excl;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (remaining <= above + c[q]) {
+            s_digit = 255u - 4u * lane - q;
+            s_remaining = remaining - above;
+            break;
+          }
+          above += c[q];
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t dsel = s_digit;
+    remaining = s_remaining;
+    prefix |= dsel << shift;
+    pmask |= 255u << shift;
+  }
+  const uint32_t thr = prefix;     // key of the k-th largest
+  const uint32_t need = remaining; // how many keys equal to thr are taken (lowest positions)
+
+  // Block-wide exclusive prefix over (count > thr, count == thr) in position order.
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (p0 + j < T) {
+      gt += key[j] > thr;
+      eq += key[j] == thr;
+    }
+  }
+  const unsigned long long v = (unsigned long long)gt | ((unsigned long long)eq << 32);
+  unsigned long long incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wave_tot[wid] = incl;
+  __syncthreads();
+  unsigned long long base = 0;
+  for (int w2 = 0; w2 < wid; ++w2) base += s_wave_tot[w2];
+  const unsigned long long excl = base + incl - v;
+  const uint32_t gt_before = (uint32_t)(excl & 0xFFFFFFFFull);
+  uint32_t eq_seen = (uint32_t)(excl >> 32);
+  uint32_t pos = gt_before + (eq_seen < need ? eq_seen : need);
+
+  int32_t *I = idx + (int64_t)b * k;
+  float *G = gate ? gate + (int64_t)b * k : nullptr;
+  float *Bi = bias ? bias + (int64_t)b * T : nullptr;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int p = p0 + j;
+    if (p < T) {
+      bool sel = key[j] > thr;
+      if (key[j] == thr) {
+        sel = eq_seen < need;
+        ++eq_seen;
+      }
+      if (sel && pos < (uint32_t)k) {  // pos < k always holds; the test keeps writes in bounds
+        I[pos] = p;
+        if (G) G[pos] = 1.0f / (1.0f + expf(-L[p]));
+        if (Bi) Bi[p] = __fadd_rn(Bi[p], delta);
+        ++pos;
+      }
+    }
+  }
+}
+
+hipError_t launch_topk(const float *logits, int B, int T, int k, int32_t *idx, float *gate,
+                       float *bias, float delta, hipStream_t s) {
+  const int need = (T + 1023) / 1024;
+#define XMOD_TOPK(KPT_)                                                                         \
+  hipLaunchKernelGGL((topk_kernel<KPT_>), dim3(B), dim3(1024), 0, s, logits, T, k, idx, gate, \
+                     bias, delta)
+  if (need <= 1) XMOD_TOPK(1);
+  else if (need <= 2) XMOD_TOPK(2);
+  else if (need <= 4) XMOD_TOPK(4);
+  else if (need <= 8) XMOD_TOPK(8);
+  else if (need <= 16) XMOD_TOPK(16);
+  else if (need <= 32) XMOD_TOPK(32);
+  else XMOD_TOPK(64);
+#undef XMOD_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace xmod

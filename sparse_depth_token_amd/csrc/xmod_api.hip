@@ -1,0 +1,402 @@
+// C ABI of the X-MoD sparse-depth layer library: argument validation, workspace planning and
+// the order in which the kernels of one layer, or of a stack of layers, are enqueued.
+// Semantics of every entry point are documented in include/xmod.h.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/xmod.h"
+#include "common.h"
+
+using namespace xmod;
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+#define XMOD_HIP(expr)                 \
+  do {                                 \
+    hipError_t e_ = (expr);            \
+    if (e_ != hipSuccess) {            \
+      g_last_hip = (int32_t)e_;        \
+      return XMOD_ERR_HIP;             \
+    }                                  \
+  } while (0)
+
+// ---- measurement hook: events between kernels (see xmod_phase_timing_enable) ----
+constexpr int kSlots = 9;
+struct PhaseCall { size_t first; int first_slot; int n; };
+struct PhaseLog {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<PhaseCall> calls;
+};
+PhaseLog g_phase;
+
+void phase_mark(hipStream_t s) {
+  if (!g_phase.on) return;
+  if (g_phase.used == g_phase.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    g_phase.pool.push_back(e);
+  }
+  if (hipEventRecord(g_phase.pool[g_phase.used], s) != hipSuccess) return;
+  ++g_phase.used;
+  if (!g_phase.calls.empty()) ++g_phase.calls.back().n;
+}
+void phase_begin(hipStream_t s, int first_slot) {
+  if (!g_phase.on) return;
+  g_phase.calls.push_back(PhaseCall{g_phase.used, first_slot, 0});
+  phase_mark(s);
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+xmod_status check_dims(const xmod_dims *dm) {
+  if (!dm) return XMOD_ERR_INVALID_ARG;
+  if (dm->B < 1 || dm->T < 1 || dm->d < 1 || dm->n_q_heads < 1 || dm->n_kv_heads < 1 ||
+      dm->head_dim < 1 || dm->ffn_hidden < 1)
+    return XMOD_ERR_INVALID_ARG;
+  if (dm->n_q_heads % dm->n_kv_heads != 0) return XMOD_ERR_INVALID_ARG;
+  if (!(dm->rms_eps >= 0.f) || !isfinite(dm->rms_eps)) return XMOD_ERR_INVALID_ARG;
+  if (dm->head_dim != 64 && dm->head_dim != 128) return XMOD_ERR_UNSUPPORTED;
+  if (dm->d % 64 != 0 || dm->ffn_hidden % 64 != 0 || dm->d > 8192) return XMOD_ERR_UNSUPPORTED;
+  if (dm->T > 65536) return XMOD_ERR_UNSUPPORTED;
+  return XMOD_OK;
+}
+
+bool layer_ok(const xmod_layer *L, bool sparse) {
+  if (!L) return false;
+  if (sparse && !L->w_router) return false;
+  if (!L->g_attn || !L->w_qkv || !L->w_o || !L->g_ffn || !L->w_gate || !L->w_up || !L->w_down)
+    return false;
+  if (!isfinite(L->router_bias) || !isfinite(L->varsigma)) return false;
+  return true;
+}
+
+struct Plan {
+  size_t logits = 0, idx = 0, gate = 0, u = 0, qkv = 0, o = 0, a = 0, g = 0, total = 0;
+};
+
+// Workspace layout of one layer with M routed rows (all offsets 256-byte aligned).
+Plan plan_layer(const xmod_dims *dm, int64_t M, bool sparse) {
+  Plan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  const int64_t dq = (int64_t)dm->n_q_heads * dm->head_dim;
+  const int64_t nqkv = dq + 2LL * dm->n_kv_heads * dm->head_dim;
+  if (sparse) {
+    p.logits = take((size_t)dm->B * dm->T * 4);
+    p.idx = take((size_t)M * 4);
+    p.gate = take((size_t)M * 4);
+  }
+  p.u = take((size_t)M * dm->d * 2);
+  p.qkv = take((size_t)M * nqkv * 2);
+  p.o = take((size_t)M * dq * 2);
+  p.a = take((size_t)M * dm->d * 4);
+  p.g = take((size_t)M * dm->ffn_hidden * 2);
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+// Attention, FFN and the residual write-back for M = B*k rows given by idx (identity when
+// idx == nullptr). gate == nullptr selects the dense residual y = x + (a + f).
+xmod_status run_body(uint16_t *x, const int32_t *idx, const float *gate, const xmod_layer *L,
+                     const xmod_dims *dm, int k, const Plan &p, void *ws, hipStream_t s) {
+  const int B = dm->B, T = dm->T, d = dm->d;
+  const int64_t M = (int64_t)B * k;
+  const int dq = dm->n_q_heads * dm->head_dim;
+  const int nqkv = dq + 2 * dm->n_kv_heads * dm->head_dim;
+  uint16_t *u = at<uint16_t>(ws, p.u), *qkv = at<uint16_t>(ws, p.qkv), *o = at<uint16_t>(ws, p.o);
+  float *a = at<float>(ws, p.a);
+  uint16_t *gbuf = at<uint16_t>(ws, p.g);
+
+  XMOD_HIP(launch_gather_rows(x, idx, (const uint16_t *)L->g_attn, dm->rms_eps, true, B, T, d, k,
+                              u, s));
+  phase_mark(s);
+  GemmArgs g{};
+  g.A = u; g.lda = d; g.B = (const uint16_t *)L->w_qkv; g.ldb = d; g.C = qkv; g.ldc = nqkv;
+  g.M = (int)M; g.N = nqkv; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, s));
+  phase_mark(s);
+  XMOD_HIP(launch_attention(qkv, nqkv, o, dq, B, k, dm->n_q_heads, dm->n_kv_heads, dm->head_dim,
+                            s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.A = o; g.lda = dq; g.B = (const uint16_t *)L->w_o; g.ldb = dq; g.Cf = a; g.ldc = d;
+  g.M = (int)M; g.N = d; g.K = dq;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, s));
+  phase_mark(s);
+  XMOD_HIP(launch_residual_rmsnorm(x, idx, a, (const uint16_t *)L->g_ffn, dm->rms_eps, B, T, d, k,
+                                   u, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.A = u; g.lda = d; g.B = (const uint16_t *)L->w_gate; g.B2 = (const uint16_t *)L->w_up;
+  g.ldb = d; g.C = gbuf; g.ldc = dm->ffn_hidden; g.M = (int)M; g.N = dm->ffn_hidden; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_SWIGLU, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.A = gbuf; g.lda = dm->ffn_hidden; g.B = (const uint16_t *)L->w_down; g.ldb = dm->ffn_hidden;
+  g.ldc = d; g.M = (int)M; g.N = d; g.K = dm->ffn_hidden;
+  g.x = x; g.idx = idx; g.gate = gate; g.varsigma = L->varsigma; g.a = a; g.T = T; g.k = k;
+  XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
+  phase_mark(s);
+  return XMOD_OK;
+}
+
+xmod_status sparse_layer(void *x, const xmod_layer *L, const xmod_dims *dm, int32_t K,
+                         float *bias, float tau, float delta, int32_t *idx_out, float *gate_out,
+                         void *ws, hipStream_t s) {
+  const int k = dm->T / K;
+  const int64_t M = (int64_t)dm->B * k;
+  const Plan p = plan_layer(dm, M, true);
+  float *logits = at<float>(ws, p.logits);
+  int32_t *idx = idx_out ? idx_out : at<int32_t>(ws, p.idx);
+  float *gate = gate_out ? gate_out : at<float>(ws, p.gate);
+  phase_begin(s, 0);
+  XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)L->w_router, L->router_bias, bias,
+                         tau, logits, (int64_t)dm->B * dm->T, dm->d, s));
+  phase_mark(s);
+  XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s));
+  phase_mark(s);
+  return run_body((uint16_t *)x, idx, gate, L, dm, k, p, ws, s);
+}
+
+xmod_status dense_layer(void *x, const xmod_layer *L, const xmod_dims *dm, void *ws,
+                        hipStream_t s) {
+  const Plan p = plan_layer(dm, (int64_t)dm->B * dm->T, false);
+  phase_begin(s, 2);
+  return run_body((uint16_t *)x, nullptr, nullptr, L, dm, dm->T, p, ws, s);
+}
+
+__global__ void zero_f32_kernel(float *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+int block_sparse_per_block(float A, int32_t K, bool *ok) {
+  const double ak = (double)A * (double)K;
+  const double r = nearbyint(ak);
+  *ok = isfinite(ak) && fabs(ak - r) <= 1e-6 && r >= 0 && r <= 1e6;
+  return (int)r;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_point) {
+  if (check_dims(dims) != XMOD_OK) return 0;
+  switch (entry_point) {
+    case XMOD_WS_ROUTE_TOPK: return 0;
+    case XMOD_WS_SPARSE_LAYER:
+      if (K < 1 || dims->T / K < 1) return 0;
+      return plan_layer(dims, (int64_t)dims->B * (dims->T / K), true).total;
+    case XMOD_WS_DENSE_LAYER: return plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
+    case XMOD_WS_BLOCK: {
+      const size_t dn = plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
+      if (K < 1 || dims->T / K < 1) return dn;
+      const size_t sp = plan_layer(dims, (int64_t)dims->B * (dims->T / K), true).total;
+      return dn > sp ? dn : sp;
+    }
+    default: return 0;
+  }
+}
+
+xmod_status xmod_route_topk(const void *x, const void *w_router, float router_bias,
+                            const float *bias, float tau, int32_t K, const xmod_dims *dims,
+                            float *logits, int32_t *idx, float *gate, void *ws, size_t ws_bytes,
+                            void *stream) {
+  (void)ws; (void)ws_bytes;
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !w_router || !logits || !idx || !gate || K < 1 || dims->T / K < 1)
+    return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(router_bias) || !isfinite(tau)) return XMOD_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)w_router, router_bias, bias, tau,
+                         logits, (int64_t)dims->B * dims->T, dims->d, s));
+  XMOD_HIP(launch_topk(logits, dims->B, dims->T, dims->T / K, idx, gate, nullptr, 0.f, s));
+  return XMOD_OK;
+}
+
+xmod_status xmod_topk_from_logits(const float *logits, int32_t B, int32_t T, int32_t k,
+                                  int32_t *idx, float *gate, float *bias, float delta,
+                                  void *stream) {
+  if (!logits || !idx || B < 1 || T < 1 || k < 1 || k > T) return XMOD_ERR_INVALID_ARG;
+  if (T > 65536) return XMOD_ERR_UNSUPPORTED;
+  if (!isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_topk(logits, B, T, k, idx, gate, bias, delta, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_pack(const void *x, const int32_t *idx, int32_t B, int32_t T, int32_t d,
+                      int32_t k, void *x_packed, void *stream) {
+  if (!x || !idx || !x_packed || B < 1 || T < 1 || d < 1 || k < 1 || k > T)
+    return XMOD_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > 8192) return XMOD_ERR_UNSUPPORTED;
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, idx, nullptr, 0.f, false, B, T, d, k,
+                              (uint16_t *)x_packed, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_scatter_gated(void *x, const int32_t *idx, const float *gate, float varsigma,
+                               const void *a_packed, const void *f_packed, int32_t B, int32_t T,
+                               int32_t d, int32_t k, void *stream) {
+  if (!x || !idx || !gate || !a_packed || !f_packed || B < 1 || T < 1 || d < 1 || k < 1 || k > T)
+    return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(varsigma)) return XMOD_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > 8192) return XMOD_ERR_UNSUPPORTED;
+  XMOD_HIP(launch_scatter((uint16_t *)x, idx, gate, varsigma, (const uint16_t *)a_packed,
+                          (const uint16_t *)f_packed, B, T, d, k, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_sparse_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                  int32_t K, float *bias, float tau, float delta,
+                                  int32_t *idx_out, float *gate_out, void *ws, size_t ws_bytes,
+                                  void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_LAYER);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  return sparse_layer(x, layer, dims, K, bias, tau, delta, idx_out, gate_out, ws,
+                      (hipStream_t)stream);
+}
+
+xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer_ok(layer, false)) return XMOD_ERR_INVALID_ARG;
+  const size_t need = xmod_workspace_bytes(dims, 1, XMOD_WS_DENSE_LAYER);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  return dense_layer(x, layer, dims, ws, (hipStream_t)stream);
+}
+
+xmod_status xmod_block_fwd(void *x, const xmod_layer *layers, int32_t n_layers,
+                           const xmod_dims *dims, int32_t N0, int32_t N1, float A, int32_t K,
+                           float *bias, float tau, float delta, void *ws, size_t ws_bytes,
+                           void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  bool ok = false;
+  const int ak = block_sparse_per_block(A, K, &ok);
+  if (!x || !layers || !bias || N0 < 0 || N1 < 0 || K < 1 || dims->T / K < 1 || !ok)
+    return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  const int64_t expect = (int64_t)N0 + (int64_t)N1 * (ak + 1);
+  if (expect != n_layers) return XMOD_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < n_layers; ++i) {
+    const bool sparse = i >= N0 && ((i - N0) % (ak + 1)) < ak;
+    if (!layer_ok(&layers[i], sparse)) return XMOD_ERR_INVALID_ARG;
+  }
+  const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_BLOCK);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nb = (int64_t)dims->B * dims->T;
+  const unsigned zgrid = (unsigned)((nb + 255) / 256);
+  for (int64_t i = 0; i < n_layers; ++i) {
+    const bool in_prefix = i < N0;
+    const int64_t pos = in_prefix ? 0 : (i - N0) % (ak + 1);
+    if (!in_prefix && pos == 0) {  // start of a block: the carried bias restarts from zero
+      hipLaunchKernelGGL(zero_f32_kernel, dim3(zgrid), dim3(256), 0, s, bias, nb);
+      XMOD_HIP(hipGetLastError());
+    }
+    xmod_status r;
+    if (!in_prefix && pos < ak)
+      r = sparse_layer(x, &layers[i], dims, K, bias, tau, delta, nullptr, nullptr, ws, s);
+    else
+      r = dense_layer(x, &layers[i], dims, ws, s);
+    if (r != XMOD_OK) return r;
+  }
+  return XMOD_OK;
+}
+
+xmod_status xmod_rmsnorm_rows(const void *x, const int32_t *idx, const void *gain, float eps,
+                              int32_t B, int32_t T, int32_t d, int32_t k, void *out,
+                              void *stream) {
+  if (!x || !gain || !out || B < 1 || T < 1 || d < 1 || k < 1 || k > T)
+    return XMOD_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return XMOD_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > 8192) return XMOD_ERR_UNSUPPORTED;
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, idx, (const uint16_t *)gain, eps, true, B, T, d,
+                              k, (uint16_t *)out, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_gemm_bf16_nt(const void *A, int32_t lda, const void *Bm, int32_t ldb, void *Cm,
+                              int32_t ldc, int32_t M, int32_t N, int32_t K, void *stream) {
+  if (!A || !Bm || !Cm || M < 1 || N < 1 || K < 1 || lda < K || ldb < K || ldc < N)
+    return XMOD_ERR_INVALID_ARG;
+  if (K % 64 != 0 || N % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || ldc % 8 != 0)
+    return XMOD_ERR_UNSUPPORTED;
+  GemmArgs g{};
+  g.A = (const uint16_t *)A; g.lda = lda; g.B = (const uint16_t *)Bm; g.ldb = ldb;
+  g.C = (uint16_t *)Cm; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_attention_fwd(const void *qkv, int32_t ld_qkv, void *o, int32_t ld_o, int32_t B,
+                               int32_t k, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                               void *stream) {
+  if (!qkv || !o || B < 1 || k < 1 || n_q_heads < 1 || n_kv_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return XMOD_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return XMOD_ERR_UNSUPPORTED;
+  const int32_t nqkv = (n_q_heads + 2 * n_kv_heads) * head_dim;
+  if (ld_qkv < nqkv || ld_o < n_q_heads * head_dim || ld_qkv % 8 != 0 || ld_o % 8 != 0)
+    return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_attention((const uint16_t *)qkv, ld_qkv, (uint16_t *)o, ld_o, B, k, n_q_heads,
+                            n_kv_heads, head_dim, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+void xmod_phase_timing_enable(int32_t on) {
+  g_phase.on = on != 0;
+  g_phase.used = 0;
+  g_phase.calls.clear();
+}
+
+xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls) {
+  if (!ms || n_slots < 1) return XMOD_ERR_INVALID_ARG;
+  for (int i = 0; i < n_slots; ++i) ms[i] = 0.f;
+  if (n_calls) *n_calls = (int32_t)g_phase.calls.size();
+  if (g_phase.used > 0) XMOD_HIP(hipEventSynchronize(g_phase.pool[g_phase.used - 1]));
+  for (const PhaseCall &c : g_phase.calls) {
+    for (int i = 1; i < c.n; ++i) {
+      const int slot = c.first_slot + i - 1;
+      float t = 0.f;
+      XMOD_HIP(hipEventElapsedTime(&t, g_phase.pool[c.first + i - 1], g_phase.pool[c.first + i]));
+      if (slot < n_slots) ms[slot] += t;
+    }
+  }
+  g_phase.used = 0;
+  g_phase.calls.clear();
+  return XMOD_OK;
+}
+
+const char *xmod_status_string(xmod_status st) {
+  switch (st) {
+    case XMOD_OK: return "ok";
+    case XMOD_ERR_INVALID_ARG: return "invalid argument";
+    case XMOD_ERR_UNSUPPORTED: return "unsupported shape";
+    case XMOD_ERR_WORKSPACE: return "workspace missing or too small";
+    case XMOD_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t xmod_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+"""Thin ctypes binding of libxmod.so (the C ABI declared in include/xmod.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind the C ABI.
+Tensors are torch tensors on a ROCm device; their data pointers and the current stream are
+passed through. Importing this module fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxmod.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m sparse_depth_token_amd.build`")
+lib = ctypes.CDLL(_LIB_PATH)
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK = 0, 1, 2, 3
+
+# Every symbol include/xmod.h declares, in declaration order.
+EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", "xmod_pack",
+            "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_dense_layer_fwd", "xmod_block_fwd",
+            "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_attention_fwd",
+            "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
+            "xmod_last_hip_error"]
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn_hidden", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("router_bias", ctypes.c_float),
+                ("varsigma", ctypes.c_float), ("g_attn", ctypes.c_void_p),
+                ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("g_ffn", ctypes.c_void_p),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_P = ctypes.POINTER
+_sig = {
+    "xmod_workspace_bytes": (_sz, [_P(Dims), _i32, _i32]),
+    "xmod_route_topk": (_i32, [_vp, _vp, _f32, _vp, _f32, _i32, _P(Dims), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "xmod_topk_from_logits": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _f32, _vp]),
+    "xmod_pack": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "xmod_scatter_gated": (_i32, [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_sparse_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp, _vp,
+                                     _vp, _sz, _vp]),
+    "xmod_dense_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _sz, _vp]),
+    "xmod_block_fwd": (_i32, [_vp, _P(Layer), _i32, _P(Dims), _i32, _i32, _f32, _i32, _vp, _f32,
+                              _f32, _vp, _sz, _vp]),
+    "xmod_rmsnorm_rows": (_i32, [_vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "xmod_gemm_bf16_nt": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_attention_fwd": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_phase_timing_enable": (None, [_i32]),
+    "xmod_phase_times": (_i32, [_P(_f32), _i32, _P(_i32)]),
+    "xmod_status_string": (ctypes.c_char_p, [_i32]),
+    "xmod_last_hip_error": (_i32, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(lib, _name)
+    _fn.restype, _fn.argtypes = _res, _args
+
+
+class XmodError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib.xmod_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {lib.xmod_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise XmodError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_dims(B, T, d, n_q_heads, n_kv_heads, head_dim, ffn_hidden, rms_eps=1e-6) -> Dims:
+    return Dims(B, T, d, n_q_heads, n_kv_heads, head_dim, ffn_hidden, rms_eps)
+
+
+def make_layer(w: dict) -> Layer:
+    """w: dict of device tensors (bf16) w_router, g_attn, w_qkv, w_o, g_ffn, w_gate, w_up,
+    w_down, and host floats router_bias, varsigma."""
+    return Layer(_ptr(w.get("w_router")), float(w.get("router_bias", 0.0)),
+                 float(w.get("varsigma", 1.0)), _ptr(w["g_attn"]), _ptr(w["w_qkv"]),
+                 _ptr(w["w_o"]), _ptr(w["g_ffn"]), _ptr(w["w_gate"]), _ptr(w["w_up"]),
+                 _ptr(w["w_down"]))
+
+
+def workspace_bytes(dims: Dims, K: int, entry: int) -> int:
+    return int(lib.xmod_workspace_bytes(ctypes.byref(dims), K, entry))
+
+
+def alloc_workspace(dims: Dims, K: int, entry: int, device="cuda"):
+    n = workspace_bytes(dims, K, entry)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def route_topk(x, w_router, router_bias, bias, tau, K, dims, logits, idx, gate, stream=None):
+    _check(lib.xmod_route_topk(_ptr(x), _ptr(w_router), router_bias, _ptr(bias), tau, K,
+                               ctypes.byref(dims), _ptr(logits), _ptr(idx), _ptr(gate), None, 0,
+                               _stream(stream)), "xmod_route_topk")
+
+
+def topk_from_logits(logits, k, idx, gate=None, bias=None, delta=0.0, stream=None):
+    B, T = logits.shape
+    _check(lib.xmod_topk_from_logits(_ptr(logits), B, T, k, _ptr(idx), _ptr(gate), _ptr(bias),
+                                     delta, _stream(stream)), "xmod_topk_from_logits")
+
+
+def pack(x, idx, x_packed, stream=None):
+    B, T, d = x.shape
+    _check(lib.xmod_pack(_ptr(x), _ptr(idx), B, T, d, idx.shape[1], _ptr(x_packed),
+                         _stream(stream)), "xmod_pack")
+
+
+def scatter_gated(x, idx, gate, varsigma, a_packed, f_packed, stream=None):
+    B, T, d = x.shape
+    _check(lib.xmod_scatter_gated(_ptr(x), _ptr(idx), _ptr(gate), varsigma, _ptr(a_packed),
+                                  _ptr(f_packed), B, T, d, idx.shape[1], _stream(stream)),
+           "xmod_scatter_gated")
+
+
+def sparse_layer_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_out=None,
+                     gate_out=None, stream=None):
+    _check(lib.xmod_sparse_layer_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
+                                     _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
+                                     _ptr(ws), ws.numel(), _stream(stream)),
+           "xmod_sparse_layer_fwd")
+
+
+def dense_layer_fwd(x, layer: Layer, dims: Dims, ws, stream=None):
+    _check(lib.xmod_dense_layer_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "xmod_dense_layer_fwd")
+
+
+def block_fwd(x, layers: list, dims: Dims, N0, N1, A, K, bias, tau, delta, ws, stream=None):
+    arr = (Layer * len(layers))(*layers)
+    _check(lib.xmod_block_fwd(_ptr(x), arr, len(layers), ctypes.byref(dims), N0, N1, A, K,
+                              _ptr(bias), tau, delta, _ptr(ws), ws.numel(), _stream(stream)),
+           "xmod_block_fwd")
+
+
+def rmsnorm_rows(x, idx, gain, eps, k, out, stream=None):
+    B, T, d = x.shape
+    _check(lib.xmod_rmsnorm_rows(_ptr(x), _ptr(idx), _ptr(gain), eps, B, T, d, k, _ptr(out),
+                                 _stream(stream)), "xmod_rmsnorm_rows")
+
+
+def gemm_bf16_nt(A, Bm, C, stream=None):
+    M, K = A.shape
+    N = Bm.shape[0]
+    _check(lib.xmod_gemm_bf16_nt(_ptr(A), A.stride(0), _ptr(Bm), Bm.stride(0), _ptr(C),
+                                 C.stride(0), M, N, K, _stream(stream)), "xmod_gemm_bf16_nt")
+
+
+def attention_fwd(qkv, o, B, k, Hq, Hkv, hd, stream=None):
+    _check(lib.xmod_attention_fwd(_ptr(qkv), qkv.stride(0), _ptr(o), o.stride(0), B, k, Hq, Hkv,
+                                  hd, _stream(stream)), "xmod_attention_fwd")
+
+
+PHASES = ["router", "topk", "gather_rmsnorm", "qkv_gemm", "attention", "o_gemm",
+          "residual_rmsnorm", "gateup_swiglu_gemm", "down_scatter_gemm"]
+
+
+def phase_timing(on: bool):
+    lib.xmod_phase_timing_enable(1 if on else 0)
+
+
+def phase_times():
+    """Milliseconds per kernel slot summed over the recorded calls, and the number of calls."""
+    ms = (ctypes.c_float * len(PHASES))()
+    n = ctypes.c_int32(0)
+    _check(lib.xmod_phase_times(ms, len(PHASES), ctypes.byref(n)), "xmod_phase_times")
+    return {p: float(ms[i]) for i, p in enumerate(PHASES)}, int(n.value)

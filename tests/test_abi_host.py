@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every symbol the header
+declares, sizes workspaces, and rejects invalid arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "sparse_depth_token_amd", "libxmod.so")
+HEADER = os.path.join(ROOT, "include", "xmod.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libxmod.so not built")
+
+
+@pytest.fixture(scope="module")
+def x():
+    from sparse_depth_token_amd import xmod
+    return xmod
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xmod_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(x):
+    declared = _declared()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(x.lib, name), name
+    assert sorted(x.EXPORTED) == declared
+
+
+def test_status_strings(x):
+    for st in range(5):
+        assert x.lib.xmod_status_string(st)
+    assert x.lib.xmod_last_hip_error() == 0
+
+
+def _dims(x, **kw):
+    base = dict(B=8, T=4096, d=2048, n_q_heads=16, n_kv_heads=16, head_dim=128, ffn_hidden=5632,
+                rms_eps=1e-6)
+    base.update(kw)
+    return x.Dims(**base)
+
+
+def test_workspace_sizes(x):
+    dm = _dims(x)
+    M = 8 * 512
+    ws = x.workspace_bytes(dm, 8, x.WS_SPARSE_LAYER)
+    # logits + idx + gate + u + qkv + o + a (fp32) + g (each rounded up to 256 bytes)
+    want = (8 * 4096 * 4 + 2 * M * 4 + M * 2048 * 2 + M * 6144 * 2 + M * 2048 * 2 + M * 2048 * 4
+            + M * 5632 * 2)
+    assert want <= ws <= want + 8 * 256
+    dense = x.workspace_bytes(dm, 8, x.WS_DENSE_LAYER)
+    assert x.workspace_bytes(dm, 8, x.WS_BLOCK) == max(ws, dense)
+    assert x.workspace_bytes(dm, 8, x.WS_ROUTE_TOPK) == 0
+    assert x.workspace_bytes(_dims(x, head_dim=96), 8, x.WS_SPARSE_LAYER) == 0
+    assert x.workspace_bytes(dm, 0, x.WS_SPARSE_LAYER) == 0
+    assert x.workspace_bytes(dm, 8, 99) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _layer(x):
+    return x.Layer(FAKE, 0.0, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_sparse_layer_rejects_before_launch(x):
+    L = _layer(x)
+    dm = _dims(x)
+    f = x.lib.xmod_sparse_layer_fwd
+    args = lambda **o: [o.get("x", FAKE), ctypes.byref(o.get("L", L)), ctypes.byref(o.get("dm", dm)),
+                        o.get("K", 8), None, 1.0, 0.05, None, None, o.get("ws", FAKE),
+                        o.get("wsb", 1 << 40), None]
+    assert f(*args(K=0)) == x.ERR_INVALID_ARG
+    assert f(*args(K=5000)) == x.ERR_INVALID_ARG                  # floor(T/K) < 1
+    assert f(*args(x=None)) == x.ERR_INVALID_ARG
+    assert f(*args(dm=_dims(x, n_kv_heads=3))) == x.ERR_INVALID_ARG  # Hq % Hkv != 0
+    assert f(*args(dm=_dims(x, head_dim=96))) == x.ERR_UNSUPPORTED
+    assert f(*args(dm=_dims(x, d=2000))) == x.ERR_UNSUPPORTED
+    assert f(*args(dm=_dims(x, T=70000))) == x.ERR_UNSUPPORTED
+    assert f(*args(dm=_dims(x, B=0))) == x.ERR_INVALID_ARG
+    assert f(*args(wsb=1024)) == x.ERR_WORKSPACE
+    assert f(*args(ws=None)) == x.ERR_WORKSPACE
+    bad = _layer(x)
+    bad.w_router = None
+    assert f(*args(L=bad)) == x.ERR_INVALID_ARG
+    nan = _layer(x)
+    nan.varsigma = float("nan")
+    assert f(*args(L=nan)) == x.ERR_INVALID_ARG
+
+
+def test_block_rejects_before_launch(x):
+    dm = _dims(x)
+    layers = (x.Layer * 5)(*[_layer(x) for _ in range(5)])
+    f = x.lib.xmod_block_fwd
+    call = lambda n, N0, N1, A, K: f(FAKE, layers, n, ctypes.byref(dm), N0, N1, A, K, FAKE, 1.0,
+                                     0.05, FAKE, 1 << 40, None)
+    assert call(4, 1, 2, 0.5, 2) == x.ERR_INVALID_ARG          # wrong layer count
+    assert call(5, 1, 2, 0.3, 2) == x.ERR_INVALID_ARG          # A*K not an integer
+    assert call(5, -1, 2, 0.5, 2) == x.ERR_INVALID_ARG
+    nowr = (x.Layer * 5)(*[_layer(x) for _ in range(5)])
+    nowr[1].w_router = None                                   # layer 1 is sparse: needs a router
+    assert f(FAKE, nowr, 5, ctypes.byref(dm), 1, 2, 0.5, 2, FAKE, 1.0, 0.05, FAKE, 1 << 40,
+             None) == x.ERR_INVALID_ARG
+
+
+def test_stage_entry_points_reject_before_launch(x):
+    L = x.lib
+    assert L.xmod_topk_from_logits(FAKE, 2, 100, 0, FAKE, None, None, 0.0, None) == x.ERR_INVALID_ARG
+    assert L.xmod_topk_from_logits(FAKE, 2, 100, 101, FAKE, None, None, 0.0, None) == x.ERR_INVALID_ARG
+    assert L.xmod_topk_from_logits(FAKE, 1, 70000, 5, FAKE, None, None, 0.0, None) == x.ERR_UNSUPPORTED
+    assert L.xmod_pack(FAKE, FAKE, 2, 10, 100, 5, FAKE, None) == x.ERR_UNSUPPORTED
+    assert L.xmod_pack(FAKE, None, 2, 10, 128, 5, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_scatter_gated(FAKE, FAKE, FAKE, float("inf"), FAKE, FAKE, 2, 10, 128, 5,
+                                None) == x.ERR_INVALID_ARG
+    assert L.xmod_gemm_bf16_nt(FAKE, 100, FAKE, 100, FAKE, 64, 10, 64, 100, None) == x.ERR_UNSUPPORTED
+    assert L.xmod_gemm_bf16_nt(FAKE, 64, FAKE, 64, FAKE, 64, 0, 64, 64, None) == x.ERR_INVALID_ARG
+    assert L.xmod_attention_fwd(FAKE, 384, FAKE, 128, 1, 10, 2, 1, 80, None) == x.ERR_UNSUPPORTED
+    assert L.xmod_attention_fwd(FAKE, 384, FAKE, 128, 1, 10, 3, 2, 64, None) == x.ERR_INVALID_ARG
+    assert L.xmod_route_topk(FAKE, FAKE, 0.0, None, 1.0, 0, ctypes.byref(_dims(x)), FAKE, FAKE,
+                             FAKE, None, 0, None) == x.ERR_INVALID_ARG

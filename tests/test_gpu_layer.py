@@ -1,0 +1,194 @@
+"""End-to-end parity of one sparse layer and one dense layer: HIP path vs the oracle.
+
+Checks: selection equal to the oracle's (swaps allowed only between tokens whose oracle logits
+differ by < 1e-5; rows of a sequence after a swap are not compared, their attention context
+differs), unselected rows bit-identical, selected rows within max |diff| <= 2e-2 (+ half a bf16
+spacing) and relative L2 <= 5e-3, carried bias updated exactly. Full-size workloads are checked
+on sampled sequences / rows the oracle computes exactly, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as wl
+from parity import (bf16_vals, check_values, compare_selection, dev_bf16, host_bits, layer_to_device,
+                    say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def x():
+    from sparse_depth_token_amd import xmod
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return xmod
+
+
+def _dims(x, w):
+    return x.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden, w.rms_eps)
+
+
+def run_sparse_gpu(x, w, xb, lay, bias):
+    """One xmod_sparse_layer_fwd call. Returns (y bits, idx, gate, bias_out)."""
+    dims = _dims(x, w)
+    k = w.k
+    xt = dev_bf16(xb)
+    bt = torch.from_numpy(bias.copy()).cuda() if bias is not None else None
+    idx = torch.empty((w.B, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((w.B, k), dtype=torch.float32, device="cuda")
+    ws = x.alloc_workspace(dims, w.K, x.WS_SPARSE_LAYER)
+    dl = layer_to_device(lay)
+    x.sparse_layer_fwd(xt, x.make_layer(dl), dims, w.K, bt, w.tau, w.delta, ws, idx, gate)
+    torch.cuda.synchronize()
+    return (host_bits(xt), idx.cpu().numpy(), gate.cpu().numpy(),
+            None if bt is None else bt.cpu().numpy())
+
+
+def check_sparse(w, xb, lay, bias, got, sample=None):
+    """Compare a GPU sparse-layer result with the oracle (full, or sampled sequences/rows)."""
+    y_bits, idx_g, gate_g, bias_g = got
+    B, T, k = w.B, w.T, w.k
+    ref = oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=sample)
+    ell = ref["ell"]
+    first = compare_selection(idx_g, ref["idx"], ell)
+    # every row the GPU did not select is bit-identical to the input
+    sel = np.zeros((B, T), bool)
+    sel[np.arange(B)[:, None], idx_g] = True
+    assert np.array_equal(y_bits[~sel], xb[~sel]), "unselected rows changed"
+    # gate and bias follow the GPU's selection exactly (fp32 decisions on its own logits)
+    same = first == k
+    if same.any():
+        assert np.allclose(gate_g[same], ref["gate"][same], rtol=2e-6, atol=2e-6)
+        if bias_g is not None:
+            assert np.array_equal(bias_g[same], ref["bias_out"][same])
+    yv = bf16_vals(y_bits)
+    stats = []
+    if sample is None:
+        for b in range(B):
+            rows = idx_g[b, :first[b]]
+            if len(rows):
+                stats.append(check_values(yv[b, rows], ref["y"][b, rows], f"seq {b}"))
+    else:
+        for b, (prow, pos, ysel) in ref["rows"].items():
+            keep = prow < first[b]
+            assert np.array_equal(pos[keep], idx_g[b, prow[keep]])
+            if keep.any():
+                stats.append(check_values(yv[b, pos[keep]], ysel[keep], f"seq {b} sampled"))
+    say(f"    swaps in {int(np.sum(first < k))} of {B} sequences; max|diff|, relL2 = "
+        f"{max(s[0] for s in stats):.3g}, {max(s[1] for s in stats):.3g}")
+    return ref
+
+
+SMALL = {
+    "tiny_k2 (B2 T512 d256, as specified)": wl.WORKLOADS["sparse_k2_b2x512_d256"],
+    "tiny_k2 with gains, router bias, carried bias, varsigma": wl.scaled(
+        wl.WORKLOADS["sparse_k2_b2x512_d256"], seed=21, gain_std=0.2, router_bias=0.3,
+        bias_std=0.1, varsigma_range=(0.5, 1.5)),
+    "ragged B3 T700 K3 d512 GQA 8/2 hd64": wl.Workload(
+        "ragged", 22, 3, 700, 512, 8, 2, 64, 1536, 3, bias_std=0.1, varsigma_range=(0.5, 1.5),
+        gain_std=0.1),
+    "B2 T1024 K4 d1024 GQA 8/2 hd128": wl.Workload(
+        "gqa128", 23, 2, 1024, 1024, 8, 2, 128, 2816, 4, bias_std=0.1, varsigma_range=(0.5, 1.5)),
+    "k = 1 (B2 T50 K50)": wl.Workload("k1", 24, 2, 50, 256, 4, 4, 64, 512, 50),
+    "K = 1, every token (B1 T300)": wl.Workload("kall", 25, 1, 300, 256, 4, 2, 64, 512, 1,
+                                                 bias_std=0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_sparse_layer_small(x, name):
+    w = SMALL[name]
+    say(f"[sparse layer] {name}")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    got = run_sparse_gpu(x, w, xb, lay, bias)
+    check_sparse(w, xb, lay, bias, got)
+
+
+def run_dense_gpu(x, w, xb, lay):
+    dims = _dims(x, w)
+    xt = dev_bf16(xb)
+    ws = x.alloc_workspace(dims, 1, x.WS_DENSE_LAYER)
+    x.dense_layer_fwd(xt, x.make_layer(layer_to_device(lay)), dims, ws)
+    torch.cuda.synchronize()
+    return host_bits(xt)
+
+
+@pytest.mark.parametrize("name,w", [
+    ("dense B2 T512 d256", wl.WORKLOADS["sparse_k2_b2x512_d256"]),
+    ("dense ragged B2 T333 d512 GQA 8/2", wl.Workload("dr", 26, 2, 333, 512, 8, 2, 64, 1024, 1,
+                                                        gain_std=0.1)),
+    ("dense B1 T1024 d1024 hd128", wl.Workload("d128", 27, 1, 1024, 1024, 8, 8, 128, 2816, 1))])
+def test_dense_layer(x, name, w):
+    say(f"[dense layer] {name}")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    y = run_dense_gpu(x, w, xb, lay)
+    ref = oracle.dense_layer(xb, lay, w)
+    check_values(bf16_vals(y), ref, name)
+
+
+def test_check1_k1_unit_gate_equals_dense_on_gpu(x):
+    # K = 1 selects every token in order; w_r = 0 and beta_r = 100 give r = 1 exactly in fp32,
+    # and varsigma = 1: the gated residual X + 1*(a + f) is the dense residual, bit for bit.
+    w = wl.Workload("eq", 28, 2, 256, 256, 4, 2, 64, 512, 1)
+    say("[check 1] K=1, r=1, varsigma=1 vs dense layer")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    lay["w_router"] = np.zeros_like(lay["w_router"])
+    lay["router_bias"] = 100.0
+    ys = run_sparse_gpu(x, w, xb, lay, None)[0]
+    yd = run_dense_gpu(x, w, xb, lay)
+    assert np.array_equal(ys, yd)
+
+
+def test_check4_varsigma_zero_is_identity(x):
+    w = wl.scaled(wl.WORKLOADS["sparse_k2_b2x512_d256"], seed=29)
+    say("[check 4] varsigma = 0")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    lay["varsigma"] = 0.0
+    assert np.array_equal(run_sparse_gpu(x, w, xb, lay, None)[0], xb)
+
+
+# ---------------------------------------------------------------------------------------------
+# full-size workloads: the launch configuration the benchmark times
+# ---------------------------------------------------------------------------------------------
+
+def test_bench_workload_full_size_sampled(x):
+    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    say(f"[full size] {w.name}: GPU layer, oracle on sequences 0 and 5")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    got = run_sparse_gpu(x, w, xb, lay, bias)
+    idx_g = got[1]
+    assert idx_g.shape == (w.B, w.k) and np.all(np.diff(idx_g, axis=1) > 0)
+    assert idx_g.min() >= 0 and idx_g.max() < w.T
+    assert np.all(np.isfinite(bf16_vals(got[0])))
+    check_sparse(w, xb, lay, bias, got, sample={0: np.arange(w.k), 5: np.arange(w.k)})
+
+
+def test_bench_workload_deterministic(x):
+    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    say(f"[determinism] {w.name}: two runs, bitwise")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    a = run_sparse_gpu(x, w, xb, lay, bias)
+    b = run_sparse_gpu(x, w, xb, lay, bias)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_long_context_gqa_full_size_sampled(x):
+    w = wl.WORKLOADS["sparse_k4_gqa_b1x32768_d4096"]
+    say(f"[full size] {w.name}: oracle on 128 sampled packed rows")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    got = run_sparse_gpu(x, w, xb, lay, None)
+    assert np.all(np.isfinite(bf16_vals(got[0])))
+    rows = np.concatenate([np.arange(0, 48), np.arange(4090, 4106), np.arange(w.k - 64, w.k)])
+    check_sparse(w, xb, lay, None, got, sample={0: rows})
