@@ -49,6 +49,11 @@ def build(verbose: bool = False) -> str:
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # every internal symbol must be defined (a kernel whose host stub was dropped shows up here)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "xmod" in l]
+    if missing:
+        raise RuntimeError("undefined library symbols after link: " + ", ".join(missing[:5]))
     os.replace(tmp, OUT)
     if verbose:
         print("built", OUT)

@@ -11,9 +11,11 @@
 //    per-wave tiles cut LDS bytes per MFMA: 128x128 needs 512 B of fragments per MFMA.
 //  * The weight fragment is the MFMA's first operand and the activation fragment its second,
 //    so each lane ends with 4 consecutive output columns of one row.
-//  * Software pipeline: the next k-tile's 16-byte global loads are issued before the current
-//    tile's MFMAs; operand fragments are double-buffered in registers, so the LDS reads of
-//    k-step s+1 are in flight under the MFMAs of k-step s; one barrier per k-tile.
+//  * Software pipeline: the next k-tile is copied global -> LDS by the DMA form of the load
+//    (global_load_lds_dwordx4: 16 bytes per lane, no staging registers) while the current tile
+//    is multiplied; operand fragments are double-buffered in registers, so the LDS reads of
+//    k-step s+1 are in flight under the MFMAs of k-step s; one barrier per k-tile. The loop is
+//    unrolled over the two LDS stages so every stage offset is a constant.
 //  * LDS rows are 128 bytes (64 bf16); 16-byte chunks are XOR-swizzled with (r ^ (r >> 3)) & 7
 //    so the 16 lanes of one LDS cycle hit distinct banks on reads and writes.
 //  * Workgroup ids are remapped so each XCD (own L2) works on a contiguous range of tiles, and
@@ -26,7 +28,18 @@ namespace xmod {
 
 constexpr int GEMM_BK = 64;
 
+#ifndef XMOD_GEMM_SCHED
+#define XMOD_GEMM_SCHED 0
+#endif
+
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// 16-byte global -> LDS copy (DMA form): lane l of the wave writes bytes [16l, 16l+16) of the
+// 1 KB LDS block at `lds_block` (wave-uniform).
+__device__ __forceinline__ void dma16(const void *gsrc, uint16_t *lds_block) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_block, 16,
+                                   0, 0);
+}
 
 template <int BM, int BN, int WM, int WN, int EPI>
 struct GemmCfg {
@@ -34,14 +47,14 @@ struct GemmCfg {
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_ELEMS = BM * GEMM_BK, B_ELEMS = BN * GEMM_BK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int LA = BM * 8 / NT, LB = BN * 8 / NT;  // 16-byte loads per thread
   static constexpr int BN_OUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   static constexpr bool F32_TILE = EPI == EPI_STORE_F32 || EPI == EPI_RESIDUAL;
   static constexpr int CS = F32_TILE ? BN_OUT + 4 : BN_OUT + 8;  // C-tile row stride (elems)
-  static constexpr int LDS_MAIN = 2 * STAGE * 2;
+  static constexpr int NSTAGE = 3;                          // LDS ring depth
+  static constexpr int LDS_MAIN = NSTAGE * STAGE * 2;
   static constexpr int LDS_C = BM * CS * (F32_TILE ? 4 : 2);
   static constexpr int LDS_BYTES = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile loads must divide evenly");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "tiles are filled in 32-row DMA blocks");
   static_assert(EPI != EPI_SWIGLU || WN % 64 == 0, "SwiGLU pairs gate/up 32-column blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
@@ -75,30 +88,45 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
   const int m0 = tm * BM;
   const int n0 = tn * C::BN_OUT;  // first output column
 
-  // --- global load descriptors (rows fixed across k-tiles) ---
-  // Thread tid loads 16-byte chunk ch = tid % 8 of tile rows r0 + 32*i, r0 = tid / 8 < 32.
-  // Element offsets fit in 32 bits (every operand here holds fewer than 2^31 elements).
-  // swz(r0 + 32*i) = swz(r0) ^ (4i & 7): the LDS offsets follow from one per-thread value.
-  const int r0 = tid >> 3, ch0 = tid & 7;
-  const int sw0 = ch0 ^ swz(r0);
-  uint32_t a_off[C::LA], b_off[C::LB];
-#pragma unroll
-  for (int i = 0; i < C::LA; ++i) {
-    const int gm = min(m0 + r0 + 32 * i, M - 1);
-    a_off[i] = (uint32_t)gm * (uint32_t)g.lda + ch0 * 8;
-  }
-  // With four waves NT = 256, so the i-th chunk row is r0 + 32*i; for SwiGLU the 32-row
-  // blocks of the B tile alternate gate (even i) and up (odd i) weights.
+  // --- DMA descriptors (rows fixed across k-tiles) ---
+  // Wave w fills 1 KB blocks of a tile: its i-th block holds tile rows 32i + 8w .. +8, and lane
+  // l lands at byte 16*l of the block, i.e. row 32i + 8w + l/8, physical chunk l%8. Rows are
+  // XOR-swizzled, so lane l fetches logical chunk (l%8) ^ swz(row). Element offsets fit in 32
+  // bits (every operand here holds fewer than 2^31 elements).
   static_assert(C::NT == 256, "four waves per workgroup");
+  const int nk = K / GEMM_BK;
+  const int nk_last = nk - 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  const int lrow = 8 * wv + (lane >> 3);
+  constexpr int NA = BM / 32, NB = BN / 32;  // DMA blocks per wave per tile
+  uint32_t a_off[NA], b_off[NB];
 #pragma unroll
-  for (int i = 0; i < C::LB; ++i) {
-    int gn = EPI == EPI_SWIGLU ? n0 + (i >> 1) * 32 + r0 : n0 + r0 + 32 * i;
-    gn = min(gn, g.N - 1);
-    b_off[i] = (uint32_t)gn * (uint32_t)g.ldb + ch0 * 8;
+  for (int i = 0; i < NA; ++i) {
+    const int row = 32 * i + lrow;
+    const int gm = min(m0 + row, M - 1);
+    a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane & 7) ^ swz(row)) << 3)) * 2u;
   }
-  auto b_src = [&](int i) { return (EPI == EPI_SWIGLU && (i & 1)) ? g.B2 : g.B; };
-  auto lds_off = [&](int i) {  // LDS element offset of this thread's i-th chunk within a tile
-    return (r0 + 32 * i) * GEMM_BK + ((sw0 ^ ((4 * i) & 7)) << 3);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = 32 * i + lrow;
+    // SwiGLU: 32-row blocks alternate gate (even i) and up (odd i) weights.
+    int gn = EPI == EPI_SWIGLU ? n0 + (i >> 1) * 32 + lrow : n0 + row;
+    gn = min(gn, g.N - 1);
+    b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+  }
+  const char *a_bytes = (const char *)g.A;
+  const char *b_bytes[2] = {(const char *)g.B, (const char *)(EPI == EPI_SWIGLU ? g.B2 : g.B)};
+  // Copy k-tile kt (clamped to the last one) into the stage at element offset `stage`.
+  // Sources are a uniform base plus a 32-bit byte offset per lane.
+  auto issue_tile = [&](int kt, int stage) {
+    const uint32_t kb = (uint32_t)min(kt, nk_last) * (GEMM_BK * 2);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      dma16(a_bytes + (a_off[i] + kb), lds + stage + (32 * i + 8 * wv) * GEMM_BK);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      dma16(b_bytes[EPI == EPI_SWIGLU ? (i & 1) : 0] + (b_off[i] + kb),
+            lds + stage + C::A_ELEMS + (32 * i + 8 * wv) * GEMM_BK);
   };
 
   // --- fragment read offsets within a stage ---
@@ -118,9 +146,7 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  u32x4 ra[C::LA], rb[C::LB];
   bf16x8 fa[2][C::TM], fb[2][C::TN];
-  const int nk = K / GEMM_BK;
 
   auto load_frags = [&](const uint16_t *st, int ks, int buf) {
     const int c_even = ((2 * ks + gq) ^ sw_lane) << 3, c_odd = c_even ^ 32;
@@ -133,30 +159,11 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
     for (int j = 0; j < C::TN; ++j)
       fb[buf][j] = *(const bf16x8 *)(((j & 1) ? pb1 : pb0) + 32 * GEMM_BK * j);
   };
-
-#pragma unroll
-  for (int i = 0; i < C::LA; ++i) ra[i] = *(const u32x4 *)(g.A + a_off[i]);
-#pragma unroll
-  for (int i = 0; i < C::LB; ++i) rb[i] = *(const u32x4 *)(b_src(i) + b_off[i]);
-#pragma unroll
-  for (int i = 0; i < C::LA; ++i) *(u32x4 *)(lds + lds_off(i)) = ra[i];
-#pragma unroll
-  for (int i = 0; i < C::LB; ++i) *(u32x4 *)(lds + C::A_ELEMS + lds_off(i)) = rb[i];
-  __syncthreads();
-  load_frags(lds, 0, 0);
-
-#pragma unroll 1
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int koff = (kt + 1) * GEMM_BK;
-#pragma unroll
-      for (int i = 0; i < C::LA; ++i) ra[i] = *(const u32x4 *)(g.A + a_off[i] + koff);
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i) rb[i] = *(const u32x4 *)(b_src(i) + b_off[i] + koff);
-    }
-    const uint16_t *st = lds + cur * C::STAGE;
+  // Multiply one staged k-tile (4 k-steps); fragments of k-step 0 are already loaded.
+  // A scheduling barrier closes every k-step, so the compiler cannot regroup the MFMAs into
+  // per-accumulator chains: each step issues its TM*TN independent MFMAs while the next step's
+  // fragment reads are in flight.
+  auto compute_tile = [&](const uint16_t *st) {
 #pragma unroll
     for (int ks = 0; ks < GEMM_BK / 16; ++ks) {
       const int buf = ks & 1;
@@ -167,17 +174,56 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
         for (int j = 0; j < C::TN; ++j)
           acc[i][j] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t *nx = lds + (cur ^ 1) * C::STAGE;
+#if XMOD_GEMM_SCHED == 1
+      if (ks + 1 < GEMM_BK / 16) {
+        constexpr int NDS = C::TM + C::TN, NMF = C::TM * C::TN;
 #pragma unroll
-      for (int i = 0; i < C::LA; ++i) *(u32x4 *)(nx + lds_off(i)) = ra[i];
-#pragma unroll
-      for (int i = 0; i < C::LB; ++i) *(u32x4 *)(nx + C::A_ELEMS + lds_off(i)) = rb[i];
+        for (int q = 0; q < NDS; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NDS, 0);
+      }
+#endif
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    if (more) load_frags(lds + (cur ^ 1) * C::STAGE, 0, 0);
+  };
+
+  // Three-stage ring: tiles kt+1 and kt+2 are in flight while tile kt is multiplied. Before
+  // each barrier a wave waits only until its loads of the next tile have landed (the loads of
+  // the tile after it may stay outstanding: vmcnt <= NA + NB), then the barrier publishes the
+  // tile to all waves. vmcnt counts this wave's vector-memory loads, which return in order.
+  constexpr int NDMA = NA + NB;
+  constexpr int WAIT_NEXT = (NDMA & 15) | (7 << 4) | (15 << 8) | ((NDMA >> 4) << 14);
+  static_assert(NDMA < 64, "vmcnt field");
+  constexpr int S0 = 0, S1 = C::STAGE, S2 = 2 * C::STAGE;
+  issue_tile(0, S0);
+  issue_tile(1, S1);
+  __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+  __syncthreads();
+  load_frags(lds + S0, 0, 0);
+#pragma unroll 1
+  for (int kt = 0;; kt += 3) {
+    issue_tile(kt + 2, S2);
+    compute_tile(lds + S0);
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    __builtin_amdgcn_s_barrier();
+    load_frags(lds + S1, 0, 0);
+    if (kt + 1 >= nk) break;
+    issue_tile(kt + 3, S0);
+    compute_tile(lds + S1);
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    __builtin_amdgcn_s_barrier();
+    load_frags(lds + S2, 0, 0);
+    if (kt + 2 >= nk) break;
+    issue_tile(kt + 4, S1);
+    compute_tile(lds + S2);
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    __builtin_amdgcn_s_barrier();
+    load_frags(lds + S0, 0, 0);
+    if (kt + 3 >= nk) break;
   }
+  __syncthreads();  // the last fragment reads are done before LDS is reused for the C tile
 
   // --- epilogue: accumulators -> C tile in LDS ---
   // Lane holds output row wm0 + 32i + r32 and columns (within its 32-block) 8(e/4) + 4gq + e%4.
@@ -292,17 +338,12 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice: 256x256 (128x128 per wave) for the SwiGLU GEMM when it still gives at least
-// one tile per CU, else 256x128, else 128x128 for small problems. (The fp32-tile epilogues
-// need BN <= 128; the plain-store 256x256 variant does not fit its accumulators in registers.)
+// Tile choice: 256x128 (four 128x64 wave tiles) when there are enough tiles to fill the chip,
+// else 128x128 for small problems.
 template <int EPI>
 static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
   const int half = EPI == EPI_SWIGLU ? 2 : 1;
-  const long t256 = (long)((g.M + 255) / 256) * ((g.N + 256 / half - 1) / (256 / half));
   const long t128 = (long)((g.M + 255) / 256) * ((g.N + 128 / half - 1) / (128 / half));
-  if constexpr (EPI == EPI_SWIGLU) {
-    if (t256 >= 256) return run_gemm<256, 256, 128, 128, EPI>(g, s);
-  }
   if (t128 >= 160) return run_gemm<256, 128, 128, 64, EPI>(g, s);
   return run_gemm<128, 128, 64, 64, EPI>(g, s);
 }
