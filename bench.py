@@ -54,6 +54,22 @@ def algorithmic_work(w):
     }
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None if
+    there is none or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle (float64 NumPy) on a bounded sample of the same workload on this host."""
     import oracle
@@ -88,6 +104,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 256 MiB device copy first (a known-size reference for "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -116,6 +135,14 @@ def main():
 
     def step():
         xmod.sparse_layer_fwd(x, L, dims, w.K, bias, w.tau, w.delta, ws, stream=stream)
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -158,12 +185,12 @@ def main():
         achieved = work[dom]["flops"] / dom_avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom)}
     else:
         achieved = work[dom]["bytes"] / dom_avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None}
+                "traffic": measured_traffic(dom)}
     layer_flops = sum(v["flops"] for k2, v in work.items())
 
     out = {

@@ -6,33 +6,27 @@
 // layout of v_mfma_f32_32x32x16_bf16: every lane reads 8 consecutive bf16 (16 bytes) of a row.
 //
 // Design (gfx950, wave64):
-//  * Workgroup tile BM x BN, BK = 64, four waves in a 2 x 2 grid, each computing a WM x WN
-//    sub-tile as (WM/32) x (WN/32) MFMA 32x32x16 tiles (accumulators live in AGPRs). Larger
-//    per-wave tiles cut LDS bytes per MFMA: 128x128 needs 512 B of fragments per MFMA.
+//  * Workgroup tile BM x BN x BK, four waves in a 2 x 2 grid, each computing a WM x WN
+//    sub-tile as (WM/32) x (WN/32) MFMA 32x32x16 tiles (accumulators live in AGPRs).
 //  * The weight fragment is the MFMA's first operand and the activation fragment its second,
 //    so each lane ends with 4 consecutive output columns of one row.
-//  * Software pipeline: the next k-tile is copied global -> LDS by the DMA form of the load
-//    (global_load_lds_dwordx4: 16 bytes per lane, no staging registers) while the current tile
-//    is multiplied; operand fragments are double-buffered in registers, so the LDS reads of
-//    k-step s+1 are in flight under the MFMAs of k-step s; one barrier per k-tile. The loop is
-//    unrolled over the two LDS stages so every stage offset is a constant.
-//  * LDS rows are 128 bytes (64 bf16); 16-byte chunks are XOR-swizzled with (r ^ (r >> 3)) & 7
-//    so the 16 lanes of one LDS cycle hit distinct banks on reads and writes.
+//  * k-tiles are copied global -> LDS by the DMA form of the load (global_load_lds_dwordx4:
+//    16 bytes per lane, no staging registers) into a three-stage LDS ring: tiles kt+1 and kt+2
+//    are in flight while tile kt is multiplied. Before each barrier a wave waits only for its
+//    own loads of the next tile. Operand fragments are double-buffered in registers, and a
+//    scheduling barrier closes every k-step so the MFMAs of one step run while the next step's
+//    fragments are read.
+//  * With BK = 32 a workgroup needs at most 72 KB of LDS and 256 registers per lane, so two
+//    workgroups share a CU and each covers the other's barrier bubbles.
+//  * LDS rows (BK bf16) are split in 16-byte chunks, XOR-swizzled per row so that the lanes of
+//    one LDS cycle read distinct banks.
 //  * Workgroup ids are remapped so each XCD (own L2) works on a contiguous range of tiles, and
 //    tiles are visited in groups of 8 row-blocks for L2 reuse.
-//  * The epilogue goes through LDS (bf16 or fp32 tile) so global stores and the residual's
-//    reads of x and a are full 16-byte row chunks.
+//  * The epilogue goes through LDS (bf16 or fp32 tile, in row chunks when the fp32 tile does
+//    not fit) so global stores and the residual's reads of x and a are 16-byte row chunks.
 #include "common.h"
 
 namespace xmod {
-
-constexpr int GEMM_BK = 64;
-
-#ifndef XMOD_GEMM_SCHED
-#define XMOD_GEMM_SCHED 0
-#endif
-
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // 16-byte global -> LDS copy (DMA form): lane l of the wave writes bytes [16l, 16l+16) of the
 // 1 KB LDS block at `lds_block` (wave-uniform).
@@ -41,27 +35,51 @@ __device__ __forceinline__ void dma16(const void *gsrc, uint16_t *lds_block) {
                                    0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// Physical 16-byte chunk index of logical chunk c in LDS row r (rows of BK bf16).
+//  BK = 64 (8 chunks): c ^ ((r ^ (r >> 3)) & 7) - 16 consecutive rows reading one logical chunk
+//    land in distinct 4-bank groups (128-byte rows: even/odd rows cover the two 32-bank halves).
+//  BK = 32 (4 chunks): c ^ (((r >> 1) ^ (r >> 3)) & 3) - rows r..r+15 map to distinct
+//    (r % 4, chunk) pairs, i.e. distinct banks, and any aligned 8 rows to distinct 32-bank slots.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if (BK == 64) return (r ^ (r >> 3)) & 7;
+  return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int EPI>
 struct GemmCfg {
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int A_ELEMS = BM * GEMM_BK, B_ELEMS = BN * GEMM_BK;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;            // elements per LDS stage
+  static constexpr int NSTAGE = 3;                           // LDS ring depth
+  static constexpr int CPR = BK / 8;                         // 16-byte chunks per LDS row
+  static constexpr int RPB = 64 / CPR;                       // rows per 1 KB DMA block
+  static constexpr int NA = BM / RPB / 4, NB = BN / RPB / 4; // DMA blocks per wave per tile
   static constexpr int BN_OUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   static constexpr bool F32_TILE = EPI == EPI_STORE_F32 || EPI == EPI_RESIDUAL;
+  static constexpr int ESZ = F32_TILE ? 4 : 2;
   static constexpr int CS = F32_TILE ? BN_OUT + 4 : BN_OUT + 8;  // C-tile row stride (elems)
-  static constexpr int NSTAGE = 3;                          // LDS ring depth
   static constexpr int LDS_MAIN = NSTAGE * STAGE * 2;
-  static constexpr int LDS_C = BM * CS * (F32_TILE ? 4 : 2);
-  static constexpr int LDS_BYTES = LDS_MAIN > LDS_C ? LDS_MAIN : LDS_C;
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tiles are filled in 32-row DMA blocks");
+  // C-tile rows per epilogue pass (a multiple of 32, at most BM, fitting in the ring's LDS)
+  static constexpr int RCH_FIT = LDS_MAIN / (CS * ESZ) / 32 * 32;
+  static constexpr int RCH = RCH_FIT < BM ? RCH_FIT : BM;
+  static constexpr int NCH = BM / RCH;
+  static constexpr int LDS_BYTES = LDS_MAIN;
+  static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
+  static_assert(NT == 256, "four waves per workgroup");
+  static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
+  static_assert(NA >= 1 && NB >= 1 && BM % (4 * RPB) == 0 && BN % (4 * RPB) == 0, "DMA blocks");
   static_assert(EPI != EPI_SWIGLU || WN % 64 == 0, "SwiGLU pairs gate/up 32-column blocks");
+  static_assert(RCH >= 32 && BM % RCH == 0 && WM % 32 == 0, "epilogue row chunks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kernel(GemmArgs g) {
-  using C = GemmCfg<BM, BN, WM, WN, EPI>;
+template <int BM, int BN, int WM, int WN, int BK, int EPI>
+__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, EPI>::NT),
+                             (GemmCfg<BM, BN, WM, WN, BK, EPI>::WAVES_PER_EU)) void
+gemm_kernel(GemmArgs g) {
+  using C = GemmCfg<BM, BN, WM, WN, BK, EPI>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -89,54 +107,53 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
   const int n0 = tn * C::BN_OUT;  // first output column
 
   // --- DMA descriptors (rows fixed across k-tiles) ---
-  // Wave w fills 1 KB blocks of a tile: its i-th block holds tile rows 32i + 8w .. +8, and lane
-  // l lands at byte 16*l of the block, i.e. row 32i + 8w + l/8, physical chunk l%8. Rows are
-  // XOR-swizzled, so lane l fetches logical chunk (l%8) ^ swz(row). Element offsets fit in 32
-  // bits (every operand here holds fewer than 2^31 elements).
-  static_assert(C::NT == 256, "four waves per workgroup");
-  const int nk = K / GEMM_BK;
+  // 1 KB block b of a tile holds rows RPB*b .. RPB*b + RPB-1 and is filled by wave b % 4 with
+  // its instruction b / 4; lane l lands at byte 16*l, i.e. row RPB*b + l / CPR, physical chunk
+  // l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row). Element offsets fit in 32 bits
+  // (every operand here holds fewer than 2^31 elements); the DMA takes byte offsets.
+  const int nk = K / BK;
   const int nk_last = nk - 1;
   const int wv = __builtin_amdgcn_readfirstlane(wid);
-  const int lrow = 8 * wv + (lane >> 3);
-  constexpr int NA = BM / 32, NB = BN / 32;  // DMA blocks per wave per tile
-  uint32_t a_off[NA], b_off[NB];
+  uint32_t a_off[C::NA], b_off[C::NB];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int row = 32 * i + lrow;
+  for (int i = 0; i < C::NA; ++i) {
+    const int row = C::RPB * (4 * i + wv) + lane / C::CPR;
     const int gm = min(m0 + row, M - 1);
-    a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+    a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
   }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int row = 32 * i + lrow;
-    // SwiGLU: 32-row blocks alternate gate (even i) and up (odd i) weights.
-    int gn = EPI == EPI_SWIGLU ? n0 + (i >> 1) * 32 + lrow : n0 + row;
+  for (int i = 0; i < C::NB; ++i) {
+    const int row = C::RPB * (4 * i + wv) + lane / C::CPR;
+    // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
+    int gn = EPI == EPI_SWIGLU ? n0 + (row >> 6) * 32 + (row & 31) : n0 + row;
     gn = min(gn, g.N - 1);
-    b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane & 7) ^ swz(row)) << 3)) * 2u;
+    b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
   }
   const char *a_bytes = (const char *)g.A;
   const char *b_bytes[2] = {(const char *)g.B, (const char *)(EPI == EPI_SWIGLU ? g.B2 : g.B)};
+  auto b_half = [&](int i) {  // which weight matrix DMA block i of B reads (SwiGLU: gate / up)
+    return EPI == EPI_SWIGLU ? (((C::RPB * (4 * i + wv)) >> 5) & 1) : 0;  // wave-uniform
+  };
   // Copy k-tile kt (clamped to the last one) into the stage at element offset `stage`.
-  // Sources are a uniform base plus a 32-bit byte offset per lane.
   auto issue_tile = [&](int kt, int stage) {
-    const uint32_t kb = (uint32_t)min(kt, nk_last) * (GEMM_BK * 2);
+    const uint32_t kb = (uint32_t)min(kt, nk_last) * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      dma16(a_bytes + (a_off[i] + kb), lds + stage + (32 * i + 8 * wv) * GEMM_BK);
+    for (int i = 0; i < C::NA; ++i)
+      dma16(a_bytes + (a_off[i] + kb), lds + stage + C::RPB * (4 * i + wv) * BK);
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-      dma16(b_bytes[EPI == EPI_SWIGLU ? (i & 1) : 0] + (b_off[i] + kb),
-            lds + stage + C::A_ELEMS + (32 * i + 8 * wv) * GEMM_BK);
+    for (int i = 0; i < C::NB; ++i)
+      dma16(b_bytes[b_half(i)] + (b_off[i] + kb),
+            lds + stage + C::A_ELEMS + C::RPB * (4 * i + wv) * BK);
   };
 
   // --- fragment read offsets within a stage ---
   // Fragment rows are wm0 + 32i + r32 (A) and wn0 + 32j + r32 (B), with wm0, wn0 multiples of
-  // 64, so swz(row) = swz(r32) ^ (4i & 7): two chunk offsets per k-step (even / odd tile) and a
-  // constant 32-row stride that folds into the instruction's immediate offset.
+  // 64; then swz(row) = swz(r32) ^ (BK == 64 ? 4i & 7 : 0), so a k-step needs two chunk
+  // offsets (even / odd tile) plus a constant 32-row stride folded into the immediate offset.
   const int wm0 = (wid / C::NWN) * WM, wn0 = (wid % C::NWN) * WN;
-  const int a_base = (wm0 + r32) * GEMM_BK;
-  const int b_base = C::A_ELEMS + (wn0 + r32) * GEMM_BK;
-  const int sw_lane = swz(r32);
+  const int a_base = (wm0 + r32) * BK;
+  const int b_base = C::A_ELEMS + (wn0 + r32) * BK;
+  const int sw_lane = swz<BK>(r32);
 
   f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -147,55 +164,53 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   bf16x8 fa[2][C::TM], fb[2][C::TN];
-
   auto load_frags = [&](const uint16_t *st, int ks, int buf) {
-    const int c_even = ((2 * ks + gq) ^ sw_lane) << 3, c_odd = c_even ^ 32;
+    const int c_even = ((2 * ks + gq) ^ sw_lane) << 3;
+    const int c_odd = BK == 64 ? c_even ^ 32 : c_even;
     const uint16_t *pa0 = st + a_base + c_even, *pa1 = st + a_base + c_odd;
     const uint16_t *pb0 = st + b_base + c_even, *pb1 = st + b_base + c_odd;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
-      fa[buf][i] = *(const bf16x8 *)(((i & 1) ? pa1 : pa0) + 32 * GEMM_BK * i);
+      fa[buf][i] = *(const bf16x8 *)(((i & 1) ? pa1 : pa0) + 32 * BK * i);
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
-      fb[buf][j] = *(const bf16x8 *)(((j & 1) ? pb1 : pb0) + 32 * GEMM_BK * j);
+      fb[buf][j] = *(const bf16x8 *)(((j & 1) ? pb1 : pb0) + 32 * BK * j);
   };
-  // Multiply one staged k-tile (4 k-steps); fragments of k-step 0 are already loaded.
-  // A scheduling barrier closes every k-step, so the compiler cannot regroup the MFMAs into
-  // per-accumulator chains: each step issues its TM*TN independent MFMAs while the next step's
-  // fragment reads are in flight.
-  auto compute_tile = [&](const uint16_t *st) {
+  auto mfma_step = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < GEMM_BK / 16; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < GEMM_BK / 16) load_frags(st, ks + 1, buf ^ 1);
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-#if XMOD_GEMM_SCHED == 1
-      if (ks + 1 < GEMM_BK / 16) {
-        constexpr int NDS = C::TM + C::TN, NMF = C::TM * C::TN;
-#pragma unroll
-        for (int q = 0; q < NDS; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMF - NDS, 0);
-      }
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Three-stage ring: tiles kt+1 and kt+2 are in flight while tile kt is multiplied. Before
-  // each barrier a wave waits only until its loads of the next tile have landed (the loads of
-  // the tile after it may stay outstanding: vmcnt <= NA + NB), then the barrier publishes the
-  // tile to all waves. vmcnt counts this wave's vector-memory loads, which return in order.
-  constexpr int NDMA = NA + NB;
-  constexpr int WAIT_NEXT = (NDMA & 15) | (7 << 4) | (15 << 8) | ((NDMA >> 4) << 14);
+  // Three-stage ring; vmcnt counts this wave's vector-memory loads, which return in order, so
+  // "vmcnt <= loads of one tile" means the next tile's loads have landed.
+  constexpr int NDMA = C::NA + C::NB;
   static_assert(NDMA < 64, "vmcnt field");
+  constexpr int WAIT_NEXT = (NDMA & 15) | (7 << 4) | (15 << 8) | ((NDMA >> 4) << 14);
+  constexpr int WAIT_NEXT_LDS0 = (NDMA & 15) | (7 << 4) | (0 << 8) | ((NDMA >> 4) << 14);
+  constexpr int KS = BK / 16;  // k-steps per tile
+  // One k-tile, pipelined across the barrier that publishes the next tile: the last k-step's
+  // fragments are read (and waited for) before the barrier, so no wave still reads this stage
+  // when another wave's DMA overwrites it two tiles later; after the barrier the next tile's
+  // first fragments are read while the last k-step's MFMAs run from registers.
+  auto step = [&](const uint16_t *st, const uint16_t *st_next, int dma_kt, int dma_stage) {
+    issue_tile(dma_kt, dma_stage);
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      load_frags(st, ks + 1, (ks + 1) & 1);
+      mfma_step(ks & 1);
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT_LDS0);
+    __builtin_amdgcn_s_barrier();
+    load_frags(st_next, 0, 0);
+    mfma_step((KS - 1) & 1);
+  };
+  static_assert(((KS - 1) & 1) == 1, "the last k-step uses fragment buffer 1");
+
   constexpr int S0 = 0, S1 = C::STAGE, S2 = 2 * C::STAGE;
   issue_tile(0, S0);
   issue_tile(1, S1);
@@ -204,148 +219,139 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, EPI>::NT)) void gemm_kerne
   load_frags(lds + S0, 0, 0);
 #pragma unroll 1
   for (int kt = 0;; kt += 3) {
-    issue_tile(kt + 2, S2);
-    compute_tile(lds + S0);
-    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
-    __builtin_amdgcn_s_barrier();
-    load_frags(lds + S1, 0, 0);
+    step(lds + S0, lds + S1, kt + 2, S2);
     if (kt + 1 >= nk) break;
-    issue_tile(kt + 3, S0);
-    compute_tile(lds + S1);
-    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
-    __builtin_amdgcn_s_barrier();
-    load_frags(lds + S2, 0, 0);
+    step(lds + S1, lds + S2, kt + 3, S0);
     if (kt + 2 >= nk) break;
-    issue_tile(kt + 4, S1);
-    compute_tile(lds + S2);
-    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
-    __builtin_amdgcn_s_barrier();
-    load_frags(lds + S0, 0, 0);
+    step(lds + S2, lds + S0, kt + 4, S1);
     if (kt + 3 >= nk) break;
   }
-  __syncthreads();  // the last fragment reads are done before LDS is reused for the C tile
+  __syncthreads();  // all DMA landed and all fragment reads done before LDS holds the C tile
 
-  // --- epilogue: accumulators -> C tile in LDS ---
+  // --- epilogue, in NCH passes of RCH tile rows ---
   // Lane holds output row wm0 + 32i + r32 and columns (within its 32-block) 8(e/4) + 4gq + e%4.
-  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+  for (int ch = 0; ch < C::NCH; ++ch) {
+    const int r_lo = ch * C::RCH;
+    if (ch > 0) __syncthreads();  // previous pass's reads of the C tile are done
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
-      const int row = wm0 + 32 * i + r32;
+      const int row = wm0 + 32 * i + r32 - r_lo;  // row within this pass
+      if (wm0 + 32 * i < r_lo || wm0 + 32 * i >= r_lo + C::RCH) continue;
+      if (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int p = 0; p < C::TN / 2; ++p) {
-        const int colblk = (wn0 / 64 + p) * 32;  // output columns of this gate/up pair
+        for (int p = 0; p < C::TN / 2; ++p) {
+          const int colblk = (wn0 / 64 + p) * 32;  // output columns of this gate/up pair
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float v[4];
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float zg = acc[i][2 * p][4 * q4 + e];
-            const float zu = acc[i][2 * p + 1][4 * q4 + e];
-            v[e] = zg / (1.0f + __expf(-zg)) * zu;
+            for (int e = 0; e < 4; ++e) {
+              const float zg = acc[i][2 * p][4 * q4 + e];
+              const float zu = acc[i][2 * p + 1][4 * q4 + e];
+              v[e] = zg / (1.0f + __expf(-zg)) * zu;
+            }
+            u32x2 w2;
+            w2[0] = pack_bf16x2(v[0], v[1]);
+            w2[1] = pack_bf16x2(v[2], v[3]);
+            *(u32x2 *)(lds + row * C::CS + colblk + 8 * q4 + 4 * gq) = w2;
           }
-          const int col = colblk + 8 * q4 + 4 * gq;
-          u32x2 w2;
-          w2[0] = pack_bf16x2(v[0], v[1]);
-          w2[1] = pack_bf16x2(v[2], v[3]);
-          *(u32x2 *)(lds + row * C::CS + col) = w2;
         }
+      } else if (C::F32_TILE) {
+        float *lf = (float *)lds;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 v4;
+            v4[0] = acc[i][j][4 * q4];
+            v4[1] = acc[i][j][4 * q4 + 1];
+            v4[2] = acc[i][j][4 * q4 + 2];
+            v4[3] = acc[i][j][4 * q4 + 3];
+            *(f32x4 *)(lf + row * C::CS + wn0 + 32 * j + 8 * q4 + 4 * gq) = v4;
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            u32x2 w2;
+            w2[0] = pack_bf16x2(acc[i][j][4 * q4 + 0], acc[i][j][4 * q4 + 1]);
+            w2[1] = pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
+            *(u32x2 *)(lds + row * C::CS + wn0 + 32 * j + 8 * q4 + 4 * gq) = w2;
+          }
       }
     }
-  } else if (C::F32_TILE) {
-    float *lf = (float *)lds;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const int row = wm0 + 32 * i + r32;
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = wn0 + 32 * j + 8 * q4 + 4 * gq;
-          f32x4 v4;
-          v4[0] = acc[i][j][4 * q4];
-          v4[1] = acc[i][j][4 * q4 + 1];
-          v4[2] = acc[i][j][4 * q4 + 2];
-          v4[3] = acc[i][j][4 * q4 + 3];
-          *(f32x4 *)(lf + row * C::CS + col) = v4;
-        }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const int row = wm0 + 32 * i + r32;
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = wn0 + 32 * j + 8 * q4 + 4 * gq;
-          u32x2 w2;
-          w2[0] = pack_bf16x2(acc[i][j][4 * q4 + 0], acc[i][j][4 * q4 + 1]);
-          w2[1] = pack_bf16x2(acc[i][j][4 * q4 + 2], acc[i][j][4 * q4 + 3]);
-          *(u32x2 *)(lds + row * C::CS + col) = w2;
-        }
-      }
-    }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // --- epilogue: LDS C tile -> global, 8 columns per thread per step ---
-  constexpr int CPR = C::BN_OUT / 8;  // chunks per row
-  constexpr int CHUNKS = BM * CPR;
+    // LDS C rows -> global, 8 columns per thread per step
+    constexpr int CPRO = C::BN_OUT / 8;  // chunks per output row
+    constexpr int CHUNKS = C::RCH * CPRO;
 #pragma unroll 2
-  for (int id = tid; id < CHUNKS; id += C::NT) {
-    const int r = id / CPR, cc = id % CPR;
-    const int m = m0 + r, n = n0 + cc * 8;
-    if (m >= M || n >= n_out) continue;
-    if (EPI == EPI_RESIDUAL) {
-      const float *lf = (const float *)lds + r * C::CS + cc * 8;
-      const f32x4 f0 = *(const f32x4 *)lf, f1 = *(const f32x4 *)(lf + 4);
-      const int64_t xrow =
-          g.idx ? (int64_t)(m / g.k) * g.T + min(max(g.idx[m], 0), g.T - 1) : (int64_t)m;
-      uint16_t *xp = g.x + xrow * g.ldc + n;
-      const float *ap = g.a + (size_t)m * g.ldc + n;
-      const f32x4 a0 = *(const f32x4 *)ap, a1 = *(const f32x4 *)(ap + 4);
-      const u32x4 xv = *(const u32x4 *)xp;
-      const float gg = g.gate ? __fmul_rn(g.varsigma, g.gate[m]) : 0.f;
-      u32x4 yv;
+    for (int id = tid; id < CHUNKS; id += C::NT) {
+      const int r = id / CPRO, cc = id % CPRO;
+      const int m = m0 + r_lo + r, n = n0 + cc * 8;
+      if (m >= M || n >= n_out) continue;
+      if (EPI == EPI_RESIDUAL) {
+        const float *lf = (const float *)lds + r * C::CS + cc * 8;
+        const f32x4 f0 = *(const f32x4 *)lf, f1 = *(const f32x4 *)(lf + 4);
+        const int64_t xrow =
+            g.idx ? (int64_t)(m / g.k) * g.T + min(max(g.idx[m], 0), g.T - 1) : (int64_t)m;
+        uint16_t *xp = g.x + xrow * g.ldc + n;
+        const float *ap = g.a + (size_t)m * g.ldc + n;
+        const f32x4 a0 = *(const f32x4 *)ap, a1 = *(const f32x4 *)(ap + 4);
+        const u32x4 xv = *(const u32x4 *)xp;
+        const float gg = g.gate ? __fmul_rn(g.varsigma, g.gate[m]) : 0.f;
+        u32x4 yv;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float xlo = __uint_as_float(xv[h] << 16), xhi = __uint_as_float(xv[h] & 0xFFFF0000u);
-        const float alo = h < 2 ? a0[2 * h] : a1[2 * h - 4], ahi = h < 2 ? a0[2 * h + 1] : a1[2 * h - 3];
-        const float flo = h < 2 ? f0[2 * h] : f1[2 * h - 4], fhi = h < 2 ? f0[2 * h + 1] : f1[2 * h - 3];
-        const float ylo = g.gate ? gated_residual(xlo, gg, alo, flo) : dense_residual(xlo, alo, flo);
-        const float yhi = g.gate ? gated_residual(xhi, gg, ahi, fhi) : dense_residual(xhi, ahi, fhi);
-        yv[h] = pack_bf16x2(ylo, yhi);
+        for (int h = 0; h < 4; ++h) {
+          const float xlo = __uint_as_float(xv[h] << 16);
+          const float xhi = __uint_as_float(xv[h] & 0xFFFF0000u);
+          const float alo = h < 2 ? a0[2 * h] : a1[2 * h - 4];
+          const float ahi = h < 2 ? a0[2 * h + 1] : a1[2 * h - 3];
+          const float flo = h < 2 ? f0[2 * h] : f1[2 * h - 4];
+          const float fhi = h < 2 ? f0[2 * h + 1] : f1[2 * h - 3];
+          const float ylo = g.gate ? gated_residual(xlo, gg, alo, flo) : dense_residual(xlo, alo, flo);
+          const float yhi = g.gate ? gated_residual(xhi, gg, ahi, fhi) : dense_residual(xhi, ahi, fhi);
+          yv[h] = pack_bf16x2(ylo, yhi);
+        }
+        *(u32x4 *)xp = yv;
+      } else if (EPI == EPI_STORE_F32) {
+        const float *lf = (const float *)lds + r * C::CS + cc * 8;
+        float *cp = g.Cf + (size_t)m * g.ldc + n;
+        *(f32x4 *)cp = *(const f32x4 *)lf;
+        *(f32x4 *)(cp + 4) = *(const f32x4 *)(lf + 4);
+      } else {
+        *(u32x4 *)(g.C + (size_t)m * g.ldc + n) = *(const u32x4 *)(lds + r * C::CS + cc * 8);
       }
-      *(u32x4 *)xp = yv;
-    } else if (EPI == EPI_STORE_F32) {
-      const float *lf = (const float *)lds + r * C::CS + cc * 8;
-      float *cp = g.Cf + (size_t)m * g.ldc + n;
-      *(f32x4 *)cp = *(const f32x4 *)lf;
-      *(f32x4 *)(cp + 4) = *(const f32x4 *)(lf + 4);
-    } else {
-      *(u32x4 *)(g.C + (size_t)m * g.ldc + n) = *(const u32x4 *)(lds + r * C::CS + cc * 8);
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int EPI>
 static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
-  using C = GemmCfg<BM, BN, WM, WN, EPI>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, EPI>;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + C::BN_OUT - 1) / C::BN_OUT;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT), 0,
-                     s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT),
+                     0, s, g);
   return hipGetLastError();
 }
 
-// Tile choice: 256x128 (four 128x64 wave tiles) when there are enough tiles to fill the chip,
-// else 128x128 for small problems.
+#ifndef XMOD_GEMM_BK
+#define XMOD_GEMM_BK 64
+#endif
+
+// Tile choice: 256x128 (four 128x64 wave tiles) when there are enough tiles to give every
+// workgroup slot work, else 128x128 (four 64x64 wave tiles).
 template <int EPI>
 static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
+  constexpr int BK = XMOD_GEMM_BK;
+  constexpr int slots = BK == 32 ? 512 : 256;  // resident workgroups on 256 CUs
   const int half = EPI == EPI_SWIGLU ? 2 : 1;
-  const long t128 = (long)((g.M + 255) / 256) * ((g.N + 128 / half - 1) / (128 / half));
-  if (t128 >= 160) return run_gemm<256, 128, 128, 64, EPI>(g, s);
-  return run_gemm<128, 128, 64, 64, EPI>(g, s);
+  const long t_big = (long)((g.M + 255) / 256) * ((g.N + 128 / half - 1) / (128 / half));
+  if (t_big >= slots * 5 / 8) return run_gemm<256, 128, 128, 64, BK, EPI>(g, s);
+  return run_gemm<128, 128, 64, 64, BK, EPI>(g, s);
 }
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s) {
