@@ -233,7 +233,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
         sel = eq_seen < need;
         ++eq_seen;
       }
-      if (sel && pos < (uint32_t)k) {  // pos < k always holds; the test keeps writes in bounds
+      // Exactly k keys of the sequence pass (all keys above the threshold key, plus the first
+      // `need` equal to it), so pos < k; the bound is a cheap guarantee that idx is never
+      // overrun, not a selection rule.
+      if (sel && pos < (uint32_t)k) {
         I[pos] = p;
         if (G) G[pos] = 1.0f / (1.0f + expf(-L[p]));
         if (Bi) Bi[p] = __fadd_rn(Bi[p], delta);
