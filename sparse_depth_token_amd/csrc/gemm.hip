@@ -6,18 +6,18 @@
 // layout of v_mfma_f32_32x32x16_bf16: every lane reads 8 consecutive bf16 (16 bytes) of a row.
 //
 // Design (gfx950, wave64):
-//  * Workgroup tile BM x BN x BK, four waves in a 2 x 2 grid, each computing a WM x WN
-//    sub-tile as (WM/32) x (WN/32) MFMA 32x32x16 tiles (accumulators live in AGPRs).
+//  * Workgroup tile BM x BN x BK, four or eight waves in a grid, each computing a WM x WN
+//    sub-tile as (WM/32) x (WN/32) MFMA 32x32x16 tiles (fp32 accumulators in registers).
 //  * The weight fragment is the MFMA's first operand and the activation fragment its second,
 //    so each lane ends with 4 consecutive output columns of one row.
 //  * k-tiles are copied global -> LDS by the DMA form of the load (global_load_lds_dwordx4:
-//    16 bytes per lane, no staging registers) into a three-stage LDS ring: tiles kt+1 and kt+2
+//    16 bytes per lane, no staging registers) into an NS-stage LDS ring: tiles kt+1 .. kt+NS-1
 //    are in flight while tile kt is multiplied. Before each barrier a wave waits only for its
-//    own loads of the next tile. Operand fragments are double-buffered in registers, and a
-//    scheduling barrier closes every k-step so the MFMAs of one step run while the next step's
-//    fragments are read.
-//  * With BK = 32 a workgroup needs at most 72 KB of LDS and 256 registers per lane, so two
-//    workgroups share a CU and each covers the other's barrier bubbles.
+//    own loads of the next tile. The CU's vector-memory path moves 64 bytes per clock, so the
+//    copies are spread over the k-steps of a tile rather than issued in one burst.
+//  * Operand fragments are double-buffered in registers. Every k-step is laid out slot by slot
+//    (one MFMA per slot, scheduling barriers between slots): the next k-step's fragment reads
+//    go out in the first slots, the DMA copies in the later ones.
 //  * LDS rows (BK bf16) are split in 16-byte chunks, XOR-swizzled per row so that the lanes of
 //    one LDS cycle read distinct banks.
 //  * Workgroup ids are remapped so each XCD (own L2) works on a contiguous range of tiles, and
@@ -46,40 +46,42 @@ __device__ __forceinline__ int swz(int r) {
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
 struct GemmCfg {
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;            // elements per LDS stage
-  static constexpr int NSTAGE = 3;                           // LDS ring depth
+  static constexpr int NSTAGE = NS;                          // LDS ring depth
   static constexpr int CPR = BK / 8;                         // 16-byte chunks per LDS row
   static constexpr int RPB = 64 / CPR;                       // rows per 1 KB DMA block
-  static constexpr int NA = BM / RPB / 4, NB = BN / RPB / 4; // DMA blocks per wave per tile
+  static constexpr int NA = BM / RPB / NW, NB = BN / RPB / NW;  // DMA blocks per wave per tile
   static constexpr int BN_OUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
   static constexpr bool F32_TILE = EPI == EPI_STORE_F32 || EPI == EPI_RESIDUAL;
   static constexpr int ESZ = F32_TILE ? 4 : 2;
   static constexpr int CS = F32_TILE ? BN_OUT + 4 : BN_OUT + 8;  // C-tile row stride (elems)
   static constexpr int LDS_MAIN = NSTAGE * STAGE * 2;
-  // C-tile rows per epilogue pass (a multiple of 32, at most BM, fitting in the ring's LDS)
-  static constexpr int RCH_FIT = LDS_MAIN / (CS * ESZ) / 32 * 32;
-  static constexpr int RCH = RCH_FIT < BM ? RCH_FIT : BM;
+  // C-tile rows per epilogue pass: BM / 2^j, the largest that fits in the ring's LDS
+  static constexpr int RCH_FIT = LDS_MAIN / (CS * ESZ);
+  static constexpr int RCH = BM <= RCH_FIT ? BM : BM / 2 <= RCH_FIT ? BM / 2 : BM / 4 <= RCH_FIT ? BM / 4 : BM / 8;
   static constexpr int NCH = BM / RCH;
   static constexpr int LDS_BYTES = LDS_MAIN;
-  static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
-  static_assert(NT == 256, "four waves per workgroup");
+  // waves per SIMD: NW / 4 per workgroup, two workgroups per CU when the LDS allows it
+  static constexpr int WAVES_PER_EU = (NW / 4) * (LDS_BYTES <= 80 * 1024 ? 2 : 1);
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
-  static_assert(NA >= 1 && NB >= 1 && BM % (4 * RPB) == 0 && BN % (4 * RPB) == 0, "DMA blocks");
+  static_assert(NS >= 2, "at least one k-tile in flight");
+  static_assert(NA >= 1 && NB >= 1 && BM % (NW * RPB) == 0 && BN % (NW * RPB) == 0, "DMA blocks");
   static_assert(EPI != EPI_SWIGLU || WN % 64 == 0, "SwiGLU pairs gate/up 32-column blocks");
   static_assert(RCH >= 32 && BM % RCH == 0 && WM % 32 == 0, "epilogue row chunks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int BM, int BN, int WM, int WN, int BK, int EPI>
-__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, EPI>::NT),
-                             (GemmCfg<BM, BN, WM, WN, BK, EPI>::WAVES_PER_EU)) void
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
+__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI>::NT),
+                             (GemmCfg<BM, BN, WM, WN, BK, NS, EPI>::WAVES_PER_EU)) void
 gemm_kernel(GemmArgs g) {
-  using C = GemmCfg<BM, BN, WM, WN, BK, EPI>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -107,8 +109,8 @@ gemm_kernel(GemmArgs g) {
   const int n0 = tn * C::BN_OUT;  // first output column
 
   // --- DMA descriptors (rows fixed across k-tiles) ---
-  // 1 KB block b of a tile holds rows RPB*b .. RPB*b + RPB-1 and is filled by wave b % 4 with
-  // its instruction b / 4; lane l lands at byte 16*l, i.e. row RPB*b + l / CPR, physical chunk
+  // 1 KB block b of a tile holds rows RPB*b .. RPB*b + RPB-1 and is filled by wave b % NW with
+  // its instruction b / NW; lane l lands at byte 16*l, i.e. row RPB*b + l / CPR, physical chunk
   // l % CPR, so it fetches logical chunk (l % CPR) ^ swz(row). Element offsets fit in 32 bits
   // (every operand here holds fewer than 2^31 elements); the DMA takes byte offsets.
   const int nk = K / BK;
@@ -117,13 +119,13 @@ gemm_kernel(GemmArgs g) {
   uint32_t a_off[C::NA], b_off[C::NB];
 #pragma unroll
   for (int i = 0; i < C::NA; ++i) {
-    const int row = C::RPB * (4 * i + wv) + lane / C::CPR;
+    const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
     const int gm = min(m0 + row, M - 1);
     a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
   }
 #pragma unroll
   for (int i = 0; i < C::NB; ++i) {
-    const int row = C::RPB * (4 * i + wv) + lane / C::CPR;
+    const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
     // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
     int gn = EPI == EPI_SWIGLU ? n0 + (row >> 6) * 32 + (row & 31) : n0 + row;
     gn = min(gn, g.N - 1);
@@ -132,19 +134,24 @@ gemm_kernel(GemmArgs g) {
   const char *a_bytes = (const char *)g.A;
   const char *b_bytes[2] = {(const char *)g.B, (const char *)(EPI == EPI_SWIGLU ? g.B2 : g.B)};
   auto b_half = [&](int i) {  // which weight matrix DMA block i of B reads (SwiGLU: gate / up)
-    return EPI == EPI_SWIGLU ? (((C::RPB * (4 * i + wv)) >> 5) & 1) : 0;  // wave-uniform
+    return EPI == EPI_SWIGLU ? (((C::RPB * (C::NW * i + wv)) >> 5) & 1) : 0;  // wave-uniform
   };
   // Copy k-tile kt (clamped to the last one) into the stage at element offset `stage`.
-  auto issue_tile = [&](int kt, int stage) {
+  // Copies [lo, hi) of the tile's NA + NB DMA blocks (A blocks first) of k-tile kt, clamped to
+  // the last one, into the stage at element offset `stage`.
+  auto issue_part = [&](int kt, int stage, int lo, int hi) {
     const uint32_t kb = (uint32_t)min(kt, nk_last) * (BK * 2);
 #pragma unroll
     for (int i = 0; i < C::NA; ++i)
-      dma16(a_bytes + (a_off[i] + kb), lds + stage + C::RPB * (4 * i + wv) * BK);
+      if (i >= lo && i < hi)
+        dma16(a_bytes + (a_off[i] + kb), lds + stage + C::RPB * (C::NW * i + wv) * BK);
 #pragma unroll
     for (int i = 0; i < C::NB; ++i)
-      dma16(b_bytes[b_half(i)] + (b_off[i] + kb),
-            lds + stage + C::A_ELEMS + C::RPB * (4 * i + wv) * BK);
+      if (C::NA + i >= lo && C::NA + i < hi)
+        dma16(b_bytes[b_half(i)] + (b_off[i] + kb),
+              lds + stage + C::A_ELEMS + C::RPB * (C::NW * i + wv) * BK);
   };
+  auto issue_tile = [&](int kt, int stage) { issue_part(kt, stage, 0, C::NA + C::NB); };
 
   // --- fragment read offsets within a stage ---
   // Fragment rows are wm0 + 32i + r32 (A) and wn0 + 32j + r32 (B), with wm0, wn0 multiples of
@@ -164,67 +171,97 @@ gemm_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   bf16x8 fa[2][C::TM], fb[2][C::TN];
-  auto load_frags = [&](const uint16_t *st, int ks, int buf) {
+  // Fragment f of k-step ks of stage st into buffer buf, in first-use order of the MFMA loop
+  // below (row-major over (i, j)): A0, B0 .. B(TN-1), A1 .. A(TM-1).
+  auto load_frag = [&](const uint16_t *st, int ks, int buf, int f) {
     const int c_even = ((2 * ks + gq) ^ sw_lane) << 3;
     const int c_odd = BK == 64 ? c_even ^ 32 : c_even;
-    const uint16_t *pa0 = st + a_base + c_even, *pa1 = st + a_base + c_odd;
-    const uint16_t *pb0 = st + b_base + c_even, *pb1 = st + b_base + c_odd;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      fa[buf][i] = *(const bf16x8 *)(((i & 1) ? pa1 : pa0) + 32 * BK * i);
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      fb[buf][j] = *(const bf16x8 *)(((j & 1) ? pb1 : pb0) + 32 * BK * j);
+    if (f >= 1 && f <= C::TN) {
+      const int j = f - 1;
+      fb[buf][j] = *(const bf16x8 *)(st + b_base + ((j & 1) ? c_odd : c_even) + 32 * BK * j);
+    } else {
+      const int i = f == 0 ? 0 : f - C::TN;
+      fa[buf][i] = *(const bf16x8 *)(st + a_base + ((i & 1) ? c_odd : c_even) + 32 * BK * i);
+    }
   };
-  auto mfma_step = [&](int buf) {
+  constexpr int NMF = C::TM * C::TN, NFR = C::TM + C::TN;
+  constexpr int HALF = NMF / 2;
+  constexpr int FPS = (NFR + HALF - 1) / HALF;  // fragment reads per early slot
+
+  // NS-stage ring: while tile kt is multiplied, tiles kt+1 .. kt+NS-1 are in flight. vmcnt
+  // counts this wave's vector-memory loads, which complete in order, so "vmcnt <= loads of
+  // NS-2 tiles" means tile kt+1 has landed.
+  constexpr int NDMA = C::NA + C::NB;
+  constexpr int VM = (NS - 2) * NDMA;
+  static_assert(VM < 64, "vmcnt field");
+  constexpr int WAIT_NEXT = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
+  constexpr int WAIT_NEXT_LDS0 = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
+  constexpr int KS = BK / 16;  // k-steps per tile
+#ifndef XMOD_DMA_SPLIT
+#define XMOD_DMA_SPLIT (KS - 1)
+#endif
+  constexpr int SH = (NDMA + XMOD_DMA_SPLIT - 1) / XMOD_DMA_SPLIT;  // DMA blocks per k-step
+
+  // One k-step as NMF slots of one MFMA each, in a fixed order (a scheduling barrier closes
+  // every slot; each MFMA takes 8 passes, during which the wave issues the slot's other
+  // instructions). The next k-step's fragment reads go out in the first slots, so they land
+  // long before they are needed; the k-step's share [dma_lo, dma_hi) of the DMA copies goes
+  // out one or two per slot in the later slots, so copies never hold up MFMA issue for long.
+  // Left to itself the compiler sinks the fragment reads below the MFMAs and waits on them at
+  // the start of every k-step, and issues the copies in one burst.
+  auto kstep = [&](int buf, const uint16_t *ld_st, int ld_ks, int ld_buf, int dma_kt,
+                   int dma_stage, int dma_lo, int dma_hi) {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+    for (int t = 0; t < NMF; ++t) {
+      const int i = t / C::TN, j = t % C::TN;
+      acc[i][j] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        acc[i][j] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int f = t * FPS; f < (t + 1) * FPS; ++f)
+        if (f < NFR) load_frag(ld_st, ld_ks, ld_buf, f);
+      if (t >= HALF && dma_hi > dma_lo) {
+        const int per = (dma_hi - dma_lo + (NMF - HALF) - 1) / (NMF - HALF);
+        const int lo = dma_lo + (t - HALF) * per;
+        issue_part(dma_kt, dma_stage, lo, min(lo + per, dma_hi));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // Three-stage ring; vmcnt counts this wave's vector-memory loads, which return in order, so
-  // "vmcnt <= loads of one tile" means the next tile's loads have landed.
-  constexpr int NDMA = C::NA + C::NB;
-  static_assert(NDMA < 64, "vmcnt field");
-  constexpr int WAIT_NEXT = (NDMA & 15) | (7 << 4) | (15 << 8) | ((NDMA >> 4) << 14);
-  constexpr int WAIT_NEXT_LDS0 = (NDMA & 15) | (7 << 4) | (0 << 8) | ((NDMA >> 4) << 14);
-  constexpr int KS = BK / 16;  // k-steps per tile
   // One k-tile, pipelined across the barrier that publishes the next tile: the last k-step's
   // fragments are read (and waited for) before the barrier, so no wave still reads this stage
-  // when another wave's DMA overwrites it two tiles later; after the barrier the next tile's
-  // first fragments are read while the last k-step's MFMAs run from registers.
+  // when another wave's DMA overwrites it in the next step; after the barrier the next tile's
+  // first fragments are read while the last k-step's MFMAs run from registers. The DMA copies
+  // of tile dma_kt are spread over the k-steps before the barrier.
   auto step = [&](const uint16_t *st, const uint16_t *st_next, int dma_kt, int dma_stage) {
-    issue_tile(dma_kt, dma_stage);
 #pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      load_frags(st, ks + 1, (ks + 1) & 1);
-      mfma_step(ks & 1);
-    }
+    for (int ks = 0; ks < KS - 1; ++ks)
+      kstep(ks & 1, st, ks + 1, (ks + 1) & 1, dma_kt, dma_stage, ks * SH,
+            min((ks + 1) * SH, NDMA));
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT_LDS0);
     __builtin_amdgcn_s_barrier();
-    load_frags(st_next, 0, 0);
-    mfma_step((KS - 1) & 1);
+    kstep((KS - 1) & 1, st_next, 0, 0, 0, 0, 0, 0);
   };
   static_assert(((KS - 1) & 1) == 1, "the last k-step uses fragment buffer 1");
 
-  constexpr int S0 = 0, S1 = C::STAGE, S2 = 2 * C::STAGE;
-  issue_tile(0, S0);
-  issue_tile(1, S1);
+  // Tile kt lives in stage kt % NS. Step kt refills stage (kt - 1) % NS, read in step kt - 1
+  // and released by that step's barrier, with tile kt + NS - 1 (clamped to the last tile: the
+  // surplus copies land in stages no later step reads, and keep the vmcnt accounting uniform).
+  // One loop body with rotating stage offsets (kept in scalar registers): a single exit keeps
+  // the accumulators in one register assignment for the epilogue.
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
   __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
   __syncthreads();
-  load_frags(lds + S0, 0, 0);
+#pragma unroll
+  for (int f = 0; f < NFR; ++f) load_frag(lds, 0, 0, f);
+  int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
 #pragma unroll 1
-  for (int kt = 0;; kt += 3) {
-    step(lds + S0, lds + S1, kt + 2, S2);
-    if (kt + 1 >= nk) break;
-    step(lds + S1, lds + S2, kt + 3, S0);
-    if (kt + 2 >= nk) break;
-    step(lds + S2, lds + S0, kt + 4, S1);
-    if (kt + 3 >= nk) break;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st_next = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
+    step(lds + st_cur, lds + st_next, kt + NS - 1, st_dma);
+    st_dma = st_cur;
+    st_cur = st_next;
   }
   __syncthreads();  // all DMA landed and all fragment reads done before LDS holds the C tile
 
@@ -328,30 +365,32 @@ gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
 static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
-  using C = GemmCfg<BM, BN, WM, WN, BK, EPI>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI>;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + C::BN_OUT - 1) / C::BN_OUT;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT),
                      0, s, g);
   return hipGetLastError();
 }
 
-#ifndef XMOD_GEMM_BK
-#define XMOD_GEMM_BK 64
-#endif
-
-// Tile choice: 256x128 (four 128x64 wave tiles) when there are enough tiles to give every
-// workgroup slot work, else 128x128 (four 64x64 wave tiles).
+// Tile choice (measured on the projections of the X-MoD layer at 4096 routed rows):
+//  * SwiGLU with at least two waves of 256x256 tiles: 256x256 (eight waves of 128x64, two per
+//    SIMD, BK = 32, four-stage ring): the halved epilogue per flop and the second wave per SIMD
+//    beat 256x128 by ~5 %.
+//  * otherwise 256x128 (four waves of 128x64, BK = 64, three-stage ring) when the grid gives
+//    at least 5/8 of the 256 CUs a tile, else 128x128.
 template <int EPI>
 static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
-  constexpr int BK = XMOD_GEMM_BK;
-  constexpr int slots = BK == 32 ? 512 : 256;  // resident workgroups on 256 CUs
   const int half = EPI == EPI_SWIGLU ? 2 : 1;
+  if (EPI == EPI_SWIGLU) {
+    const long t_256 = (long)((g.M + 255) / 256) * ((g.N + 256 / half - 1) / (256 / half));
+    if (t_256 >= 512) return run_gemm<256, 256, 128, 64, 32, 4, EPI>(g, s);
+  }
   const long t_big = (long)((g.M + 255) / 256) * ((g.N + 128 / half - 1) / (128 / half));
-  if (t_big >= slots * 5 / 8) return run_gemm<256, 128, 128, 64, BK, EPI>(g, s);
-  return run_gemm<128, 128, 64, 64, BK, EPI>(g, s);
+  if (t_big >= 160) return run_gemm<256, 128, 128, 64, 64, 3, EPI>(g, s);
+  return run_gemm<128, 128, 64, 64, 64, 3, EPI>(g, s);
 }
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s) {

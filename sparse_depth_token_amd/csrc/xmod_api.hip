@@ -6,7 +6,7 @@
 
 #include <vector>
 
-#include "../../include/xmod.h"
+#include "xmod.h"
 #include "common.h"
 
 using namespace xmod;
