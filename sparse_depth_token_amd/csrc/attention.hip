@@ -6,36 +6,125 @@
 // 0-based). Softmax uses the scale 1/sqrt(head_dim) and the usual online recurrence (running
 // max, rescaled running sum and output), so the k x k score matrix is never stored.
 //
-// Work split: one workgroup = (q-tile of 128 packed rows, query head, sequence); its 4 waves
-// own 32 query rows each. Key/value tiles of 64 rows are staged in LDS: K row-major (padded),
-// V transposed (hd rows of 64 keys, padded) so that the P*V product reads 8 keys of one hd row
-// per lane. Scores are computed transposed, S^T = K Q^T, so that each lane holds one query's
-// scores: lane l owns query l % 32 and keys 8(e/4) + 4(l/32) + e%4 of each 32-key block. The
-// same lane then holds query l % 32 of O^T = V^T P^T, so the softmax statistics never leave
-// the lane pair (l, l ^ 32). The P fragment is fed as the second MFMA operand in the key
-// order the score accumulator already has; V^T is read in that same key order.
+// Work split: one workgroup = (pair of q-tiles of 128 packed rows, query head, sequence); its
+// 8 waves own 32 query rows each and share key/value tiles of 64 rows.
+//
+//  * K and V tiles are copied global -> LDS by the DMA form of the load (no staging registers)
+//    into a two-stage ring: tile j+1 is in flight while tile j is used. Both stay row-major
+//    ([key][hd]) with their 16-byte chunks XOR-swizzled per row.
+//  * Scores are computed transposed, S^T = K Q^T (K fragment first), so each lane holds one
+//    query's scores: lane l owns query l % 32 and keys 8(e/4) + 4(l/32) + e%4 of each 32-key
+//    block. The same lane then holds query l % 32 of O^T = V^T P^T, so the softmax statistics
+//    never leave the lane pair (l, l ^ 32).
+//  * The P fragment is the second MFMA operand, in the key order the score accumulator already
+//    has. The V^T fragment (hd rows, 8 keys per lane in that same order) comes straight from
+//    the row-major V tile through the transposing LDS read (ds_read_b64_tr_b16): within each
+//    16-lane group, lane 4a+b receives element b of the 8-byte reads of lanes 4e+a, e = 0..3,
+//    so lanes that address 4 consecutive keys at 4 consecutive hd offsets hand every lane 4
+//    keys of one hd column.
 #include "common.h"
 
 namespace xmod {
 
-template <int HD>
-__global__ __launch_bounds__(256) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
-                                                   uint16_t *__restrict__ o, int ldo, int k,
-                                                   int Hq, int Hkv, float scale_log2) {
-  constexpr int BQ = 128, BKV = 64, KS = HD / 16, NT_HD = HD / 32;
-  constexpr int KROW = HD + 8;   // K tile row stride (elements)
-  constexpr int VROW = BKV + 4;  // V^T row stride (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BKV * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * VROW];
 
+__device__ __forceinline__ void attn_dma16(const void *gsrc, uint16_t *lds_block) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_block, 16,
+                                   0, 0);
+}
+
+template <int HD>
+struct AttnCfg {
+  static constexpr int BQ = 128, BKV = 64, NW = 8, NT = 64 * NW;
+  static constexpr int CPR = HD / 8;              // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;            // rows per 1 KB DMA block
+  static constexpr int TILE = BKV * HD;           // elements of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;          // K then V
+  static constexpr int NBLK = 2 * TILE * 2 / 1024;  // 1 KB DMA blocks per stage (K and V)
+  static constexpr int NDMA = NBLK / NW;          // per wave
+  static_assert(NBLK % NW == 0, "DMA blocks split over the waves");
+  // K: 32 consecutive rows read one logical chunk (ds_read_b128), 16 lanes per LDS pass
+  // must hit distinct 16-byte bank groups.
+  static __device__ __forceinline__ int kswz(int r) {
+    return HD == 128 ? (r & 15) : ((r >> 1) & 7);
+  }
+  // V: a transposing read touches rows base..base+7 and 4 consecutive chunks 4t..4t+3;
+  // moving the chunk's upper bits with the row spreads the 32 (row, chunk) pairs evenly over
+  // the 64 banks.
+  static __device__ __forceinline__ int vswz(int r) {
+    return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
+};
+
+template <int HD>
+__global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
+                                                      uint16_t *__restrict__ o, int ldo, int k,
+                                                      int Hq, int Hkv, float scale_log2) {
+  using C = AttnCfg<HD>;
+  constexpr int BQ = C::BQ, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
+  // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
+  // it by more than 2^RESCALE_LOG2 (log2 units), so weights exp2(x - M) stay below 2^8 and most
+  // tiles skip the rescale of the running sum and output.
+  constexpr float RESCALE_LOG2 = 8.0f;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+
+  // Workgroup = pair (q-tile nqt-1-p, q-tile p): waves 0-3 take the later tile, waves 4-7 the
+  // earlier one (none when both are the same middle tile). Every workgroup then has the same
+  // causal work, each SIMD runs one wave of each tile, and the earlier tile's key/value tiles
+  // are a prefix of the later one's, so the pair loads them once.
   const int nqt = (k + BQ - 1) / BQ;
-  const int qt = nqt - 1 - (int)blockIdx.x;  // longest (latest) q-tiles first
+  const int p = (int)blockIdx.x;
+  const int qt_hi = nqt - 1 - p;
   const int h = blockIdx.y, b = blockIdx.z;
   const int gkv = (h * Hkv) / Hq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int gq = lane >> 5, r32 = lane & 31;
-  const int q_pos = qt * BQ + wid * 32 + r32;
+  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  const int half = wid >> 2;
+  const bool active = half == 0 || p != qt_hi;
+  const int qt = half == 0 ? qt_hi : p;
+  const int q_pos = qt * BQ + (wid & 3) * 32 + r32;
+  // the last query this wave owns (-1: nothing to do)
+  const int q_last_wave = active ? qt * BQ + (wid & 3) * 32 + 31 : -1;
   const int64_t row0 = (int64_t)b * k;
+
+  const int q_hi = min(qt_hi * BQ + BQ, k);
+  const int n_kv = (q_hi + BKV - 1) / BKV;
+  const char *kbase = (const char *)(qkv + row0 * ldq + Hq * HD + gkv * HD);
+  const char *vbase = kbase + (size_t)Hkv * HD * 2;
+
+  // DMA: block i of a stage (i < NBLK/2: K, else V) is filled by wave i % 4; lane l lands at
+  // byte 16 l, i.e. row RPB * (i mod NBLK/2) + l / CPR, physical chunk l % CPR. The byte
+  // offset of a lane's source within a tile is fixed; tiles advance by BKV rows.
+  uint32_t dma_off[C::NDMA];
+  int dma_row[C::NDMA], dma_lc[C::NDMA];
+#pragma unroll
+  for (int n = 0; n < C::NDMA; ++n) {
+    const int i = C::NW * n + wv;
+    const bool is_v = i >= C::NBLK / 2;
+    const int blk = is_v ? i - C::NBLK / 2 : i;
+    dma_row[n] = C::RPB * blk + lane / C::CPR;
+    dma_lc[n] = (lane % C::CPR) ^ (is_v ? C::vswz(dma_row[n]) : C::kswz(dma_row[n]));
+    dma_off[n] = (uint32_t)dma_row[n] * (uint32_t)ldq * 2u + (uint32_t)dma_lc[n] * 16u;
+  }
+  auto issue_tile = [&](int jt, int stage) {
+    const size_t tile_bytes = (size_t)jt * BKV * ldq * 2;
+    const bool ragged = jt * BKV + BKV > k;  // rows past the sequence read its last row
+#pragma unroll
+    for (int n = 0; n < C::NDMA; ++n) {
+      const int i = C::NW * n + wv;
+      const bool is_v = i >= C::NBLK / 2;
+      const int blk = is_v ? i - C::NBLK / 2 : i;
+      uint32_t off = dma_off[n];
+      if (ragged) {
+        const int row = min(dma_row[n], k - 1 - jt * BKV);
+        off = (uint32_t)row * (uint32_t)ldq * 2u + (uint32_t)dma_lc[n] * 16u;
+      }
+      attn_dma16((is_v ? vbase : kbase) + tile_bytes + off,
+                 lds + stage + (is_v ? C::TILE : 0) + C::RPB * blk * HD);
+    }
+  };
+
+  issue_tile(0, 0);
 
   bf16x8 qf[KS];
   {
@@ -49,127 +138,200 @@ __global__ __launch_bounds__(256) void attn_kernel(const uint16_t *__restrict__ 
   for (int t = 0; t < NT_HD; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // m_ref in log2 units (score * scale_log2)
 
-  const int q_hi = min(qt * BQ + BQ, k);
-  const int n_kv = (q_hi + BKV - 1) / BKV;
-  const uint16_t *kbase = qkv + row0 * ldq + Hq * HD + gkv * HD;
-  const uint16_t *vbase = kbase + Hkv * HD;
+  // K fragment offsets (elements, within a stage): row t*32 + r32, logical chunk 2s + gq
+  int k_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) k_off[s] = r32 * HD + (((2 * s + gq) ^ C::kswz(r32)) * 8);
+  // Transposing-read byte offsets (within a stage's V tile): this lane, as the source of an
+  // 8-byte read, addresses key row 16 s + 4 (g >> 1) + e (+ 8 for keys 4..7) and hd column
+  // 32 t + 16 (g & 1) + 4 a, g = lane / 16, e = lane / 4 % 4, a = lane % 4. The swizzle of
+  // those rows depends on the lane only, so (s, half) go into the instruction's offset.
+  const int tg = lane >> 4, te = (lane >> 2) & 3, ta = lane & 3;
+  const int v_row = 4 * (tg >> 1) + te;
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)lds;
+  uint32_t v_off[NT_HD];
+#pragma unroll
+  for (int t = 0; t < NT_HD; ++t) {
+    const int col = 32 * t + 16 * (tg & 1) + 4 * ta;
+    v_off[t] = 2u * (uint32_t)(C::TILE + v_row * HD + ((col >> 3) ^ C::vswz(v_row)) * 8 + (col & 7));
+  }
+  static_assert(HD == 128 || HD == 64, "swizzle of V rows depends on row % 4 (HD 128) or row % 4 / 2 (HD 64)");
+
+  __builtin_amdgcn_s_waitcnt(0);  // tile 0 and the Q fragments
+  __syncthreads();
 
 #pragma unroll 1
   for (int jt = 0; jt < n_kv; ++jt) {
+    const int st = (jt & 1) * C::STAGE;
+    if (jt + 1 < n_kv) issue_tile(jt + 1, C::STAGE - st);
+    const uint16_t *Ks = lds + st;
     const int key0 = jt * BKV;
-    __syncthreads();
-    // K tile: 64 keys x HD, 16-byte chunks
+    // a tile that starts after this wave's last query contributes nothing to it
+    if (key0 <= q_last_wave) {
+      // S^T[key, query] for 64 keys x this wave's 32 queries. The K fragments of the second
+      // 32-key block are read while the first block's MFMAs run.
+      f32x16 sacc[2];
+      bf16x8 kf[KS];
 #pragma unroll
-    for (int c = tid; c < BKV * HD / 8; c += 256) {
-      const int r = c / (HD / 8), ch = c % (HD / 8);
-      const int key = min(key0 + r, k - 1);
-      *(uint4 *)(Ks + r * KROW + ch * 8) = *(const uint4 *)(kbase + (int64_t)key * ldq + ch * 8);
-    }
-    // V tile transposed: a thread takes two adjacent keys x 8 hd and writes 8 key pairs.
+      for (int s = 0; s < KS; ++s) kf[s] = *(const bf16x8 *)(Ks + k_off[s]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = tid; c < (BKV / 2) * (HD / 8); c += 256) {
-      const int rp = c / (HD / 8), ch = c % (HD / 8);
-      const int k0 = min(key0 + 2 * rp, k - 1), k1 = min(key0 + 2 * rp + 1, k - 1);
-      const uint4 v0 = *(const uint4 *)(vbase + (int64_t)k0 * ldq + ch * 8);
-      const uint4 v1 = *(const uint4 *)(vbase + (int64_t)k1 * ldq + ch * 8);
-      const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (a0[e] & 0xFFFFu) | (a1[e] << 16);
-        const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xFFFF0000u);
-        *(uint32_t *)(Vt + (ch * 8 + 2 * e) * VROW + 2 * rp) = lo;
-        *(uint32_t *)(Vt + (ch * 8 + 2 * e + 1) * VROW + 2 * rp) = hi;
+        for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc[t], 0, 0, 0);
+          if (t == 0) kf[s] = *(const bf16x8 *)(Ks + 32 * HD + k_off[s]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    __syncthreads();
+      // The first 16-key step's V fragments are read while the softmax runs.
+      u32x2 vr[2][NT_HD][2];
+      const uint32_t v_st = lds_base + 2u * (uint32_t)st;
+      auto issue_v = [&](int s, int buf) {
+#pragma unroll
+        for (int t = 0; t < NT_HD; ++t) {
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                       : "=v"(vr[buf][t][0])
+                       : "v"(v_st + v_off[t]), "i"(2 * 16 * HD * s));
+          asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                       : "=v"(vr[buf][t][1])
+                       : "v"(v_st + v_off[t]), "i"(2 * (16 * s + 8) * HD));
+        }
+      };
+      issue_v(0, 0);
 
-    // S^T[key, query] for 64 keys x this wave's 32 queries
-    f32x16 sacc[2];
+      // causal mask only where the tile reaches past the wave's first query or the sequence
+      if (key0 + BKV - 1 > q_last_wave - 31 || key0 + BKV > k) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = *(const bf16x8 *)(Ks + (t * 32 + r32) * KROW + s * 16 + gq * 8);
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + t * 32 + 8 * (e >> 2) + 4 * gq + (e & 3);
+            if (key > q_pos || key >= k) sacc[t][e] = -INFINITY;
+          }
       }
-    }
-    // causal mask and online softmax (statistics shared by lanes l and l^32)
-    float mt = -INFINITY;
+      // online softmax in log2 units (statistics shared by lanes l and l^32)
+      float mt = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + t * 32 + 8 * (e >> 2) + 4 * gq + (e & 3);
-        if (key > q_pos || key >= k) sacc[t][e] = -INFINITY;
-        mt = fmaxf(mt, sacc[t][e]);
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[t][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m_ref + RESCALE_LOG2)) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float corr = __builtin_amdgcn_exp2f(m_ref - m_new);  // exp2(-inf) = 0
+        l_run *= corr;
+#pragma unroll
+        for (int t = 0; t < NT_HD; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[t][e] *= corr;
+        m_ref = m_new;
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float corr = exp2f((m_run - m_new) * scale_log2);
-    const float mb = m_new * scale_log2;
-    float psum = 0.f;
+      float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(fmaf(sacc[t][e], scale_log2, -mb));
-        sacc[t][e] = p;
-        psum += p;
-      }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < NT_HD; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[t][e] *= corr;
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], scale_log2, -m_ref));
+          sacc[t][e] = p;
+          psum += p;
+        }
+      l_run += psum;
 
-    // O^T[hd, query] += V^T[hd, key] P^T[key, query], 16 keys per MFMA
+      // O^T[hd, query] += V^T[hd, key] P^T[key, query], 16 keys per MFMA. The transposing
+      // reads are issued as inline assembly, one 16-key step ahead of their MFMAs, and waited
+      // for explicitly: the compiler's own form of this read is ordered behind every pending
+      // DMA copy, which would stall the wave on the next tile's copies here.
 #pragma unroll
-    for (int s = 0; s < BKV / 16; ++s) {
-      bf16x8 pf;
+      for (int s = 0; s < BKV / 16; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < BKV / 16) {
+          issue_v(s + 1, buf ^ 1);
+          // all but the 2 * NT_HD reads just issued have completed
+          if (NT_HD == 4)
+            asm volatile("s_waitcnt lgkmcnt(8)"
+                         : "+v"(vr[buf][0][0]), "+v"(vr[buf][0][1]), "+v"(vr[buf][1][0]),
+                           "+v"(vr[buf][1][1]), "+v"(vr[buf][2 % NT_HD][0]),
+                           "+v"(vr[buf][2 % NT_HD][1]), "+v"(vr[buf][3 % NT_HD][0]),
+                           "+v"(vr[buf][3 % NT_HD][1]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(4)"
+                         : "+v"(vr[buf][0][0]), "+v"(vr[buf][0][1]), "+v"(vr[buf][1][0]),
+                           "+v"(vr[buf][1][1]));
+        } else {
+          if (NT_HD == 4)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(vr[buf][0][0]), "+v"(vr[buf][0][1]), "+v"(vr[buf][1][0]),
+                           "+v"(vr[buf][1][1]), "+v"(vr[buf][2 % NT_HD][0]),
+                           "+v"(vr[buf][2 % NT_HD][1]), "+v"(vr[buf][3 % NT_HD][0]),
+                           "+v"(vr[buf][3 % NT_HD][1]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(vr[buf][0][0]), "+v"(vr[buf][0][1]), "+v"(vr[buf][1][0]),
+                           "+v"(vr[buf][1][1]));
+        }
+        bf16x8 pf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = (__bf16)sacc[s >> 1][8 * (s & 1) + j];
+        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)sacc[s >> 1][8 * (s & 1) + j];
 #pragma unroll
-      for (int t = 0; t < NT_HD; ++t) {
-        const uint16_t *vr = Vt + (t * 32 + r32) * VROW + 16 * s + 4 * gq;
-        const uint2 lo = *(const uint2 *)vr;
-        const uint2 hi = *(const uint2 *)(vr + 8);
-        const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        bf16x8 vf;
-        __builtin_memcpy(&vf, &vv, 16);
-        oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
+        for (int t = 0; t < NT_HD; ++t) {
+          bf16x8 vf;
+          __builtin_memcpy(&vf, &vr[buf][t][0], 8);
+          __builtin_memcpy((char *)&vf + 8, &vr[buf][t][1], 8);
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
+        }
       }
     }
+    // the next tile's copies (this wave's) have landed; then every wave's have, and every wave
+    // is done reading this stage before it is refilled
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    __syncthreads();
   }
 
+  // Epilogue: O = O^T / l, staged through LDS (the ring is free after the last barrier; each
+  // wave owns 32 rows x HD, 16-byte chunks XOR-swizzled by row) so that global stores are
+  // whole row segments. Written straight from the MFMA layout, every store instruction would
+  // touch 32 rows with 16 bytes each, which the memory system handles far below its rate.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
-  if (q_pos < k) {
-    uint16_t *op = o + (row0 + q_pos) * ldo + h * HD;
+  if (active) {
+    uint16_t *ow = lds + wid * 32 * HD;
 #pragma unroll
     for (int t = 0; t < NT_HD; ++t)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int hd = t * 32 + 8 * q4 + 4 * gq;
-        *(uint2 *)(op + hd) = make_uint2(pack_bf16x2(oacc[t][4 * q4] * inv, oacc[t][4 * q4 + 1] * inv),
-                                         pack_bf16x2(oacc[t][4 * q4 + 2] * inv, oacc[t][4 * q4 + 3] * inv));
+        const int c = 4 * t + q4;  // 16-byte chunk of hd 32t + 8q4 .. +7
+        *(uint2 *)(ow + r32 * HD + ((c ^ (r32 & (C::CPR - 1))) * 8) + 4 * gq) =
+            make_uint2(pack_bf16x2(oacc[t][4 * q4] * inv, oacc[t][4 * q4 + 1] * inv),
+                       pack_bf16x2(oacc[t][4 * q4 + 2] * inv, oacc[t][4 * q4 + 3] * inv));
       }
+    // the same wave reads back: LDS operations of one wave complete in order
+    constexpr int RPI = 64 / C::CPR;  // rows per store instruction
+    const int q0 = qt * BQ + (wid & 3) * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + lane / C::CPR, c = lane % C::CPR;
+      const uint4 v = *(const uint4 *)(ow + r * HD + ((c ^ (r & (C::CPR - 1))) * 8));
+      if (q0 + r < k) *(uint4 *)(o + (row0 + q0 + r) * ldo + h * HD + c * 8) = v;
+    }
   }
 }
 
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
                             int Hq, int Hkv, int hd, hipStream_t s) {
-  const dim3 grid((unsigned)((k + 127) / 128), (unsigned)Hq, (unsigned)B);
+  const int nqt = (k + 127) / 128;
+  const dim3 grid((unsigned)((nqt + 1) / 2), (unsigned)Hq, (unsigned)B);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 128)
-    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(256), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
+    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
                        scale_log2);
   else
-    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(256), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
+    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
                        scale_log2);
   return hipGetLastError();
 }

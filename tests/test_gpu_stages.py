@@ -206,7 +206,9 @@ def test_gemm(x, M, N, K):
 
 
 @pytest.mark.parametrize("B,k,Hq,Hkv,hd", [(2, 256, 4, 4, 64), (1, 333, 4, 2, 128), (3, 200, 8, 2, 64),
-                                           (2, 512, 16, 16, 128), (1, 1100, 4, 1, 128)])
+                                           (2, 512, 16, 16, 128), (1, 1100, 4, 1, 128),
+                                           (1, 1, 2, 1, 128), (2, 65, 4, 4, 64), (1, 129, 2, 2, 128),
+                                           (1, 64, 2, 2, 64)])
 def test_attention(x, B, k, Hq, Hkv, hd):
     say(f"[attention] B{B} k{k} Hq{Hq} Hkv{Hkv} hd{hd}")
     rng = np.random.default_rng(13)
