@@ -381,15 +381,18 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
 //    beat 256x128 by ~5 %.
 //  * otherwise 256x128 (four waves of 128x64, BK = 64, three-stage ring) when the grid gives
 //    at least 5/8 of the 256 CUs a tile, else 128x128.
+constexpr int GEMM_CUS = 256;
+
 template <int EPI>
 static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
   const int half = EPI == EPI_SWIGLU ? 2 : 1;
+  const long tm = (g.M + 255) / 256;
   if (EPI == EPI_SWIGLU) {
-    const long t_256 = (long)((g.M + 255) / 256) * ((g.N + 256 / half - 1) / (256 / half));
-    if (t_256 >= 512) return run_gemm<256, 256, 128, 64, 32, 4, EPI>(g, s);
+    const long t_256 = tm * ((g.N + 256 / half - 1) / (256 / half));
+    if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI>(g, s);
   }
-  const long t_big = (long)((g.M + 255) / 256) * ((g.N + 128 / half - 1) / (128 / half));
-  if (t_big >= 160) return run_gemm<256, 128, 128, 64, 64, 3, EPI>(g, s);
+  const long t_big = tm * ((g.N + 128 / half - 1) / (128 / half));
+  if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 128, 64, 64, 3, EPI>(g, s);
   return run_gemm<128, 128, 64, 64, 64, 3, EPI>(g, s);
 }
 

@@ -111,18 +111,11 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Add each lane's digit to the LDS histogram, one atomic per distinct digit in the wave
-// (router logits share their top bits, so plain per-lane atomics would serialise).
-__device__ __forceinline__ void wave_hist_add(uint32_t *hist, uint32_t dg, bool cand) {
-  uint64_t active = __ballot(cand);
-  const int lane = threadIdx.x & 63;
-  while (active) {
-    const int leader = __ffsll((unsigned long long)active) - 1;
-    const uint32_t dl = __shfl(dg, leader, 64);
-    const uint64_t same = __ballot(cand && dg == dl);
-    if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
-    active &= ~same;
-  }
+// Add each candidate lane's digit to the LDS histogram. LDS atomics on the same address
+// within one instruction are serialised by the LDS itself, which is far cheaper than
+// aggregating equal digits in the wave first (a ballot / shuffle round per distinct digit).
+__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t dg, bool cand) {
+  if (cand) atomicAdd(&hist[dg], 1u);
 }
 
 template <int KPT>
@@ -130,8 +123,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
                                                     int32_t *__restrict__ idx,
                                                     float *__restrict__ gate,
                                                     float *__restrict__ bias, float delta) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_remaining;
+  __shared__ uint32_t hist[4][256];  // one histogram per pass: a single barrier per pass
   __shared__ unsigned long long s_wave_tot[16];
 
   const int b = blockIdx.x;
@@ -139,58 +131,67 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
   const float *L = logits + (int64_t)b * T;
   const int p0 = tid * KPT;
 
+  hist[tid >> 8][tid & 255] = 0u;
+  // The logits (for the gate) and carried bias values of this thread's positions are loaded
+  // up front, so the output phase waits on no global read.
+  float* const Bi = bias ? bias + (int64_t)b * T : nullptr;
   uint32_t key[KPT];
+  float lv[KPT], bv[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int p = p0 + j;
-    key[j] = p < T ? order_key(L[p]) : 0u;
+    lv[j] = p < T ? L[p] : 0.f;
+    bv[j] = (Bi && p < T) ? Bi[p] : 0.f;
+    key[j] = p < T ? order_key(lv[j]) : 0u;
   }
+  __syncthreads();
 
-  // Radix select of the k-th largest key, 8 bits per pass from the top.
+  // Radix select of the k-th largest key, 8 bits per pass from the top. After each pass's
+  // barrier every wave scans that pass's histogram itself (no broadcast, no second barrier).
   uint32_t prefix = 0u, pmask = 0u, remaining = (uint32_t)k;
-#pragma unroll 1
+#pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const bool cand = (p0 + j < T) && ((key[j] & pmask) == prefix);
-      wave_hist_add(hist, (key[j] >> shift) & 255u, cand);
+      hist_add(hist[pass], (key[j] >> shift) & 255u, cand);
     }
     __syncthreads();
-    if (wid == 0) {
-      // lane l owns bins 255-4l .. 252-4l, scanned from the top (largest digit first)
-      uint32_t c[4], tot = 0;
+    // lane l owns bins 255-4l .. 252-4l, scanned from the top (largest digit first)
+    uint32_t c[4], tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hist[pass][255 - 4 * lane - q];
+      tot += c[q];
+    }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const uint32_t excl = incl - tot;
+    // exactly one lane holds the bin where the running count reaches `remaining`
+    uint32_t digit = 0u, rem_new = 0u;
+    const bool mine = excl < remaining && remaining <= incl;
+    if (mine) {
+      uint32_t above = excl;
+      bool found = false;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * lane - q];
-        tot += c[q];
-      }
-      uint32_t incl = tot;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
-      const uint32_t excl = incl - tot;
-      if (excl < remaining && remaining <= incl) {
-        uint32_t above = excl;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (remaining <= above + c[q]) {
-            s_digit = 255u - 4u * lane - q;
-            s_remaining = remaining - above;
-            break;
-          }
-          above += c[q];
+        if (!found && remaining <= above + c[q]) {
+          digit = 255u - 4u * lane - q;
+          rem_new = remaining - above;
+          found = true;
         }
+        if (!found) above += c[q];
       }
     }
-    __syncthreads();
-    const uint32_t dsel = s_digit;
-    remaining = s_remaining;
-    prefix |= dsel << shift;
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    digit = __shfl(digit, src, 64);
+    remaining = __shfl(rem_new, src, 64);
+    prefix |= digit << shift;
     pmask |= 255u << shift;
   }
   const uint32_t thr = prefix;     // key of the k-th largest
@@ -223,7 +224,6 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
 
   int32_t *I = idx + (int64_t)b * k;
   float *G = gate ? gate + (int64_t)b * k : nullptr;
-  float *Bi = bias ? bias + (int64_t)b * T : nullptr;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int p = p0 + j;
@@ -238,8 +238,8 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
       // overrun, not a selection rule.
       if (sel && pos < (uint32_t)k) {
         I[pos] = p;
-        if (G) G[pos] = 1.0f / (1.0f + expf(-L[p]));
-        if (Bi) Bi[p] = __fadd_rn(Bi[p], delta);
+        if (G) G[pos] = 1.0f / (1.0f + expf(-lv[j]));
+        if (Bi) Bi[p] = __fadd_rn(bv[j], delta);
         ++pos;
       }
     }

@@ -189,7 +189,9 @@ def test_rmsnorm_rows(x, B, T, d, k, use_idx):
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K", [(512, 768, 256), (300, 200, 128), (4096, 2048, 2048),
-                                   (1000, 1536, 1024), (8192, 6144, 512)])
+                                   (1000, 1536, 1024), (8192, 6144, 512),
+                                   # wide grids: several waves of 256x128 tiles, ragged rows
+                                   (4096, 6144, 128), (3900, 6144, 192)])
 def test_gemm(x, M, N, K):
     say(f"[gemm] M{M} N{N} K{K}")
     rng = np.random.default_rng(12)
