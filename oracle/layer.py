@@ -6,7 +6,8 @@ Sources (cited by page title and section / equation):
   [XMOD] "X-MoD: Practical Scaling Laws for Sparse-Depth Routing Beyond Mixture-of-Depths",
          close-reading page. Sections "X-MoD: decoupling token sparsity K and anchor stride A"
          (Eqs. (3)-(5), Fig. 1(b)), "three stabilisers" (Eqs. (6)-(8)), "training-time top-k",
-         "backbone configuration" (Table 4), "mechanism controls" (Table 7).
+         "backbone configuration" (Table 4), "mechanism controls" (Table 7), "training-time
+         top-k, eval-time causal threshold", "routing diagnostics" (Table 10).
   [MOD]  "Mixture-of-Depths explained" blog page, section "basic architecture" (the MoDLayer
          sketch: scalar Linear(d, 1) router, top-k of int(T * ratio) tokens, RMSNorm before
          attention and before the FFN, skipped rows passed through).
@@ -23,6 +24,9 @@ Readings taken where the pages are silent or ambiguous (all listed in the design doc)
   * FFN input is RMSNorm(X + a) (sequential pre-norm); output y = X + varsigma*r*(a + f).
   * The bias update b[S] += delta happens after the gate is read.
   * Softmax scale 1/sqrt(head_dim); GQA head h uses KV head floor(h*Hkv/Hq) (0-based).
+  * Eval-time threshold routing: the probability that is compared with 1/2 is the gate of
+    Eq. (8), sigmoid(s - tau*b) (the pages' routing diagnostics run threshold-driven forwards
+    with and without the carried bias and get different coverage), decided as ell >= 0.
 """
 from __future__ import annotations
 
@@ -158,8 +162,45 @@ def _attn_ffn_on_rows(X, lay, dims, out_rows):
 
 # --- the Sparse(K) layer: [XMOD] Fig. 1(b), Eqs. (7)-(8) ---------------------------------------
 
+def _routed_layer(x, lay, dims, ell, sel, bias, delta, sample):
+    """The routed part of a sparse layer for given selections sel[b] (ascending positions).
+
+    gate r = sigmoid(ell) on the selected tokens; attention and FFN over the packed selected
+    rows only; y_S = X + varsigma * r * (a + f) ([XMOD] Eq. (7)); unselected rows y = x
+    (Fig. 1(b), skip path); then b[S] += delta in fp32. sample: None or {b: packed rows}.
+    """
+    B = x.shape[0]
+    gate = [sigmoid(ell[b, sel[b]]) for b in range(B)]
+    bias_out = bias.copy()
+    for b in range(B):
+        bias_out[b, sel[b]] = (bias[b, sel[b]] + np.float32(delta)).astype(np.float32)
+    vs = float(lay.get("varsigma", 1.0))
+    res = {"gate": gate, "bias_out": bias_out}
+    seqs = range(B) if sample is None else sorted(sample)
+    y = x.copy() if sample is None else None
+    rows = {}
+    for b in seqs:
+        if len(sel[b]) == 0:
+            continue
+        X = x[b, sel[b]]                                      # packed, ascending position
+        out_rows = np.arange(len(sel[b])) if sample is None else np.asarray(sample[b])
+        if len(out_rows) == 0:
+            continue
+        a, f = _attn_ffn_on_rows(X, lay, dims, out_rows)
+        y_sel = X[out_rows] + (vs * gate[b][out_rows])[:, None] * (a + f)
+        if sample is None:
+            y[b, sel[b]] = y_sel
+        else:
+            rows[b] = (out_rows, sel[b][out_rows], y_sel)
+    if sample is None:
+        res["y"] = y
+    else:
+        res["rows"] = rows
+    return res
+
+
 def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None, sample=None):
-    """Forward of one X-MoD Sparse(K) layer.
+    """Forward of one X-MoD Sparse(K) layer with the training-time top-k selection.
 
     x: [B, T, d] bf16 bits or float64 values. lay: dict of layer weights (bf16 bits) plus
     "router_bias" and "varsigma". bias: fp32 [B, T] carried bias or None (zeros).
@@ -184,32 +225,69 @@ def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None
     bias = np.asarray(bias, dtype=np.float32)
     s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
     idx = topk_select(ell, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
-    bsel = np.arange(B)[:, None]
-    gate = sigmoid(ell[bsel, idx])
-    bias_out = bias.copy()
-    bias_out[bsel, idx] = (bias[bsel, idx] + np.float32(delta)).astype(np.float32)
-    vs = float(lay.get("varsigma", 1.0))
-
-    res = {"s": s, "ell": ell, "idx": idx, "gate": gate, "bias_out": bias_out}
-    seqs = range(B) if sample is None else sorted(sample)
-    if sample is None:
-        y = x.copy()
-    else:
-        rows = {}
-    for b in seqs:
-        X = x[b, idx[b]]                                       # packed, ascending position
-        out_rows = np.arange(k) if sample is None else np.asarray(sample[b])
-        a, f = _attn_ffn_on_rows(X, lay, dims, out_rows)
-        y_sel = X[out_rows] + (vs * gate[b, out_rows])[:, None] * (a + f)
-        if sample is None:
-            y[b, idx[b]] = y_sel
-        else:
-            rows[b] = (out_rows, idx[b, out_rows], y_sel)
-    if sample is None:
-        res["y"] = y
-    else:
-        res["rows"] = rows
+    res = _routed_layer(x, lay, dims, ell, [idx[b] for b in range(B)], bias, delta, sample)
+    res.update({"s": s, "ell": ell, "idx": idx, "gate": np.stack(res["gate"])})
     return res
+
+
+# --- eval-time causal threshold routing: [XMOD] "training-time top-k, eval-time causal threshold"
+
+def threshold_select(ell):
+    """Per sequence, the tokens whose routing probability sigmoid(ell) is at least 1/2.
+
+    sigmoid(ell) >= 1/2 exactly when ell >= 0, so the rule is taken on the fp32 logit itself
+    (-0 counts as 0); it is causal, each token's decision reads only its own logit. Returns a
+    list of int64 arrays of ascending positions, one per sequence (possibly empty).
+    """
+    ell = np.asarray(ell, dtype=np.float32)
+    assert np.all(np.isfinite(ell)), "router logits must be finite"
+    return [np.nonzero(ell[b] >= 0)[0].astype(np.int64) for b in range(ell.shape[0])]
+
+
+def sparse_layer_threshold(x, lay, dims, bias=None, tau=1.0, delta=0.0, sample=None):
+    """Forward of one sparse layer with the eval-time causal threshold rule.
+
+    Identical to sparse_layer except for the selection: every token with ell = s - tau*b >= 0
+    enters (Eq. (8)'s r = sigmoid(ell) >= 1/2), so each sequence routes its own number of
+    tokens k_b (0 .. T). The carried bias is updated on the selected tokens as in training.
+
+    Returns a dict with s, ell, idx (list of int64 arrays), counts (int64 [B]), gate (list),
+    bias_out, and y or rows (as sparse_layer; sample: {b: packed rows of that sequence}).
+    """
+    x = _f64(x)
+    B, T, d = x.shape
+    if bias is None:
+        bias = np.zeros((B, T), dtype=np.float32)
+    bias = np.asarray(bias, dtype=np.float32)
+    s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
+    sel = threshold_select(ell)
+    res = _routed_layer(x, lay, dims, ell, sel, bias, delta, sample)
+    res.update({"s": s, "ell": ell, "idx": sel,
+                "counts": np.array([len(v) for v in sel], dtype=np.int64)})
+    return res
+
+
+def mask_agreement(ell, idx):
+    """Mask agreement of [XMOD] "routing diagnostics" (Table 10) for one sparse layer.
+
+    From the same routing scores ell, the top-k mask (positions idx [B, k]) and the threshold
+    mask (ell >= 0) are compared position by position; a position agrees when both select it
+    or both skip it. Returns (agreeing positions, all positions).
+    """
+    ell = np.asarray(ell, dtype=np.float32)
+    B, T = ell.shape
+    topk = np.zeros((B, T), dtype=bool)
+    topk[np.arange(B)[:, None], np.asarray(idx)] = True
+    thr = ell >= 0
+    return int(np.sum(topk == thr)), B * T
+
+
+def differing_selected_share(agreement, K):
+    """The page's rough reading of a mask agreement rate (Table 10 commentary): if both masks
+    select the same number of tokens, the disagreeing positions split evenly into top-k-only
+    and threshold-only tokens, so the share of selected tokens that differ is
+    ((1 - agreement) / 2) / (1 / K)."""
+    return (1.0 - float(agreement)) / 2.0 * float(K)
 
 
 # --- the dense layer: every token enters, no gate ---------------------------------------------

@@ -229,8 +229,11 @@ def test_attention_closed_forms():
 # the sparse layer: brute-force loop implementation on tiny shapes, and checks (1)-(4)
 # ---------------------------------------------------------------------------------------------
 
-def _brute_sparse_layer(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta):
-    """Plain-loop X-MoD layer written from the pages' steps, for tiny shapes only."""
+def _brute_sparse_layer(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta, threshold=False):
+    """Plain-loop X-MoD layer written from the pages' steps, for tiny shapes only.
+
+    threshold=True takes the eval-time rule instead of top-k: a token enters when its routing
+    probability 1 / (1 + exp(-logit)) is at least 1/2 (evaluated here as written, in float64)."""
     B, T, d = x.shape
     k = T // K
     f64 = lambda a: bf16_to_f64(a) if np.asarray(a).dtype == np.uint16 else np.asarray(a, float)
@@ -254,8 +257,11 @@ def _brute_sparse_layer(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta):
         for t in range(T):
             s = np.float32(math.fsum([x[b, t, c] * wr[c] for c in range(d)]) + lay["router_bias"])
             logit.append(np.float32(s - np.float32(np.float32(tau) * bias[b, t])))
-        ranked = sorted(range(T), key=lambda t: (-float(logit[t]), t))
-        S = sorted(ranked[:k])
+        if threshold:
+            S = [t for t in range(T) if 1.0 / (1.0 + math.exp(-float(logit[t]))) >= 0.5]
+        else:
+            ranked = sorted(range(T), key=lambda t: (-float(logit[t]), t))
+            S = sorted(ranked[:k])
         u = [norm(list(x[b, t]), g1) for t in S]
         q = [matvec(wqkv, uu, range(0, dq)) for uu in u]
         kk = [matvec(wqkv, uu, range(dq, dq + dkv)) for uu in u]
@@ -546,3 +552,91 @@ def test_block_walk_rounds_to_bf16_and_resets_bias():
             y, b = r["y"], r["bias_out"]
         cur = round_to_bf16(y)
     assert np.array_equal(xf, cur)
+
+
+# ---------------------------------------------------------------------------------------------
+# eval-time causal threshold routing and the mask agreement of Table 10
+# ---------------------------------------------------------------------------------------------
+
+def test_threshold_select_definition():
+    ell = np.array([[-1.0, 0.0, -0.0, 2.0, -1e-30, 1e-30, -3.5, 0.25]], dtype=np.float32)
+    assert oracle.threshold_select(ell)[0].tolist() == [1, 2, 3, 5, 7]
+    # away from 0, the rule is sigmoid >= 1/2 evaluated as written
+    rng = np.random.default_rng(40)
+    ell = (rng.standard_normal((3, 500)) * 2).astype(np.float32)
+    ell[np.abs(ell) < 1e-6] = 1.0
+    sel = oracle.threshold_select(ell)
+    for b in range(3):
+        want = [t for t in range(500) if 1.0 / (1.0 + math.exp(-float(ell[b, t]))) >= 0.5]
+        assert sel[b].tolist() == want
+
+
+@pytest.mark.parametrize("Hq,Hkv,shift", [(2, 2, 0.0), (4, 2, 0.4), (2, 1, -0.6)])
+def test_sparse_layer_threshold_brute_force(Hq, Hkv, shift):
+    rng = np.random.default_rng(50 + Hq)
+    B, T, d, hd, F = 3, 7, 8, 2, 6
+    lay = _rand_layer(rng, d, Hq, Hkv, hd, F)
+    lay["router_bias"] = shift
+    lay["varsigma"] = 0.7
+    x = bf16_to_f64(wl.f32_to_bf16_bits(rng.standard_normal((B, T, d)).astype(np.float32)))
+    bias = (rng.standard_normal((B, T)) * 0.3).astype(np.float32)
+    dims = Dims(Hq, Hkv, hd, 1e-5)
+    got = oracle.sparse_layer_threshold(x, lay, dims, bias=bias, tau=1.2, delta=0.05)
+    want_y, want_b = _brute_sparse_layer(x, lay, Hq, Hkv, hd, 1e-5, 1, bias, 1.2, 0.05,
+                                         threshold=True)
+    assert got["counts"].sum() > 0
+    assert np.allclose(got["y"], want_y, rtol=1e-11, atol=1e-12)
+    assert np.array_equal(got["bias_out"], want_b)
+
+
+def test_threshold_extremes():
+    x, lay, dims = _tiny(seed=41)
+    bias = (np.random.default_rng(42).standard_normal(x.shape[:2]) * 0.1).astype(np.float32)
+    lay_all = dict(lay, router_bias=100.0)          # every ell >= 0: all tokens, like K = 1
+    r = oracle.sparse_layer_threshold(x, lay_all, dims, bias=bias, delta=0.05)
+    r1 = oracle.sparse_layer(x, lay_all, dims, 1, bias=bias, delta=0.05)
+    assert np.array_equal(r["counts"], np.full(x.shape[0], x.shape[1]))
+    assert np.array_equal(r["y"], r1["y"]) and np.array_equal(r["bias_out"], r1["bias_out"])
+    lay_none = dict(lay, router_bias=-100.0)        # no token enters: identity, bias unchanged
+    r = oracle.sparse_layer_threshold(x, lay_none, dims, bias=bias, delta=0.05)
+    assert np.all(r["counts"] == 0)
+    assert np.array_equal(r["y"], x) and np.array_equal(r["bias_out"], bias)
+
+
+def test_threshold_sampling_matches_full():
+    x, lay, dims = _tiny(seed=43, T=40)
+    r = oracle.sparse_layer_threshold(x, lay, dims)
+    assert np.all(r["counts"] > 3)
+    sample = {b: np.array([0, 2, int(r["counts"][b]) - 1]) for b in range(x.shape[0])}
+    rs = oracle.sparse_layer_threshold(x, lay, dims, sample=sample)
+    for b, (prow, pos, ysel) in rs["rows"].items():
+        assert np.array_equal(pos, r["idx"][b][prow])
+        assert np.array_equal(ysel, r["y"][b, pos])
+
+
+def test_mask_agreement_counts():
+    rng = np.random.default_rng(44)
+    B, T, k = 4, 64, 8
+    ell = (rng.standard_normal((B, T)) - 1.0).astype(np.float32)
+    idx = oracle.topk_select(ell, k)
+    agree, n = oracle.mask_agreement(ell, idx)
+    # symmetric difference of the two position sets, counted by hand
+    diff = 0
+    for b in range(B):
+        a = set(idx[b].tolist())
+        t = {i for i in range(T) if ell[b, i] >= 0}
+        diff += len(a ^ t)
+    assert n == B * T and agree == B * T - diff
+    # when exactly the top-k logits are non-negative, the two masks coincide
+    ell2 = ell.copy()
+    for b in range(B):
+        ell2[b] = -1.0
+        ell2[b, idx[b]] = 1.0
+    assert oracle.mask_agreement(ell2, idx) == (B * T, B * T)
+
+
+def test_mask_agreement_reading_table10(golden_dir):
+    for line in _read_table(golden_dir, "mask_agreement.txt"):
+        _, K, agree, share = line.split()
+        got = 100.0 * oracle.differing_selected_share(float(agree) / 100.0, int(K))
+        assert round(got) == int(share), (line, got)
