@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -68,6 +69,46 @@ def measured_traffic(kernel):
     if h.hexdigest()[:16] != rec["source_sha256_16"]:
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def threshold_layer(xmod, w, xb, dl, dims, steps, warmup):
+    """The same layer with the eval-time causal threshold rule (ell >= 0 enters). An untrained
+    router would pass half of the tokens; here its bias beta_r is set so that the expected
+    share of tokens with s >= 0 is 1/K, as the rule is meant to route (s ~ N(beta_r, sigma^2),
+    sigma = 0.02 * sqrt(d) for N(0, 1) activations and N(0, 0.02) router weights), and no
+    carried bias is used, so every call routes about B*T/K tokens. Reports the time per call
+    and routed tokens/s at the number the last call routed. Informational; the headline is the
+    training-time top-k layer."""
+    import statistics
+    import torch
+    sigma = 0.02 * math.sqrt(w.d)
+    beta = -sigma * statistics.NormalDist().inv_cdf(1.0 - 1.0 / w.K)
+    L = xmod.make_layer(dict(dl, router_bias=beta))
+    x0 = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).cuda()
+    x = x0.clone()
+    n_total = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = xmod.alloc_workspace(dims, 1, xmod.WS_SPARSE_THRESHOLD)
+    stream = torch.cuda.current_stream()
+
+    # every call starts from the same hidden state (restored outside the timed calls), so the
+    # routed count does not drift as in-place updates accumulate
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    for i in range(warmup + steps):
+        x.copy_(x0)
+        if i >= warmup:
+            events[i - warmup][0].record(stream)
+        xmod.sparse_layer_fwd_threshold(x, L, dims, None, w.tau, w.delta, ws, n_total_out=n_total,
+                                        stream=stream)
+        if i >= warmup:
+            events[i - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in events) / steps
+    routed = int(n_total.item())   # the same for every call
+    return {"ms_per_call": round(ms, 5), "routed_tokens": routed,
+            "routed_tokens_per_s": round(routed / (ms * 1e-3), 1),
+            "rule": "ell >= 0 (routing probability >= 1/2)", "router_bias": round(beta, 4),
+            "timing": "each call on the same input, events around each call"}
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -206,6 +247,7 @@ def main():
         "roofline": roof,
         "phases": phases,
     }
+    out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

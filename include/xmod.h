@@ -13,6 +13,9 @@
  *          and before the FFN, unselected rows passed through.
  *   [MOE]  "Beyond dense Transformers: MoE, SSMs and hybrids", bias-free SwiGLU FFN.
  *   [MODA] "Mixture-of-Depths Attention" reading notes, section 2.1: GQA head mapping.
+ *   [XMOD] section "training-time top-k, eval-time causal threshold": at evaluation a token
+ *          enters a sparse layer when its routing probability is at least 1/2; section
+ *          "routing diagnostics", Table 10: agreement of the top-k and threshold masks.
  *
  * One Sparse(K) layer, per sequence b of length T:
  *   s_t   = w_r . x_t + beta_r                      (fp32 accumulate)
@@ -97,7 +100,8 @@ enum {
   XMOD_WS_ROUTE_TOPK = 0,
   XMOD_WS_SPARSE_LAYER = 1,
   XMOD_WS_DENSE_LAYER = 2,
-  XMOD_WS_BLOCK = 3
+  XMOD_WS_BLOCK = 3,
+  XMOD_WS_SPARSE_THRESHOLD = 4
 };
 
 /* Workspace bytes an entry point needs for these shapes (0 if none). K is ignored for the
@@ -140,6 +144,43 @@ xmod_status xmod_sparse_layer_fwd(void *x, const xmod_layer *layer, const xmod_d
                                   int32_t K, float *bias, float tau, float delta,
                                   int32_t *idx_out, float *gate_out, void *ws, size_t ws_bytes,
                                   void *stream);
+
+/* Eval-time causal threshold routing of given fp32 logits [B,T] ([XMOD] "training-time top-k,
+ * eval-time causal threshold"): a token enters when its routing probability sigmoid(ell) is at
+ * least 1/2, i.e. ell >= 0 (-0 included, NaN never). Each sequence selects its own number of
+ * tokens; the selection is written flat, sequence after sequence, ascending within each:
+ *   counts [B] int32 out: tokens selected in sequence b;
+ *   offsets [B] int32 out: first flat row of sequence b (sum of the counts before it);
+ *   src [B*T] int32 out: flat row m -> row b*T + t of x (only the first *n_total are written);
+ *   gate [B*T] fp32 out or NULL: sigmoid(ell) of flat row m;
+ *   n_total [1] int32 out: number of selected tokens (device memory: no host sync happens);
+ *   bias [B,T] fp32 in/out or NULL: bias[b,t] += delta for every selected token. */
+xmod_status xmod_threshold_select(const float *logits, int32_t B, int32_t T, int32_t *counts,
+                                  int32_t *offsets, int32_t *src, float *gate, int32_t *n_total,
+                                  float *bias, float delta, void *stream);
+
+/* Forward of one sparse layer with the eval-time causal threshold rule (same layer as
+ * xmod_sparse_layer_fwd, every token with ell >= 0 selected), in place on x. The number of
+ * selected rows stays on the device: the kernels are launched for all B*T rows and the surplus
+ * workgroups exit at once, so the call never waits for the host. Attention is causal within each
+ * sequence's own selected rows. Workspace: xmod_workspace_bytes(dims, 1,
+ * XMOD_WS_SPARSE_THRESHOLD) (sized for B*T rows).
+ *   bias [B,T] fp32 in/out or NULL: read for ell, then bias[selected] += delta.
+ *   src_out [B*T], counts_out [B], n_total_out [1] int32: optional copies of the selection
+ *   (as xmod_threshold_select; NULL to keep them in the workspace). */
+xmod_status xmod_sparse_layer_fwd_threshold(void *x, const xmod_layer *layer,
+                                            const xmod_dims *dims, float *bias, float tau,
+                                            float delta, int32_t *src_out, int32_t *counts_out,
+                                            int32_t *n_total_out, void *ws, size_t ws_bytes,
+                                            void *stream);
+
+/* Mask agreement of one sparse layer ([XMOD] "routing diagnostics", Table 10): from the same
+ * logits [B,T] fp32, the top-k mask (idx [B,k] int32, the selected positions) and the threshold
+ * mask (logit >= 0) are compared position by position; *agree (one uint32 in device memory) is
+ * increased by the number of positions where both select or both skip. The caller zeroes
+ * *agree and may accumulate over layers; the rate is agree / (B*T*layers). */
+xmod_status xmod_mask_agreement(const float *logits, const int32_t *idx, int32_t B, int32_t T,
+                                int32_t k, uint32_t *agree, void *stream);
 
 /* Forward of one dense layer (every token, no gate): y = x + (a + f), in place on x. */
 xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,

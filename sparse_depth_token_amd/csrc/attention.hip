@@ -57,8 +57,11 @@ struct AttnCfg {
 
 template <int HD>
 __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
-                                                      uint16_t *__restrict__ o, int ldo, int k,
-                                                      int Hq, int Hkv, float scale_log2) {
+                                                      uint16_t *__restrict__ o, int ldo,
+                                                      int k_fixed, int Hq, int Hkv,
+                                                      float scale_log2,
+                                                      const int32_t *__restrict__ seq_off,
+                                                      const int32_t *__restrict__ seq_len) {
   using C = AttnCfg<HD>;
   constexpr int BQ = C::BQ, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
   // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
@@ -71,10 +74,16 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   // earlier one (none when both are the same middle tile). Every workgroup then has the same
   // causal work, each SIMD runs one wave of each tile, and the earlier tile's key/value tiles
   // are a prefix of the later one's, so the pair loads them once.
-  const int nqt = (k + BQ - 1) / BQ;
-  const int p = (int)blockIdx.x;
-  const int qt_hi = nqt - 1 - p;
   const int h = blockIdx.y, b = blockIdx.z;
+  // sequence length and first packed row: fixed, or per sequence (the grid covers the longest)
+  const int k = seq_len ? seq_len[b] : k_fixed;
+  const int64_t row0 = seq_len ? (int64_t)seq_off[b] : (int64_t)b * k_fixed;
+  const int nqt = (k + BQ - 1) / BQ;
+  // Pairs in a grid-stride loop: one per workgroup when the grid covers the sequence's pairs,
+  // several when it was sized below the longest possible sequence (per-sequence lengths).
+  for (int p = blockIdx.x; p < (nqt + 1) / 2; p += gridDim.x) {
+  if (p != (int)blockIdx.x) __syncthreads();  // the previous pair's epilogue is done with LDS
+  const int qt_hi = nqt - 1 - p;
   const int gkv = (h * Hkv) / Hq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int gq = lane >> 5, r32 = lane & 31;
@@ -85,7 +94,6 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   const int q_pos = qt * BQ + (wid & 3) * 32 + r32;
   // the last query this wave owns (-1: nothing to do)
   const int q_last_wave = active ? qt * BQ + (wid & 3) * 32 + 31 : -1;
-  const int64_t row0 = (int64_t)b * k;
 
   const int q_hi = min(qt_hi * BQ + BQ, k);
   const int n_kv = (q_hi + BKV - 1) / BKV;
@@ -320,19 +328,24 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
       if (q0 + r < k) *(uint4 *)(o + (row0 + q0 + r) * ldo + h * HD + c * 8) = v;
     }
   }
+  }  // pair loop
 }
 
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
-                            int Hq, int Hkv, int hd, hipStream_t s) {
+                            int Hq, int Hkv, int hd, const int32_t *seq_off,
+                            const int32_t *seq_len, hipStream_t s) {
   const int nqt = (k + 127) / 128;
-  const dim3 grid((unsigned)((nqt + 1) / 2), (unsigned)Hq, (unsigned)B);
+  // per-sequence lengths (k is then only their bound): a quarter of the pairs of a longest
+  // sequence per (head, sequence), each workgroup looping over its share
+  const int pairs = (nqt + 1) / 2;
+  const dim3 grid((unsigned)(seq_len ? (pairs + 3) / 4 : pairs), (unsigned)Hq, (unsigned)B);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 128)
     hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
-                       scale_log2);
+                       scale_log2, seq_off, seq_len);
   else
     hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
-                       scale_log2);
+                       scale_log2, seq_off, seq_len);
   return hipGetLastError();
 }
 

@@ -58,6 +58,37 @@ __device__ __forceinline__ float dense_residual(float X, float a, float f) {
 
 }  // namespace xmod
 
+// ---- packed-row map -------------------------------------------------------------------------
+namespace xmod {
+
+// Packed row m of a layer -> row of the hidden state x, viewed as [B*T, d]:
+//  * src != nullptr: x row src[m] (eval-time threshold routing: sequences route different
+//    numbers of tokens, so rows are listed flat and their count n_dev lives on the device);
+//  * idx != nullptr: x row (m / k) * T + idx[m] (top-k routing, k rows per sequence);
+//  * otherwise m (dense layer: every row).
+// Rows outside [0, x_rows) (a caller error) are clamped so that no access leaves x.
+struct RowMap {
+  const int32_t *idx = nullptr;
+  const int32_t *src = nullptr;
+  const int32_t *n_dev = nullptr;  // device-side number of packed rows, or nullptr
+  int T = 0, k = 0;
+  int64_t x_rows = 0;
+};
+
+__device__ __forceinline__ int64_t rowmap_x(const RowMap &r, int64_t m) {
+  int64_t row;
+  if (r.src) row = r.src[m];
+  else if (r.idx) row = (m / r.k) * r.T + min(max(r.idx[m], 0), r.T - 1);
+  else row = m;
+  return min(max(row, (int64_t)0), r.x_rows - 1);
+}
+// Number of packed rows: the device count when there is one (never above the launch bound).
+__device__ __forceinline__ int64_t rowmap_count(const RowMap &r, int64_t bound) {
+  return r.n_dev ? min((int64_t)*r.n_dev, bound) : bound;
+}
+
+}  // namespace xmod
+
 // ---- launchers (host side, defined in the .hip files) ---------------------------------------
 namespace xmod {
 
@@ -67,19 +98,31 @@ hipError_t launch_router(const uint16_t *x, const uint16_t *w, float beta, const
 hipError_t launch_topk(const float *logits, int B, int T, int k, int32_t *idx, float *gate,
                        float *bias, float delta, hipStream_t s);
 
-// Gather rows (via idx, or identity when idx == nullptr) and optionally RMSNorm them.
-hipError_t launch_gather_rows(const uint16_t *x, const int32_t *idx, const uint16_t *gain,
-                              float eps, bool normalize, int B, int T, int d, int k,
-                              uint16_t *out, hipStream_t s);
+// Eval-time threshold routing: per sequence the tokens with logit >= 0, packed flat in
+// sequence order (counts[b], offsets[b], src[m] = b*T + t, gate[m] = sigmoid(logit)), the
+// total in *n_total, and bias[b*T + t] += delta for every selected token.
+hipError_t launch_threshold_select(const float *logits, int B, int T, int32_t *counts,
+                                   int32_t *offsets, int32_t *src, float *gate, int32_t *n_total,
+                                   float *bias, float delta, hipStream_t s);
 
-// v[m] = RMSNorm(X[m] + a[m]; gain), X gathered from x via idx (identity when nullptr); a fp32.
-hipError_t launch_residual_rmsnorm(const uint16_t *x, const int32_t *idx, const float *a,
-                                   const uint16_t *gain, float eps, int B, int T, int d, int k,
+// Adds to *agree the number of positions where the top-k mask (idx [B, k]) and the threshold
+// mask (logit >= 0) take the same decision.
+hipError_t launch_mask_agreement(const float *logits, const int32_t *idx, int B, int T, int k,
+                                 uint32_t *agree, hipStream_t s);
+
+// Gather rows (via the row map) and optionally RMSNorm them. rows: launch bound.
+hipError_t launch_gather_rows(const uint16_t *x, const RowMap &map, const uint16_t *gain,
+                              float eps, bool normalize, int64_t rows, int d, uint16_t *out,
+                              hipStream_t s);
+
+// v[m] = RMSNorm(X[m] + a[m]; gain), X gathered from x via the row map; a fp32.
+hipError_t launch_residual_rmsnorm(const uint16_t *x, const RowMap &map, const float *a,
+                                   const uint16_t *gain, float eps, int64_t rows, int d,
                                    uint16_t *v, hipStream_t s);
 
-// Standalone gated scatter (gate != nullptr) or dense residual (gate == nullptr, idx == nullptr).
-hipError_t launch_scatter(uint16_t *x, const int32_t *idx, const float *gate, float varsigma,
-                          const uint16_t *a, const uint16_t *f, int B, int T, int d, int k,
+// Standalone gated scatter (gate != nullptr) or dense residual (gate == nullptr).
+hipError_t launch_scatter(uint16_t *x, const RowMap &map, const float *gate, float varsigma,
+                          const uint16_t *a, const uint16_t *f, int64_t rows, int d,
                           hipStream_t s);
 
 enum GemmEpilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2, EPI_STORE_F32 = 3 };
@@ -90,17 +133,22 @@ struct GemmArgs {
   const uint16_t *B2;              // EPI_SWIGLU: up weights [N, K], same ldb
   uint16_t *C;        int ldc;     // EPI_STORE / EPI_SWIGLU bf16 output [M, N]
   float *Cf;                       // EPI_STORE_F32 fp32 output [M, N], same ldc
-  int M, N, K;
-  // EPI_RESIDUAL: output row m is x[b*T + idx[m]] (identity when idx == nullptr); the
-  // accumulator is f (kept fp32), added as X + varsigma*gate[m]*(a + f), or X + (a + f) if
-  // gate == nullptr; a is fp32 [M, N] with leading dimension ldc, as is x.
-  uint16_t *x; const int32_t *idx; const float *gate; float varsigma;
-  const float *a; int T; int k;
+  int M, N, K;                     // M: rows, or their upper bound when map.n_dev is set
+  // Rows: map.n_dev (when set) holds the actual row count on the device; the grid covers M
+  // and workgroups past the actual tiles exit at once.
+  // EPI_RESIDUAL: output row m is x row rowmap_x(map, m); the accumulator is f (kept fp32),
+  // added as X + varsigma*gate[m]*(a + f), or X + (a + f) if gate == nullptr; a is fp32
+  // [M, N] with leading dimension ldc, as is x.
+  RowMap map;
+  uint16_t *x; const float *gate; float varsigma; const float *a;
 };
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s);
 
+// Causal attention over packed sequences: fixed length k (seq_len == nullptr, sequence b at
+// rows b*k) or per-sequence lengths and first rows (seq_len[b], seq_off[b], each <= max_len).
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
-                            int Hq, int Hkv, int hd, hipStream_t s);
+                            int Hq, int Hkv, int hd, const int32_t *seq_off,
+                            const int32_t *seq_len, hipStream_t s);
 
 }  // namespace xmod

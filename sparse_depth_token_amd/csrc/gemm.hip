@@ -86,15 +86,23 @@ gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r32 = lane & 31, gq = lane >> 5;
-  const int M = g.M, K = g.K;
+  // rows: the device-side count when there is one (the grid covers the bound g.M)
+  const int M = g.map.n_dev ? min(*g.map.n_dev, g.M) : g.M, K = g.K;
   const int n_out = g.N;  // output columns (F for SwiGLU)
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (n_out + C::BN_OUT - 1) / C::BN_OUT;
+  const int n_tiles = tiles_m * tiles_n;
+  if ((int)blockIdx.x >= n_tiles) return;  // whole workgroup, before any barrier
+
+  // Tiles are visited in a grid-stride loop: one tile per workgroup when the grid covers them
+  // all, several when the row count is device-side and the grid is only CU-sized.
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+  if (tile != (int)blockIdx.x) __syncthreads();  // the previous tile's epilogue is done with LDS
 
   // --- tile id: XCD-contiguous remap, then grouped row-block order ---
-  int wg = blockIdx.x;
+  int wg = tile;
   {
-    const int nwg = gridDim.x, q = nwg / 8, rem = nwg % 8;
+    const int nwg = n_tiles, q = nwg / 8, rem = nwg % 8;
     const int xcd = wg % 8, loc = wg / 8;
     wg = xcd * q + (xcd < rem ? xcd : rem) + loc;
   }
@@ -332,8 +340,7 @@ gemm_kernel(GemmArgs g) {
       if (EPI == EPI_RESIDUAL) {
         const float *lf = (const float *)lds + r * C::CS + cc * 8;
         const f32x4 f0 = *(const f32x4 *)lf, f1 = *(const f32x4 *)(lf + 4);
-        const int64_t xrow =
-            g.idx ? (int64_t)(m / g.k) * g.T + min(max(g.idx[m], 0), g.T - 1) : (int64_t)m;
+        const int64_t xrow = rowmap_x(g.map, m);
         uint16_t *xp = g.x + xrow * g.ldc + n;
         const float *ap = g.a + (size_t)m * g.ldc + n;
         const f32x4 a0 = *(const f32x4 *)ap, a1 = *(const f32x4 *)(ap + 4);
@@ -363,6 +370,7 @@ gemm_kernel(GemmArgs g) {
       }
     }
   }
+  }  // tile loop
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
@@ -370,8 +378,11 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
   using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI>;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + C::BN_OUT - 1) / C::BN_OUT;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT),
-                     0, s, g);
+  // device-side row count: a CU-sized grid walks the tiles (g.M is only the bound)
+  const int tiles = tiles_m * tiles_n;
+  const int wgs_per_cu = C::WAVES_PER_EU * 4 / C::NW;
+  const int grid = g.map.n_dev ? min(tiles, 256 * wgs_per_cu) : tiles;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI>), dim3(grid), dim3(C::NT), 0, s, g);
   return hipGetLastError();
 }
 

@@ -263,4 +263,140 @@ hipError_t launch_topk(const float *logits, int B, int T, int k, int32_t *idx, f
   return hipGetLastError();
 }
 
+// ---- eval-time causal threshold routing -------------------------------------------------------
+//
+// The X-MoD review's section "training-time top-k, eval-time causal threshold": at evaluation
+// a token enters the sparse layer when its routing probability is at least 1/2, which for the
+// gate sigmoid(ell) of Eq. (8) means ell >= 0 (-0 included, NaN excluded). Each sequence routes
+// its own number of tokens; the selected rows are listed flat, sequence after sequence, in
+// ascending position. Two kernels: the per-sequence counts, then (each sequence adding up the
+// counts before it) the positions, gates and bias updates.
+
+__device__ __forceinline__ uint32_t block_sum_1024(uint32_t v, uint32_t *s_part) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) s_part[wid] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += s_part[w];
+  return t;
+}
+
+__global__ __launch_bounds__(1024) void threshold_count_kernel(const float *__restrict__ logits,
+                                                               int T, int32_t *__restrict__ counts) {
+  __shared__ uint32_t s_part[16];
+  const int b = blockIdx.x;
+  const float *L = logits + (int64_t)b * T;
+  uint32_t c = 0;
+  for (int p = threadIdx.x; p < T; p += 1024) c += L[p] >= 0.f;
+  const uint32_t tot = block_sum_1024(c, s_part);
+  if (threadIdx.x == 0) counts[b] = (int32_t)tot;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void threshold_write_kernel(
+    const float *__restrict__ logits, int B, int T, const int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ src, float *__restrict__ gate,
+    int32_t *__restrict__ n_total, float *__restrict__ bias, float delta) {
+  __shared__ uint32_t s_part[16];
+  __shared__ uint32_t s_wave_tot[16];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // first flat row of this sequence: the counts of the sequences before it
+  uint32_t before = 0;
+  for (int q = tid; q < b; q += 1024) before += (uint32_t)counts[q];
+  const uint32_t off = block_sum_1024(before, s_part);
+
+  const float *L = logits + (int64_t)b * T;
+  const int p0 = tid * KPT;
+  float lv[KPT];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    lv[j] = p0 + j < T ? L[p0 + j] : -1.f;
+    mine += lv[j] >= 0.f;
+  }
+  // block-wide exclusive prefix of the selected counts, in position order
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wave_tot[wid] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wid; ++w) base += s_wave_tot[w];
+  uint32_t pos = off + base + incl - mine;
+  float *Bi = bias ? bias + (int64_t)b * T : nullptr;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (lv[j] >= 0.f) {
+      const int p = p0 + j;
+      src[pos] = (int32_t)((int64_t)b * T + p);
+      if (gate) gate[pos] = 1.0f / (1.0f + expf(-lv[j]));
+      if (Bi) Bi[p] = __fadd_rn(Bi[p], delta);
+      ++pos;
+    }
+  }
+  if (tid == 0) {
+    offsets[b] = (int32_t)off;
+    if (b == B - 1) *n_total = (int32_t)(off + (uint32_t)counts[b]);
+  }
+}
+
+hipError_t launch_threshold_select(const float *logits, int B, int T, int32_t *counts,
+                                   int32_t *offsets, int32_t *src, float *gate, int32_t *n_total,
+                                   float *bias, float delta, hipStream_t s) {
+  hipLaunchKernelGGL(threshold_count_kernel, dim3(B), dim3(1024), 0, s, logits, T, counts);
+  const int need = (T + 1023) / 1024;
+#define XMOD_THR(KPT_)                                                                         \
+  hipLaunchKernelGGL((threshold_write_kernel<KPT_>), dim3(B), dim3(1024), 0, s, logits, B, T, \
+                     counts, offsets, src, gate, n_total, bias, delta)
+  if (need <= 1) XMOD_THR(1);
+  else if (need <= 2) XMOD_THR(2);
+  else if (need <= 4) XMOD_THR(4);
+  else if (need <= 8) XMOD_THR(8);
+  else if (need <= 16) XMOD_THR(16);
+  else if (need <= 32) XMOD_THR(32);
+  else XMOD_THR(64);
+#undef XMOD_THR
+  return hipGetLastError();
+}
+
+// ---- top-k / threshold mask agreement ([XMOD] "routing diagnostics", Table 10) -----------------
+
+__global__ __launch_bounds__(1024) void mask_agreement_kernel(const float *__restrict__ logits,
+                                                              const int32_t *__restrict__ idx,
+                                                              int T, int k,
+                                                              uint32_t *__restrict__ agree) {
+  __shared__ uint32_t bits[65536 / 32];
+  __shared__ uint32_t s_part[16];
+  const int b = blockIdx.x;
+  const int nw = (T + 31) / 32;
+  for (int i = threadIdx.x; i < nw; i += 1024) bits[i] = 0u;
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += 1024) {
+    const int p = min(max(idx[(int64_t)b * k + j], 0), T - 1);
+    atomicOr(&bits[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  const float *L = logits + (int64_t)b * T;
+  uint32_t c = 0;
+  for (int p = threadIdx.x; p < T; p += 1024) {
+    const bool top = (bits[p >> 5] >> (p & 31)) & 1u;
+    c += top == (L[p] >= 0.f);
+  }
+  const uint32_t tot = block_sum_1024(c, s_part);
+  if (threadIdx.x == 0) atomicAdd(agree, tot);
+}
+
+hipError_t launch_mask_agreement(const float *logits, const int32_t *idx, int B, int T, int k,
+                                 uint32_t *agree, hipStream_t s) {
+  hipLaunchKernelGGL(mask_agreement_kernel, dim3(B), dim3(1024), 0, s, logits, idx, T, k, agree);
+  return hipGetLastError();
+}
+
 }  // namespace xmod
+

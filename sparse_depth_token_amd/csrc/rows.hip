@@ -2,31 +2,24 @@
 // rows with the RMSNorm before attention, the RMSNorm before the FFN on X + a (a in fp32), and
 // the standalone gated scatter of the X-MoD review's Eq. (7). One wave owns one row of d <= 8192 bf16 values held
 // in registers (16-byte chunks, 64 lanes side by side, so every access is coalesced).
-// Packed row m = b*k + j maps to x row b*T + idx[m]; with idx == nullptr the map is identity
-// (dense layers, where every position enters).
+// Packed row m maps to a row of x through a RowMap (top-k: b*T + idx[m] with m = b*k + j;
+// threshold routing: a flat list with a device-side count; dense layers: identity).
 #include "common.h"
 
 namespace xmod {
 
-// Positions outside [0, T) (a caller error) are clamped so that no access leaves the tensor.
-__device__ __forceinline__ int64_t src_row(const int32_t *idx, int64_t m, int T, int k) {
-  if (!idx) return m;
-  const int64_t b = m / k;
-  return b * T + min(max(idx[m], 0), T - 1);
-}
-
 template <int NI, bool NORM>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ x,
-                                                          const int32_t *__restrict__ idx,
+                                                          RowMap map,
                                                           const uint16_t *__restrict__ gain,
-                                                          float eps, int T, int d, int k,
-                                                          int64_t rows,
+                                                          float eps, int d, int64_t rows,
                                                           uint16_t *__restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= rows) return;
+  const int64_t n_rows = rowmap_count(map, rows);
+  for (int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); m < n_rows;
+       m += (int64_t)gridDim.x * 4) {
   const int nch = d >> 3;
-  const uint16_t *src = x + src_row(idx, m, T, k) * d;
+  const uint16_t *src = x + rowmap_x(map, m) * d;
   uint4 v[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -40,7 +33,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
       const int c = lane + 64 * i;
       if (c < nch) *(uint4 *)(dst + (size_t)c * 8) = v[i];
     }
-    return;
+    continue;
   }
   float ss = 0.f;
 #pragma unroll
@@ -64,18 +57,20 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
       *(uint4 *)(dst + (size_t)c * 8) = pack8(f);
     }
   }
+  }  // row loop
 }
 
 template <int NI>
 __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ idx,
-    const float *__restrict__ a, const uint16_t *__restrict__ gain, float eps, int T, int d,
-    int k, int64_t rows, uint16_t *__restrict__ out) {
+    const uint16_t *__restrict__ x, RowMap map, const float *__restrict__ a,
+    const uint16_t *__restrict__ gain, float eps, int d, int64_t rows,
+    uint16_t *__restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= rows) return;
+  const int64_t n_rows = rowmap_count(map, rows);
+  for (int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); m < n_rows;
+       m += (int64_t)gridDim.x * 4) {
   const int nch = d >> 3;
-  const uint16_t *src = x + src_row(idx, m, T, k) * d;
+  const uint16_t *src = x + rowmap_x(map, m) * d;
   const float *arow = a + m * d;
   float h[NI][8];
   float ss = 0.f;
@@ -112,21 +107,22 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
       *(uint4 *)(dst + (size_t)c * 8) = pack8(f);
     }
   }
+  }  // row loop
 }
 
 template <int NI>
-__global__ __launch_bounds__(256) void scatter_kernel(uint16_t *__restrict__ x,
-                                                      const int32_t *__restrict__ idx,
+__global__ __launch_bounds__(256) void scatter_kernel(uint16_t *__restrict__ x, RowMap map,
                                                       const float *__restrict__ gate,
                                                       float varsigma,
                                                       const uint16_t *__restrict__ a,
-                                                      const uint16_t *__restrict__ f, int T,
-                                                      int d, int k, int64_t rows) {
+                                                      const uint16_t *__restrict__ f, int d,
+                                                      int64_t rows) {
   const int lane = threadIdx.x & 63;
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= rows) return;
+  const int64_t n_rows = rowmap_count(map, rows);
+  for (int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); m < n_rows;
+       m += (int64_t)gridDim.x * 4) {
   const int nch = d >> 3;
-  uint16_t *xr = x + src_row(idx, m, T, k) * d;
+  uint16_t *xr = x + rowmap_x(map, m) * d;
   const float g = gate ? __fmul_rn(varsigma, gate[m]) : 0.f;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -142,6 +138,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(uint16_t *__restrict__ x,
       *(uint4 *)(xr + (size_t)c * 8) = pack8(Y);
     }
   }
+  }  // row loop
 }
 
 static int ni_for(int d) { return ((d >> 3) + 63) / 64; }
@@ -157,44 +154,51 @@ static int ni_for(int d) { return ((d >> 3) + 63) / 64; }
     default: MACRO(16); break;                    \
   }
 
-hipError_t launch_gather_rows(const uint16_t *x, const int32_t *idx, const uint16_t *gain,
-                              float eps, bool normalize, int B, int T, int d, int k,
-                              uint16_t *out, hipStream_t s) {
-  const int64_t rows = (int64_t)B * k;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+// Four rows per workgroup; with a device-side row count the grid is capped and the waves
+// loop, so a bound far above the actual count costs no idle workgroups.
+static dim3 row_grid(const RowMap &map, int64_t rows) {
+  const int64_t wgs = (rows + 3) / 4;
+  return dim3((unsigned)(map.n_dev ? (wgs < 2048 ? wgs : 2048) : wgs));
+}
+
+hipError_t launch_gather_rows(const uint16_t *x, const RowMap &map, const uint16_t *gain,
+                              float eps, bool normalize, int64_t rows, int d, uint16_t *out,
+                              hipStream_t s) {
+  if (rows < 1) return hipSuccess;
+  const dim3 grid = row_grid(map, rows);
 #define L_(NI)                                                                                  \
   if (normalize)                                                                                \
-    hipLaunchKernelGGL((gather_rows_kernel<NI, true>), grid, dim3(256), 0, s, x, idx, gain, eps, \
-                       T, d, k, rows, out);                                                     \
+    hipLaunchKernelGGL((gather_rows_kernel<NI, true>), grid, dim3(256), 0, s, x, map, gain, eps, \
+                       d, rows, out);                                                           \
   else                                                                                          \
-    hipLaunchKernelGGL((gather_rows_kernel<NI, false>), grid, dim3(256), 0, s, x, idx, gain,    \
-                       eps, T, d, k, rows, out)
+    hipLaunchKernelGGL((gather_rows_kernel<NI, false>), grid, dim3(256), 0, s, x, map, gain,    \
+                       eps, d, rows, out)
   XMOD_NI_SWITCH(ni_for(d), L_)
 #undef L_
   return hipGetLastError();
 }
 
-hipError_t launch_residual_rmsnorm(const uint16_t *x, const int32_t *idx, const float *a,
-                                   const uint16_t *gain, float eps, int B, int T, int d, int k,
+hipError_t launch_residual_rmsnorm(const uint16_t *x, const RowMap &map, const float *a,
+                                   const uint16_t *gain, float eps, int64_t rows, int d,
                                    uint16_t *v, hipStream_t s) {
-  const int64_t rows = (int64_t)B * k;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (rows < 1) return hipSuccess;
+  const dim3 grid = row_grid(map, rows);
 #define L_(NI)                                                                              \
-  hipLaunchKernelGGL((residual_rmsnorm_kernel<NI>), grid, dim3(256), 0, s, x, idx, a, gain, \
-                     eps, T, d, k, rows, v)
+  hipLaunchKernelGGL((residual_rmsnorm_kernel<NI>), grid, dim3(256), 0, s, x, map, a, gain, \
+                     eps, d, rows, v)
   XMOD_NI_SWITCH(ni_for(d), L_)
 #undef L_
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(uint16_t *x, const int32_t *idx, const float *gate, float varsigma,
-                          const uint16_t *a, const uint16_t *f, int B, int T, int d, int k,
+hipError_t launch_scatter(uint16_t *x, const RowMap &map, const float *gate, float varsigma,
+                          const uint16_t *a, const uint16_t *f, int64_t rows, int d,
                           hipStream_t s) {
-  const int64_t rows = (int64_t)B * k;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (rows < 1) return hipSuccess;
+  const dim3 grid = row_grid(map, rows);
 #define L_(NI)                                                                                 \
-  hipLaunchKernelGGL((scatter_kernel<NI>), grid, dim3(256), 0, s, x, idx, gate, varsigma, a, f, \
-                     T, d, k, rows)
+  hipLaunchKernelGGL((scatter_kernel<NI>), grid, dim3(256), 0, s, x, map, gate, varsigma, a, f, \
+                     d, rows)
   XMOD_NI_SWITCH(ni_for(d), L_)
 #undef L_
   return hipGetLastError();

@@ -79,10 +79,11 @@ bool layer_ok(const xmod_layer *L, bool sparse) {
 
 struct Plan {
   size_t logits = 0, idx = 0, gate = 0, u = 0, qkv = 0, o = 0, a = 0, g = 0, total = 0;
+  size_t counts = 0, offsets = 0, n_total = 0;  // threshold routing
 };
 
-// Workspace layout of one layer with M routed rows (all offsets 256-byte aligned).
-Plan plan_layer(const xmod_dims *dm, int64_t M, bool sparse) {
+// Workspace layout of one layer with (at most) M routed rows (offsets 256-byte aligned).
+Plan plan_layer(const xmod_dims *dm, int64_t M, bool sparse, bool threshold = false) {
   Plan p;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
@@ -92,6 +93,11 @@ Plan plan_layer(const xmod_dims *dm, int64_t M, bool sparse) {
     p.logits = take((size_t)dm->B * dm->T * 4);
     p.idx = take((size_t)M * 4);
     p.gate = take((size_t)M * 4);
+  }
+  if (threshold) {
+    p.counts = take((size_t)dm->B * 4);
+    p.offsets = take((size_t)dm->B * 4);
+    p.n_total = take(4);
   }
   p.u = take((size_t)M * dm->d * 2);
   p.qkv = take((size_t)M * nqkv * 2);
@@ -105,49 +111,59 @@ Plan plan_layer(const xmod_dims *dm, int64_t M, bool sparse) {
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 
-// Attention, FFN and the residual write-back for M = B*k rows given by idx (identity when
-// idx == nullptr). gate == nullptr selects the dense residual y = x + (a + f).
-xmod_status run_body(uint16_t *x, const int32_t *idx, const float *gate, const xmod_layer *L,
+// Attention, FFN and the residual write-back for the packed rows of the row map (M rows, or
+// at most M with a device-side count): the attention sees sequences of k rows each, or of
+// seq_len[b] rows from seq_off[b] (at most k). gate == nullptr selects the dense residual
+// y = x + (a + f).
+xmod_status run_body(uint16_t *x, const RowMap &map, int64_t M, const int32_t *seq_off,
+                     const int32_t *seq_len, const float *gate, const xmod_layer *L,
                      const xmod_dims *dm, int k, const Plan &p, void *ws, hipStream_t s) {
-  const int B = dm->B, T = dm->T, d = dm->d;
-  const int64_t M = (int64_t)B * k;
+  const int B = dm->B, d = dm->d;
   const int dq = dm->n_q_heads * dm->head_dim;
   const int nqkv = dq + 2 * dm->n_kv_heads * dm->head_dim;
   uint16_t *u = at<uint16_t>(ws, p.u), *qkv = at<uint16_t>(ws, p.qkv), *o = at<uint16_t>(ws, p.o);
   float *a = at<float>(ws, p.a);
   uint16_t *gbuf = at<uint16_t>(ws, p.g);
 
-  XMOD_HIP(launch_gather_rows(x, idx, (const uint16_t *)L->g_attn, dm->rms_eps, true, B, T, d, k,
-                              u, s));
+  XMOD_HIP(launch_gather_rows(x, map, (const uint16_t *)L->g_attn, dm->rms_eps, true, M, d, u, s));
   phase_mark(s);
   GemmArgs g{};
+  g.map = map;
   g.A = u; g.lda = d; g.B = (const uint16_t *)L->w_qkv; g.ldb = d; g.C = qkv; g.ldc = nqkv;
   g.M = (int)M; g.N = nqkv; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_STORE, s));
   phase_mark(s);
   XMOD_HIP(launch_attention(qkv, nqkv, o, dq, B, k, dm->n_q_heads, dm->n_kv_heads, dm->head_dim,
-                            s));
+                            seq_off, seq_len, s));
   phase_mark(s);
   g = GemmArgs{};
+  g.map = map;
   g.A = o; g.lda = dq; g.B = (const uint16_t *)L->w_o; g.ldb = dq; g.Cf = a; g.ldc = d;
   g.M = (int)M; g.N = d; g.K = dq;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, s));
   phase_mark(s);
-  XMOD_HIP(launch_residual_rmsnorm(x, idx, a, (const uint16_t *)L->g_ffn, dm->rms_eps, B, T, d, k,
-                                   u, s));
+  XMOD_HIP(launch_residual_rmsnorm(x, map, a, (const uint16_t *)L->g_ffn, dm->rms_eps, M, d, u, s));
   phase_mark(s);
   g = GemmArgs{};
+  g.map = map;
   g.A = u; g.lda = d; g.B = (const uint16_t *)L->w_gate; g.B2 = (const uint16_t *)L->w_up;
   g.ldb = d; g.C = gbuf; g.ldc = dm->ffn_hidden; g.M = (int)M; g.N = dm->ffn_hidden; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_SWIGLU, s));
   phase_mark(s);
   g = GemmArgs{};
+  g.map = map;
   g.A = gbuf; g.lda = dm->ffn_hidden; g.B = (const uint16_t *)L->w_down; g.ldb = dm->ffn_hidden;
   g.ldc = d; g.M = (int)M; g.N = d; g.K = dm->ffn_hidden;
-  g.x = x; g.idx = idx; g.gate = gate; g.varsigma = L->varsigma; g.a = a; g.T = T; g.k = k;
+  g.x = x; g.gate = gate; g.varsigma = L->varsigma; g.a = a;
   XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
   phase_mark(s);
   return XMOD_OK;
+}
+
+RowMap topk_map(const int32_t *idx, const xmod_dims *dm, int k) {
+  RowMap m;
+  m.idx = idx; m.T = dm->T; m.k = k; m.x_rows = (int64_t)dm->B * dm->T;
+  return m;
 }
 
 xmod_status sparse_layer(void *x, const xmod_layer *L, const xmod_dims *dm, int32_t K,
@@ -165,14 +181,45 @@ xmod_status sparse_layer(void *x, const xmod_layer *L, const xmod_dims *dm, int3
   phase_mark(s);
   XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s));
   phase_mark(s);
-  return run_body((uint16_t *)x, idx, gate, L, dm, k, p, ws, s);
+  return run_body((uint16_t *)x, topk_map(idx, dm, k), M, nullptr, nullptr, gate, L, dm, k, p,
+                  ws, s);
+}
+
+// Eval-time causal threshold routing: router, selection of every token with ell >= 0, then the
+// same body over the flat list of selected rows (count known only on the device; the
+// launches cover all B*T rows and surplus workgroups exit at once).
+xmod_status sparse_layer_threshold(void *x, const xmod_layer *L, const xmod_dims *dm,
+                                   float *bias, float tau, float delta, int32_t *src_out,
+                                   int32_t *counts_out, int32_t *n_total_out, void *ws,
+                                   hipStream_t s) {
+  const int64_t M = (int64_t)dm->B * dm->T;
+  const Plan p = plan_layer(dm, M, true, true);
+  float *logits = at<float>(ws, p.logits);
+  int32_t *src = src_out ? src_out : at<int32_t>(ws, p.idx);
+  float *gate = at<float>(ws, p.gate);
+  int32_t *counts = counts_out ? counts_out : at<int32_t>(ws, p.counts);
+  int32_t *offsets = at<int32_t>(ws, p.offsets);
+  int32_t *n_total = n_total_out ? n_total_out : at<int32_t>(ws, p.n_total);
+  phase_begin(s, 0);
+  XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)L->w_router, L->router_bias, bias,
+                         tau, logits, M, dm->d, s));
+  phase_mark(s);
+  XMOD_HIP(launch_threshold_select(logits, dm->B, dm->T, counts, offsets, src, gate, n_total,
+                                   bias, delta, s));
+  phase_mark(s);
+  RowMap map;
+  map.src = src; map.n_dev = n_total; map.T = dm->T; map.x_rows = M;
+  return run_body((uint16_t *)x, map, M, offsets, counts, gate, L, dm, dm->T, p, ws, s);
 }
 
 xmod_status dense_layer(void *x, const xmod_layer *L, const xmod_dims *dm, void *ws,
                         hipStream_t s) {
   const Plan p = plan_layer(dm, (int64_t)dm->B * dm->T, false);
   phase_begin(s, 2);
-  return run_body((uint16_t *)x, nullptr, nullptr, L, dm, dm->T, p, ws, s);
+  RowMap map;
+  map.T = dm->T; map.x_rows = (int64_t)dm->B * dm->T;
+  return run_body((uint16_t *)x, map, (int64_t)dm->B * dm->T, nullptr, nullptr, nullptr, L, dm,
+                  dm->T, p, ws, s);
 }
 
 __global__ void zero_f32_kernel(float *p, int64_t n) {
@@ -199,6 +246,8 @@ size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_poin
       if (K < 1 || dims->T / K < 1) return 0;
       return plan_layer(dims, (int64_t)dims->B * (dims->T / K), true).total;
     case XMOD_WS_DENSE_LAYER: return plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
+    case XMOD_WS_SPARSE_THRESHOLD:
+      return plan_layer(dims, (int64_t)dims->B * dims->T, true, true).total;
     case XMOD_WS_BLOCK: {
       const size_t dn = plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
       if (K < 1 || dims->T / K < 1) return dn;
@@ -241,7 +290,9 @@ xmod_status xmod_pack(const void *x, const int32_t *idx, int32_t B, int32_t T, i
   if (!x || !idx || !x_packed || B < 1 || T < 1 || d < 1 || k < 1 || k > T)
     return XMOD_ERR_INVALID_ARG;
   if (d % 64 != 0 || d > 8192) return XMOD_ERR_UNSUPPORTED;
-  XMOD_HIP(launch_gather_rows((const uint16_t *)x, idx, nullptr, 0.f, false, B, T, d, k,
+  RowMap map;
+  map.idx = idx; map.T = T; map.k = k; map.x_rows = (int64_t)B * T;
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, nullptr, 0.f, false, (int64_t)B * k, d,
                               (uint16_t *)x_packed, (hipStream_t)stream));
   return XMOD_OK;
 }
@@ -253,8 +304,10 @@ xmod_status xmod_scatter_gated(void *x, const int32_t *idx, const float *gate, f
     return XMOD_ERR_INVALID_ARG;
   if (!isfinite(varsigma)) return XMOD_ERR_INVALID_ARG;
   if (d % 64 != 0 || d > 8192) return XMOD_ERR_UNSUPPORTED;
-  XMOD_HIP(launch_scatter((uint16_t *)x, idx, gate, varsigma, (const uint16_t *)a_packed,
-                          (const uint16_t *)f_packed, B, T, d, k, (hipStream_t)stream));
+  RowMap map;
+  map.idx = idx; map.T = T; map.k = k; map.x_rows = (int64_t)B * T;
+  XMOD_HIP(launch_scatter((uint16_t *)x, map, gate, varsigma, (const uint16_t *)a_packed,
+                          (const uint16_t *)f_packed, (int64_t)B * k, d, (hipStream_t)stream));
   return XMOD_OK;
 }
 
@@ -329,8 +382,10 @@ xmod_status xmod_rmsnorm_rows(const void *x, const int32_t *idx, const void *gai
     return XMOD_ERR_INVALID_ARG;
   if (!(eps >= 0.f) || !isfinite(eps)) return XMOD_ERR_INVALID_ARG;
   if (d % 64 != 0 || d > 8192) return XMOD_ERR_UNSUPPORTED;
-  XMOD_HIP(launch_gather_rows((const uint16_t *)x, idx, (const uint16_t *)gain, eps, true, B, T, d,
-                              k, (uint16_t *)out, (hipStream_t)stream));
+  RowMap map;
+  map.idx = idx; map.T = T; map.k = k; map.x_rows = (int64_t)B * T;
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, (const uint16_t *)gain, eps, true,
+                              (int64_t)B * k, d, (uint16_t *)out, (hipStream_t)stream));
   return XMOD_OK;
 }
 
@@ -358,7 +413,7 @@ xmod_status xmod_attention_fwd(const void *qkv, int32_t ld_qkv, void *o, int32_t
   if (ld_qkv < nqkv || ld_o < n_q_heads * head_dim || ld_qkv % 8 != 0 || ld_o % 8 != 0)
     return XMOD_ERR_INVALID_ARG;
   XMOD_HIP(launch_attention((const uint16_t *)qkv, ld_qkv, (uint16_t *)o, ld_o, B, k, n_q_heads,
-                            n_kv_heads, head_dim, (hipStream_t)stream));
+                            n_kv_heads, head_dim, nullptr, nullptr, (hipStream_t)stream));
   return XMOD_OK;
 }
 
@@ -400,3 +455,40 @@ const char *xmod_status_string(xmod_status st) {
 int32_t xmod_last_hip_error(void) { return g_last_hip; }
 
 }  // extern "C"
+
+xmod_status xmod_threshold_select(const float *logits, int32_t B, int32_t T, int32_t *counts,
+                                  int32_t *offsets, int32_t *src, float *gate, int32_t *n_total,
+                                  float *bias, float delta, void *stream) {
+  if (!logits || !counts || !offsets || !src || !n_total || B < 1 || T < 1)
+    return XMOD_ERR_INVALID_ARG;
+  if ((int64_t)B * T > INT32_MAX) return XMOD_ERR_UNSUPPORTED;
+  if (T > 65536) return XMOD_ERR_UNSUPPORTED;
+  if (!isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_threshold_select(logits, B, T, counts, offsets, src, gate, n_total, bias, delta,
+                                   (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_sparse_layer_fwd_threshold(void *x, const xmod_layer *layer,
+                                            const xmod_dims *dims, float *bias, float tau,
+                                            float delta, int32_t *src_out, int32_t *counts_out,
+                                            int32_t *n_total_out, void *ws, size_t ws_bytes,
+                                            void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer_ok(layer, true)) return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  if ((int64_t)dims->B * dims->T > INT32_MAX) return XMOD_ERR_UNSUPPORTED;
+  const size_t need = xmod_workspace_bytes(dims, 1, XMOD_WS_SPARSE_THRESHOLD);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  return sparse_layer_threshold(x, layer, dims, bias, tau, delta, src_out, counts_out,
+                                n_total_out, ws, (hipStream_t)stream);
+}
+
+xmod_status xmod_mask_agreement(const float *logits, const int32_t *idx, int32_t B, int32_t T,
+                                int32_t k, uint32_t *agree, void *stream) {
+  if (!logits || !idx || !agree || B < 1 || T < 1 || k < 1 || k > T) return XMOD_ERR_INVALID_ARG;
+  if (T > 65536) return XMOD_ERR_UNSUPPORTED;
+  XMOD_HIP(launch_mask_agreement(logits, idx, B, T, k, agree, (hipStream_t)stream));
+  return XMOD_OK;
+}

@@ -17,11 +17,13 @@ if not os.path.exists(_LIB_PATH):
 lib = ctypes.CDLL(_LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK = 0, 1, 2, 3
+WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK, WS_SPARSE_THRESHOLD = 0, 1, 2, 3, 4
 
 # Every symbol include/xmod.h declares, in declaration order.
 EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", "xmod_pack",
-            "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_dense_layer_fwd", "xmod_block_fwd",
+            "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_threshold_select",
+            "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_dense_layer_fwd",
+            "xmod_block_fwd",
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_attention_fwd",
             "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
             "xmod_last_hip_error"]
@@ -52,6 +54,10 @@ _sig = {
     "xmod_scatter_gated": (_i32, [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "xmod_sparse_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp, _vp,
                                      _vp, _sz, _vp]),
+    "xmod_threshold_select": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp]),
+    "xmod_sparse_layer_fwd_threshold": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _f32, _f32, _vp,
+                                               _vp, _vp, _vp, _sz, _vp]),
+    "xmod_mask_agreement": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "xmod_dense_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _sz, _vp]),
     "xmod_block_fwd": (_i32, [_vp, _P(Layer), _i32, _P(Dims), _i32, _i32, _f32, _i32, _vp, _f32,
                               _f32, _vp, _sz, _vp]),
@@ -144,6 +150,29 @@ def sparse_layer_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_o
                                      _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
                                      _ptr(ws), ws.numel(), _stream(stream)),
            "xmod_sparse_layer_fwd")
+
+
+def threshold_select(logits, counts, offsets, src, n_total, gate=None, bias=None, delta=0.0,
+                     stream=None):
+    B, T = logits.shape
+    _check(lib.xmod_threshold_select(_ptr(logits), B, T, _ptr(counts), _ptr(offsets), _ptr(src),
+                                     _ptr(gate), _ptr(n_total), _ptr(bias), delta,
+                                     _stream(stream)), "xmod_threshold_select")
+
+
+def sparse_layer_fwd_threshold(x, layer: Layer, dims: Dims, bias, tau, delta, ws, src_out=None,
+                               counts_out=None, n_total_out=None, stream=None):
+    _check(lib.xmod_sparse_layer_fwd_threshold(_ptr(x), ctypes.byref(layer), ctypes.byref(dims),
+                                               _ptr(bias), tau, delta, _ptr(src_out),
+                                               _ptr(counts_out), _ptr(n_total_out), _ptr(ws),
+                                               ws.numel(), _stream(stream)),
+           "xmod_sparse_layer_fwd_threshold")
+
+
+def mask_agreement(logits, idx, agree, stream=None):
+    B, T = logits.shape
+    _check(lib.xmod_mask_agreement(_ptr(logits), _ptr(idx), B, T, idx.shape[1], _ptr(agree),
+                                   _stream(stream)), "xmod_mask_agreement")
 
 
 def dense_layer_fwd(x, layer: Layer, dims: Dims, ws, stream=None):

@@ -124,3 +124,33 @@ def test_stage_entry_points_reject_before_launch(x):
     assert L.xmod_attention_fwd(FAKE, 384, FAKE, 128, 1, 10, 3, 2, 64, None) == x.ERR_INVALID_ARG
     assert L.xmod_route_topk(FAKE, FAKE, 0.0, None, 1.0, 0, ctypes.byref(_dims(x)), FAKE, FAKE,
                              FAKE, None, 0, None) == x.ERR_INVALID_ARG
+
+
+def test_threshold_entry_points_reject_before_launch(x):
+    L = x.lib
+    dm = _dims(x)
+    # threshold routing workspace: sized for every row (B*T), plus counts / offsets / total
+    ws = x.workspace_bytes(dm, 1, x.WS_SPARSE_THRESHOLD)
+    assert ws >= x.workspace_bytes(dm, 1, x.WS_DENSE_LAYER) + 8 * 4096 * 4 * 3
+    f = L.xmod_threshold_select
+    assert f(FAKE, 0, 10, FAKE, FAKE, FAKE, None, FAKE, None, 0.0, None) == x.ERR_INVALID_ARG
+    assert f(FAKE, 2, 10, None, FAKE, FAKE, None, FAKE, None, 0.0, None) == x.ERR_INVALID_ARG
+    assert f(FAKE, 2, 10, FAKE, FAKE, FAKE, None, None, None, 0.0, None) == x.ERR_INVALID_ARG
+    assert f(FAKE, 1, 70000, FAKE, FAKE, FAKE, None, FAKE, None, 0.0, None) == x.ERR_UNSUPPORTED
+    assert f(FAKE, 2, 10, FAKE, FAKE, FAKE, None, FAKE, FAKE, float("nan"), None) == x.ERR_INVALID_ARG
+    g = L.xmod_sparse_layer_fwd_threshold
+    lay = _layer(x)
+    args = lambda **o: [o.get("x", FAKE), ctypes.byref(o.get("L", lay)),
+                        ctypes.byref(o.get("dm", dm)), None, o.get("tau", 1.0), 0.05, None, None,
+                        None, o.get("ws", FAKE), o.get("wsb", 1 << 40), None]
+    assert g(*args(x=None)) == x.ERR_INVALID_ARG
+    assert g(*args(tau=float("inf"))) == x.ERR_INVALID_ARG
+    assert g(*args(dm=_dims(x, head_dim=80))) == x.ERR_UNSUPPORTED
+    assert g(*args(wsb=ws - 1)) == x.ERR_WORKSPACE
+    bad = _layer(x)
+    bad.w_router = None
+    assert g(*args(L=bad)) == x.ERR_INVALID_ARG
+    h = L.xmod_mask_agreement
+    assert h(FAKE, FAKE, 2, 10, 11, FAKE, None) == x.ERR_INVALID_ARG
+    assert h(FAKE, FAKE, 2, 10, 5, None, None) == x.ERR_INVALID_ARG
+    assert h(FAKE, FAKE, 1, 70000, 5, FAKE, None) == x.ERR_UNSUPPORTED

@@ -1,0 +1,221 @@
+"""Eval-time causal threshold routing on the GPU vs the oracle (X-MoD review, section
+"training-time top-k, eval-time causal threshold"; Table 10 "mask agreement").
+
+Selection: a token enters when ell >= 0. The GPU decides on its own fp32 logit; a decision may
+differ from the oracle's only for tokens whose oracle logit is within 1e-5 of 0 (the same bar as
+the top-k swap rule), and rows of a sequence from the first differing packed position on are
+not compared (their attention context differs). Everything else follows the top-k layer's bar:
+unselected rows bit-identical, selected rows within max |diff| <= 2e-2 (+ half a bf16 spacing)
+and relative L2 <= 5e-3, bias updated exactly where the selections agree.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as wl
+from parity import SWAP_GAP, bf16_vals, check_values, dev_bf16, host_bits, layer_to_device, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def x():
+    from sparse_depth_token_amd import xmod
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return xmod
+
+
+def gpu_threshold_select(x, ell, bias=None, delta=0.0):
+    B, T = ell.shape
+    lt = torch.from_numpy(np.ascontiguousarray(ell, dtype=np.float32)).cuda()
+    counts = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    offsets = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    src = torch.full((B * T,), -1, dtype=torch.int32, device="cuda")
+    gate = torch.zeros(B * T, dtype=torch.float32, device="cuda")
+    n_total = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    bt = None if bias is None else torch.from_numpy(bias.copy()).cuda()
+    x.threshold_select(lt, counts, offsets, src, n_total, gate=gate, bias=bt, delta=delta)
+    torch.cuda.synchronize()
+    return (counts.cpu().numpy(), offsets.cpu().numpy(), src.cpu().numpy(), gate.cpu().numpy(),
+            int(n_total.item()), None if bt is None else bt.cpu().numpy())
+
+
+def split_selection(src, counts, T):
+    out, off = [], 0
+    for b, c in enumerate(counts):
+        rows = src[off:off + c]
+        assert np.all(rows // T == b), "flat rows must stay within their sequence"
+        out.append(rows - b * T)
+        off += c
+    return out
+
+
+@pytest.mark.parametrize("B,T", [(5, 3000), (3, 1024), (2, 65536), (1, 7)])
+def test_threshold_select_exact(x, B, T):
+    say(f"[threshold select] B{B} T{T}")
+    rng = np.random.default_rng(60 + T)
+    ell = (rng.standard_normal((B, T)) * 0.8).astype(np.float32)
+    ell[0, ::7] = 0.0                                    # exact zeros enter
+    ell[0, 3::11] = -0.0                                 # -0 enters
+    ell[-1, ::13] = -1e-30                               # tiny negatives stay out
+    if B >= 3:
+        ell[1] = -np.abs(ell[1]) - 1e-3                  # a sequence that routes nothing
+        ell[2] = np.abs(ell[2])                          # a sequence that routes everything
+    bias = (rng.standard_normal((B, T)) * 0.1).astype(np.float32)
+    counts, offsets, src, gate, n_total, bias_g = gpu_threshold_select(x, ell, bias, 0.05)
+    want = oracle.threshold_select(ell)
+    assert np.array_equal(counts, [len(w) for w in want])
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)[:-1]]))
+    assert n_total == counts.sum()
+    got = split_selection(src[:n_total], counts, T)
+    for b in range(B):
+        assert np.array_equal(got[b], want[b])
+    assert np.all(src[n_total:] == -1), "nothing past the selected rows is written"
+    want_gate = np.concatenate([oracle.sigmoid(ell[b, want[b]]) for b in range(B)])
+    assert np.allclose(gate[:n_total], want_gate, rtol=2e-6, atol=2e-6)
+    want_bias = bias.copy()
+    for b in range(B):
+        want_bias[b, want[b]] = (bias[b, want[b]] + np.float32(0.05)).astype(np.float32)
+    assert np.array_equal(bias_g, want_bias)
+
+
+def test_threshold_select_nan_never_enters(x):
+    ell = np.array([[np.nan, 1.0, -1.0, np.nan, 0.0]], dtype=np.float32)
+    counts, _, src, _, n_total, _ = gpu_threshold_select(x, ell)
+    assert n_total == 2 and counts.tolist() == [2] and src[:2].tolist() == [1, 4]
+
+
+@pytest.mark.parametrize("B,T,k", [(4, 4096, 512), (3, 1000, 37), (1, 65536, 16384)])
+def test_mask_agreement_exact(x, B, T, k):
+    say(f"[mask agreement] B{B} T{T} k{k}")
+    rng = np.random.default_rng(70 + k)
+    ell = (rng.standard_normal((B, T)) - 1.1).astype(np.float32)
+    ell[:, ::9] = 0.0
+    idx = oracle.topk_select(ell, k)
+    want, n = oracle.mask_agreement(ell, idx)
+    lt = torch.from_numpy(ell).cuda()
+    it = torch.from_numpy(idx.astype(np.int32)).cuda()
+    agree = torch.zeros(1, dtype=torch.int32, device="cuda")
+    x.mask_agreement(lt, it, agree)
+    x.mask_agreement(lt, it, agree)                       # accumulates over calls
+    torch.cuda.synchronize()
+    assert int(agree.item()) == 2 * want
+    assert 0 < want < n
+
+
+def _dims(x, w):
+    return x.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden, w.rms_eps)
+
+
+def run_threshold_gpu(x, w, xb, lay, bias):
+    dims = _dims(x, w)
+    xt = dev_bf16(xb)
+    bt = torch.from_numpy(bias.copy()).cuda() if bias is not None else None
+    src = torch.full((w.B * w.T,), -1, dtype=torch.int32, device="cuda")
+    counts = torch.empty(w.B, dtype=torch.int32, device="cuda")
+    n_total = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = x.alloc_workspace(dims, 1, x.WS_SPARSE_THRESHOLD)
+    dl = layer_to_device(lay)
+    x.sparse_layer_fwd_threshold(xt, x.make_layer(dl), dims, bt, w.tau, w.delta, ws, src_out=src,
+                                 counts_out=counts, n_total_out=n_total)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    assert int(n_total.item()) == c.sum()
+    sel = split_selection(src.cpu().numpy()[:c.sum()], c, w.T)
+    return host_bits(xt), sel, None if bt is None else bt.cpu().numpy()
+
+
+def check_threshold(w, xb, lay, bias, got, sample=None, abs_tol=2e-2):
+    y_bits, sel_g, bias_g = got
+    B, T = w.B, w.T
+    ref = oracle.sparse_layer_threshold(xb, lay, w, bias=bias, tau=w.tau, delta=w.delta,
+                                        sample=sample)
+    ell = ref["ell"]
+    first = []
+    for b in range(B):
+        g, r = sel_g[b], ref["idx"][b]
+        differ = np.setxor1d(g, r)
+        assert np.all(np.abs(ell[b, differ].astype(np.float64)) < SWAP_GAP), \
+            f"seq {b}: decisions differ away from the threshold"
+        n = min(len(g), len(r))
+        neq = np.nonzero(g[:n] != r[:n])[0]
+        first.append(int(neq[0]) if len(neq) else (n if len(g) == len(r) else n))
+    sel_mask = np.zeros((B, T), bool)
+    for b in range(B):
+        sel_mask[b, sel_g[b]] = True
+    assert np.array_equal(y_bits[~sel_mask], xb[~sel_mask]), "unselected rows changed"
+    yv = bf16_vals(y_bits)
+    stats = []
+    if sample is None:
+        for b in range(B):
+            if bias_g is not None and len(sel_g[b]) == len(ref["idx"][b]) and first[b] == len(sel_g[b]):
+                assert np.array_equal(bias_g[b], ref["bias_out"][b])
+            rows = sel_g[b][:first[b]]
+            if len(rows):
+                stats.append(check_values(yv[b, rows], ref["y"][b, rows], f"seq {b}", abs_tol=abs_tol))
+    else:
+        for b, (prow, pos, ysel) in ref["rows"].items():
+            keep = prow < first[b]
+            assert np.array_equal(pos[keep], sel_g[b][prow[keep]])
+            if keep.any():
+                stats.append(check_values(yv[b, pos[keep]], ysel[keep], f"seq {b} sampled",
+                                          abs_tol=abs_tol))
+    counts = [len(s) for s in sel_g]
+    say(f"    routed per sequence {counts}; max|diff|, relL2 = "
+        f"{max([s[0] for s in stats] or [0]):.3g}, {max([s[1] for s in stats] or [0]):.3g}")
+    return ref
+
+
+SMALL = {
+    "B3 T512 d256 (one sequence routes nothing, one everything)": (
+        wl.Workload("thr_a", 80, 3, 512, 256, 4, 4, 64, 1024, 1, bias_std=0.1), "extremes"),
+    "B4 T700 d512 GQA 8/2 hd64, router bias 0.2": (
+        wl.Workload("thr_b", 81, 4, 700, 512, 8, 2, 64, 1536, 1, bias_std=0.1,
+                    varsigma_range=(0.5, 1.5), gain_std=0.1, router_bias=0.2), None),
+    "B2 T1024 d1024 GQA 8/2 hd128, router bias -0.3": (
+        wl.Workload("thr_c", 82, 2, 1024, 1024, 8, 2, 128, 2816, 1, bias_std=0.1,
+                    router_bias=-0.3), None),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_threshold_layer_small(x, name):
+    w, mode = SMALL[name]
+    say(f"[threshold layer] {name}")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    if mode == "extremes":
+        bias[1] += 50.0          # ell = s - b: every logit of sequence 1 far below 0
+        bias[2] -= 50.0          # sequence 2: every logit far above 0
+    got = run_threshold_gpu(x, w, xb, lay, bias)
+    if mode == "extremes":
+        assert len(got[1][1]) == 0 and len(got[1][2]) == w.T
+    check_threshold(w, xb, lay, bias, got)
+
+
+def test_threshold_layer_bench_shape_sampled(x):
+    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    say(f"[threshold layer, full size] {w.name}: oracle on sequences 0 and 5")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    got = run_threshold_gpu(x, w, xb, lay, bias)
+    assert np.all(np.isfinite(bf16_vals(got[0])))
+    sample = {}
+    for b in (0, 5):
+        n = len(got[1][b])
+        sample[b] = np.unique(np.concatenate([np.arange(min(48, n)), np.arange(max(0, n - 32), n)]))
+    check_threshold(w, xb, lay, bias, got, sample=sample)
+
+
+def test_threshold_layer_deterministic(x):
+    w, _ = SMALL["B4 T700 d512 GQA 8/2 hd64, router bias 0.2"]
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w)
+    a = run_threshold_gpu(x, w, xb, lay, bias)
+    b = run_threshold_gpu(x, w, xb, lay, bias)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    assert all(np.array_equal(u, v) for u, v in zip(a[1], b[1]))
