@@ -12,7 +12,7 @@ share weights (same shapes, same work per step).
 Prints one JSON line: routed tokens/s, the roofline of the dominant kernel (HIP events around
 each kernel of the timed steps), and the CPU oracle timed on a bounded sample on this host.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
 """
 from __future__ import annotations
 
@@ -145,6 +145,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-threshold", action="store_true",
+                    help="skip the informational threshold-routing line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -247,7 +249,8 @@ def main():
         "roofline": roof,
         "phases": phases,
     }
-    out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup)
+    if not args.no_threshold:
+        out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
