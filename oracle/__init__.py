@@ -17,7 +17,8 @@ cases that reduce to a textbook definition.
 """
 from .layer import (router_logits, topk_select, sigmoid, rmsnorm, causal_attention, silu,
                     swiglu_ffn, sparse_layer, dense_layer, threshold_select,
-                    sparse_layer_threshold, mask_agreement, differing_selected_share)
+                    sparse_layer_threshold, mask_agreement, differing_selected_share,
+                    qk_head_norm, rope)
 from .stack import (stack_layer_kinds, physical_layers, active_equivalent_layers, total_params,
                     active_params, layer_params, flops_per_token_pages_convention, block_forward,
                     coverage, adjacent_jaccard, coverage_independent_reference,

@@ -24,6 +24,10 @@ Readings taken where the pages are silent or ambiguous (all listed in the design doc)
   * FFN input is RMSNorm(X + a) (sequential pre-norm); output y = X + varsigma*r*(a + f).
   * The bias update b[S] += delta happens after the gate is read.
   * Softmax scale 1/sqrt(head_dim); GQA head h uses KV head floor(h*Hkv/Hq) (0-based).
+  * Layer-form options (lay keys, absent = off): "residual" 1 for MoD's Eq. (6); "q_norm" /
+    "k_norm" gains for a per-head RMSNorm of queries / keys and "rope_theta" > 0 for rotary
+    embedding (rotate-half pairs) at original positions, applied in that order, as in the
+    Qwen3 structure the page's backbones follow.
   * Eval-time threshold routing: the probability that is compared with 1/2 is the gate of
     Eq. (8), sigmoid(s - tau*b) (the pages' routing diagnostics run threshold-driven forwards
     with and without the carried bias and get different coverage), decided as ell >= 0.
@@ -137,10 +141,52 @@ def swiglu_ffn(v, w_gate, w_up, w_down):
     return (silu(v @ _f64(w_gate).T) * (v @ _f64(w_up).T)) @ _f64(w_down).T
 
 
-def _attn_ffn_on_rows(X, lay, dims, out_rows):
+# --- layer-form options of the Qwen3-style backbones: [XMOD] "backbone configuration" ---------
+
+def qk_head_norm(Z, n_heads, head_dim, gain, eps):
+    """RMSNorm of every head_dim slice of Z [n, n_heads*head_dim], gain [head_dim] shared by
+    the heads (QK-norm of the Qwen3 backbones the page's 556M / 1.65B models follow)."""
+    Z = np.asarray(Z, dtype=np.float64).reshape(Z.shape[0], n_heads, head_dim)
+    ms = np.mean(Z * Z, axis=-1, keepdims=True)
+    return (Z / np.sqrt(ms + float(eps)) * _f64(gain)).reshape(Z.shape[0], n_heads * head_dim)
+
+
+def rope(Z, positions, n_heads, head_dim, theta):
+    """Rotary position embedding of every head of Z [n, n_heads*head_dim] at positions [n].
+
+    Pairs (i, i + head_dim/2), i < head_dim/2, rotate by the angle p * theta^(-2i/head_dim):
+    (z_i, z_j) -> (z_i cos - z_j sin, z_j cos + z_i sin). The positions are the tokens'
+    original positions in their sequence (a routed token keeps its place in the text)."""
+    Z = np.asarray(Z, dtype=np.float64).reshape(Z.shape[0], n_heads, head_dim)
+    h = head_dim // 2
+    inv = float(theta) ** (-2.0 * np.arange(h) / head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]      # [n, h]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    z1, z2 = Z[..., :h], Z[..., h:]
+    out = np.concatenate([z1 * c - z2 * s, z2 * c + z1 * s], axis=-1)
+    return out.reshape(Z.shape[0], n_heads * head_dim)
+
+
+def _qk_form(Q, Kt, lay, dims, q_pos_orig, k_pos_orig):
+    """Apply the optional QK-norm (lay["q_norm"], lay["k_norm"]) then RoPE (lay["rope_theta"]
+    > 0) to query and key rows at their original positions."""
+    Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    if lay.get("q_norm") is not None:
+        Q = qk_head_norm(Q, Hq, hd, lay["q_norm"], dims.rms_eps)
+    if lay.get("k_norm") is not None:
+        Kt = qk_head_norm(Kt, Hkv, hd, lay["k_norm"], dims.rms_eps)
+    theta = float(lay.get("rope_theta", 0.0) or 0.0)
+    if theta > 0:
+        Q = rope(Q, q_pos_orig, Hq, hd, theta)
+        Kt = rope(Kt, k_pos_orig, Hkv, hd, theta)
+    return Q, Kt
+
+
+def _attn_ffn_on_rows(X, lay, dims, out_rows, positions=None):
     """Attention residual a and FFN residual f for rows out_rows of one packed sequence X.
 
-    u = RMSNorm(X; g_attn); [Q|K|V] = u W_qkv^T; O = causal attention over X's rows;
+    u = RMSNorm(X; g_attn); [Q|K|V] = u W_qkv^T; optional QK-norm and RoPE at the rows'
+    original positions (positions[j] for packed row j); O = causal attention over X's rows;
     a = O W_o^T; v = RMSNorm(X + a; g_ffn); f = SwiGLU(v). Only rows 0..max(out_rows) of X
     are needed (causality), so only those are projected to keys and values.
     """
@@ -153,6 +199,8 @@ def _attn_ffn_on_rows(X, lay, dims, out_rows):
     Q = u[out_rows] @ Wqkv[:dq].T
     Kt = u @ Wqkv[dq:dq + dkv].T
     Vt = u @ Wqkv[dq + dkv:dq + 2 * dkv].T
+    pos = np.arange(X.shape[0]) if positions is None else np.asarray(positions)
+    Q, Kt = _qk_form(Q, Kt, lay, dims, pos[out_rows], pos[:m])
     O = causal_attention(Q, Kt, Vt, out_rows, Hq, Hkv, hd)
     a = O @ _f64(lay["w_o"]).T
     v = rmsnorm(X[out_rows] + a, lay["g_ffn"], dims.rms_eps)
@@ -166,8 +214,9 @@ def _routed_layer(x, lay, dims, ell, sel, bias, delta, sample):
     """The routed part of a sparse layer for given selections sel[b] (ascending positions).
 
     gate r = sigmoid(ell) on the selected tokens; attention and FFN over the packed selected
-    rows only; y_S = X + varsigma * r * (a + f) ([XMOD] Eq. (7)); unselected rows y = x
-    (Fig. 1(b), skip path); then b[S] += delta in fp32. sample: None or {b: packed rows}.
+    rows only; y_S = X + varsigma * r * (a + f) ([XMOD] Eq. (7)), or with lay["residual"] == 1
+    the MoD form y_S = X + a + r * f (Eq. (6)); unselected rows y = x (Fig. 1(b), skip path);
+    then b[S] += delta in fp32. sample: None or {b: packed rows}.
     """
     B = x.shape[0]
     gate = [sigmoid(ell[b, sel[b]]) for b in range(B)]
@@ -186,8 +235,12 @@ def _routed_layer(x, lay, dims, ell, sel, bias, delta, sample):
         out_rows = np.arange(len(sel[b])) if sample is None else np.asarray(sample[b])
         if len(out_rows) == 0:
             continue
-        a, f = _attn_ffn_on_rows(X, lay, dims, out_rows)
-        y_sel = X[out_rows] + (vs * gate[b][out_rows])[:, None] * (a + f)
+        a, f = _attn_ffn_on_rows(X, lay, dims, out_rows, positions=sel[b])
+        r = gate[b][out_rows][:, None]
+        if int(lay.get("residual", 0)) == 1:       # MoD, [XMOD] Eq. (6): only f is gated
+            y_sel = X[out_rows] + a + r * f
+        else:                                      # X-MoD, Eq. (7)
+            y_sel = X[out_rows] + (vs * r) * (a + f)
         if sample is None:
             y[b, sel[b]] = y_sel
         else:
@@ -313,6 +366,7 @@ def dense_layer(x, lay, dims, sample=None):
         Q = u[rows] @ Wqkv[:dq].T
         Kt = u @ Wqkv[dq:dq + dkv].T
         Vt = u @ Wqkv[dq + dkv:].T
+        Q, Kt = _qk_form(Q, Kt, lay, dims, rows, np.arange(m))
         a = causal_attention(Q, Kt, Vt, rows, Hq, Hkv, hd) @ Wo.T
         h = x[b, rows] + a
         f = swiglu_ffn(rmsnorm(h, lay["g_ffn"], dims.rms_eps), lay["w_gate"], lay["w_up"], lay["w_down"])

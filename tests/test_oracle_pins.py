@@ -230,6 +230,8 @@ def test_attention_closed_forms():
 # ---------------------------------------------------------------------------------------------
 
 def _brute_sparse_layer(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta, threshold=False):
+    # layer-form options, written out as loops: per-head RMSNorm of q / k, rotary embedding at
+    # the original position (rotate-half pairs), MoD's Eq. (6) residual
     """Plain-loop X-MoD layer written from the pages' steps, for tiny shapes only.
 
     threshold=True takes the eval-time rule instead of top-k: a token enters when its routing
@@ -266,6 +268,26 @@ def _brute_sparse_layer(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta, threshold
         q = [matvec(wqkv, uu, range(0, dq)) for uu in u]
         kk = [matvec(wqkv, uu, range(dq, dq + dkv)) for uu in u]
         vv = [matvec(wqkv, uu, range(dq + dkv, dq + 2 * dkv)) for uu in u]
+
+        def head_form(vec, n_heads, gain, pos):
+            out = list(vec)
+            for hh in range(n_heads):
+                seg = out[hh * hd:(hh + 1) * hd]
+                if gain is not None:
+                    seg = norm(seg, f64(gain))
+                theta = lay.get("rope_theta", 0.0)
+                if theta:
+                    half = hd // 2
+                    rot = list(seg)
+                    for i in range(half):
+                        ang = pos * theta ** (-2.0 * i / hd)
+                        rot[i] = seg[i] * math.cos(ang) - seg[i + half] * math.sin(ang)
+                        rot[i + half] = seg[i + half] * math.cos(ang) + seg[i] * math.sin(ang)
+                    seg = rot
+                out[hh * hd:(hh + 1) * hd] = seg
+            return out
+        q = [head_form(q[i], Hq, lay.get("q_norm"), S[i]) for i in range(len(S))]
+        kk = [head_form(kk[i], Hkv, lay.get("k_norm"), S[i]) for i in range(len(S))]
         G = Hq // Hkv
         for i, t in enumerate(S):
             o = []
@@ -285,7 +307,10 @@ def _brute_sparse_layer(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta, threshold
             f = matvec(wd, hid, range(d))
             r = 1.0 / (1.0 + math.exp(-float(logit[t])))
             for c in range(d):
-                y[b, t, c] = x[b, t, c] + lay["varsigma"] * r * (a[c] + f[c])
+                if lay.get("residual", 0) == 1:
+                    y[b, t, c] = x[b, t, c] + a[c] + r * f[c]
+                else:
+                    y[b, t, c] = x[b, t, c] + lay["varsigma"] * r * (a[c] + f[c])
             b_out[b, t] = np.float32(bias[b, t] + np.float32(delta))
     return y, b_out
 
@@ -640,3 +665,83 @@ def test_mask_agreement_reading_table10(golden_dir):
         _, K, agree, share = line.split()
         got = 100.0 * oracle.differing_selected_share(float(agree) / 100.0, int(K))
         assert round(got) == int(share), (line, got)
+
+
+# ---------------------------------------------------------------------------------------------
+# layer-form options: QK-norm, rotary embedding at original positions, MoD's Eq. (6) residual
+# ---------------------------------------------------------------------------------------------
+
+def test_rope_rotation_and_relative_positions():
+    rng = np.random.default_rng(90)
+    z = rng.standard_normal((5, 2))
+    pos = np.array([0, 1, 2, 7, 100])
+    got = oracle.rope(z, pos, 1, 2, 10000.0)          # head_dim 2: one pair, angle = position
+    for i, p_ in enumerate(pos):
+        R = np.array([[math.cos(p_), -math.sin(p_)], [math.sin(p_), math.cos(p_)]])
+        assert np.allclose(got[i], R @ z[i], rtol=1e-13, atol=1e-13)
+    Hh, hd = 3, 8
+    q = rng.standard_normal((1, Hh * hd))
+    k = rng.standard_normal((1, Hh * hd))
+    assert np.array_equal(oracle.rope(q, [0], Hh, hd, 500.0), q)           # position 0: identity
+    for theta in (10000.0, 1e6):
+        for (m, n, c) in [(5, 2, 11), (40, 40, 3), (3, 17, 250)]:
+            d1 = oracle.rope(q, [m], Hh, hd, theta) * oracle.rope(k, [n], Hh, hd, theta)
+            d2 = oracle.rope(q, [m + c], Hh, hd, theta) * oracle.rope(k, [n + c], Hh, hd, theta)
+            for hh in range(Hh):                       # per-head scores depend on m - n only
+                s1 = d1[0, hh * hd:(hh + 1) * hd].sum()
+                s2 = d2[0, hh * hd:(hh + 1) * hd].sum()
+                assert abs(s1 - s2) < 1e-11
+        r = oracle.rope(q, [123], Hh, hd, theta).reshape(Hh, 2, hd // 2)
+        q3 = q.reshape(Hh, 2, hd // 2)
+        assert np.allclose((r ** 2).sum(axis=1), (q3 ** 2).sum(axis=1))    # pairs keep their norm
+
+
+def test_qk_head_norm():
+    rng = np.random.default_rng(91)
+    Z = rng.standard_normal((4, 3 * 16)) * 5
+    ones = wl.f32_to_bf16_bits(np.ones(16, np.float32))
+    out = oracle.qk_head_norm(Z, 3, 16, ones, 0.0).reshape(4, 3, 16)
+    assert np.allclose(np.mean(out ** 2, axis=-1), 1.0)
+    assert np.allclose(oracle.qk_head_norm(7.0 * Z, 3, 16, ones, 0.0), oracle.qk_head_norm(Z, 3, 16, ones, 0.0))
+
+
+@pytest.mark.parametrize("form", ["qknorm+rope", "rope", "mod"])
+def test_sparse_layer_options_brute_force(form):
+    rng = np.random.default_rng(92 + len(form))
+    B, T, d, Hq, Hkv, hd, F, K = 2, 9, 8, 2, 1, 4, 6, 2
+    lay = _rand_layer(rng, d, Hq, Hkv, hd, F)
+    lay["router_bias"] = 0.1
+    lay["varsigma"] = 0.9
+    if "qknorm" in form:
+        lay["q_norm"] = wl.f32_to_bf16_bits((1 + 0.3 * rng.standard_normal(hd)).astype(np.float32))
+        lay["k_norm"] = wl.f32_to_bf16_bits((1 + 0.3 * rng.standard_normal(hd)).astype(np.float32))
+    if "rope" in form:
+        lay["rope_theta"] = 50.0
+    if form == "mod":
+        lay["residual"] = 1
+    x = bf16_to_f64(wl.f32_to_bf16_bits(rng.standard_normal((B, T, d)).astype(np.float32)))
+    bias = (rng.standard_normal((B, T)) * 0.2).astype(np.float32)
+    dims = Dims(Hq, Hkv, hd, 1e-5)
+    got = oracle.sparse_layer(x, lay, dims, K, bias=bias, tau=1.0, delta=0.05)
+    want_y, _ = _brute_sparse_layer(x, lay, Hq, Hkv, hd, 1e-5, K, bias, 1.0, 0.05)
+    assert np.allclose(got["y"], want_y, rtol=1e-11, atol=1e-12)
+
+
+def test_mod_residual_with_zero_attention_output_equals_gated_form():
+    x, lay, dims = _tiny(seed=93)
+    lay = dict(lay, varsigma=1.0, w_o=np.zeros_like(lay["w_o"]))     # a = 0
+    y7 = oracle.sparse_layer(x, lay, dims, 3)["y"]
+    y6 = oracle.sparse_layer(x, dict(lay, residual=1), dims, 3)["y"]
+    assert np.array_equal(y6, y7)
+
+
+def test_check1_with_rope_and_qknorm_equals_dense_layer():
+    x, lay, dims = _tiny(seed=94)
+    rng = np.random.default_rng(95)
+    lay = dict(lay, w_router=np.zeros_like(lay["w_router"]), router_bias=100.0, varsigma=1.0,
+               rope_theta=1000.0,
+               q_norm=wl.f32_to_bf16_bits((1 + 0.2 * rng.standard_normal(4)).astype(np.float32)),
+               k_norm=wl.f32_to_bf16_bits((1 + 0.2 * rng.standard_normal(4)).astype(np.float32)))
+    ys = oracle.sparse_layer(x, lay, dims, 1)["y"]
+    yd = oracle.dense_layer(x, lay, dims)
+    assert np.allclose(ys, yd, rtol=1e-12, atol=1e-12)
