@@ -93,6 +93,16 @@ typedef struct {
   const void *w_gate;    /* [F, d] */
   const void *w_up;      /* [F, d] */
   const void *w_down;    /* [d, F] */
+  /* Layer-form options; zero / NULL gives the layer described at the top of this file. */
+  int32_t residual;      /* 0: X-MoD, y = X + (varsigma*r)*(a + f), Eq. (7); 1: MoD,
+                            y = (X + a) + r*f, [XMOD] Eq. (6) (varsigma unused). Sparse layers. */
+  const void *q_norm;    /* [head_dim] bf16 or NULL: RMSNorm of every query head (QK-norm) */
+  const void *k_norm;    /* [head_dim] bf16 or NULL: RMSNorm of every key head */
+  float rope_theta;      /* > 0: rotary embedding of queries and keys at the tokens' original
+                            positions, pairs (i, i + hd/2) rotated by pos * theta^(-2i/hd),
+                            after the QK-norm; 0: none. (The page's backbones follow the Qwen3
+                            structure, [XMOD] "backbone configuration"; the pages do not list
+                            these parts, so they are options.) */
 } xmod_layer;
 
 /* Entry-point ids for xmod_workspace_bytes(). */

@@ -55,6 +55,11 @@ __device__ __forceinline__ float gated_residual(float X, float g, float a, float
 __device__ __forceinline__ float dense_residual(float X, float a, float f) {
   return __fadd_rn(X, __fadd_rn(a, f));
 }
+// MoD's residual of a routed token: the attention output enters ungated, the FFN output gated
+// by the router score r: y = (X + a) + r*f, each operation rounded in fp32.
+__device__ __forceinline__ float mod_residual(float X, float r, float a, float f) {
+  return __fadd_rn(__fadd_rn(X, a), __fmul_rn(r, f));
+}
 
 }  // namespace xmod
 
@@ -125,6 +130,13 @@ hipError_t launch_scatter(uint16_t *x, const RowMap &map, const float *gate, flo
                           const uint16_t *a, const uint16_t *f, int64_t rows, int d,
                           hipStream_t s);
 
+// In place on the packed [Q | K | V] rows (row m of M, or of the device count): per-head RMSNorm
+// of the queries (q_norm) and keys (k_norm), when given, then the rotary embedding at each
+// row's original position (x row % T) when theta > 0. V is untouched.
+hipError_t launch_qk_form(uint16_t *qkv, int ld_qkv, const RowMap &map, int64_t rows, int Hq,
+                          int Hkv, int hd, const uint16_t *q_norm, const uint16_t *k_norm,
+                          float eps, float theta, hipStream_t s);
+
 enum GemmEpilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2, EPI_STORE_F32 = 3 };
 
 struct GemmArgs {
@@ -141,6 +153,7 @@ struct GemmArgs {
   // [M, N] with leading dimension ldc, as is x.
   RowMap map;
   uint16_t *x; const float *gate; float varsigma; const float *a;
+  int residual_form;  // EPI_RESIDUAL with gate: 0 X + (varsigma*gate)*(a + f); 1 (X + a) + gate*f
 };
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s);

@@ -345,7 +345,8 @@ gemm_kernel(GemmArgs g) {
         const float *ap = g.a + (size_t)m * g.ldc + n;
         const f32x4 a0 = *(const f32x4 *)ap, a1 = *(const f32x4 *)(ap + 4);
         const u32x4 xv = *(const u32x4 *)xp;
-        const float gg = g.gate ? __fmul_rn(g.varsigma, g.gate[m]) : 0.f;
+        const bool mod = g.gate && g.residual_form == 1;
+        const float gg = g.gate ? (mod ? g.gate[m] : __fmul_rn(g.varsigma, g.gate[m])) : 0.f;
         u32x4 yv;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -355,8 +356,10 @@ gemm_kernel(GemmArgs g) {
           const float ahi = h < 2 ? a0[2 * h + 1] : a1[2 * h - 3];
           const float flo = h < 2 ? f0[2 * h] : f1[2 * h - 4];
           const float fhi = h < 2 ? f0[2 * h + 1] : f1[2 * h - 3];
-          const float ylo = g.gate ? gated_residual(xlo, gg, alo, flo) : dense_residual(xlo, alo, flo);
-          const float yhi = g.gate ? gated_residual(xhi, gg, ahi, fhi) : dense_residual(xhi, ahi, fhi);
+          const float ylo = !g.gate ? dense_residual(xlo, alo, flo)
+                            : mod ? mod_residual(xlo, gg, alo, flo) : gated_residual(xlo, gg, alo, flo);
+          const float yhi = !g.gate ? dense_residual(xhi, ahi, fhi)
+                            : mod ? mod_residual(xhi, gg, ahi, fhi) : gated_residual(xhi, gg, ahi, fhi);
           yv[h] = pack_bf16x2(ylo, yhi);
         }
         *(u32x4 *)xp = yv;

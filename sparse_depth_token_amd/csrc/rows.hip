@@ -141,6 +141,58 @@ __global__ __launch_bounds__(256) void scatter_kernel(uint16_t *__restrict__ x, 
   }  // row loop
 }
 
+// Per-head RMSNorm (QK-norm) and rotary embedding of the packed queries and keys, in place.
+// Query head h of a row sits at columns h*HD, key head g at (Hq + g)*HD. One head is handled by
+// HD/2 lanes: lane i holds the pair (i, i + HD/2) that the rotation mixes. The rotation angle
+// is pos * theta^(-2i/HD), taken in double and reduced to [-pi, pi] before the fp32 sine and
+// cosine, so long positions lose no accuracy.
+template <int HD>
+__global__ __launch_bounds__(256) void qk_form_kernel(uint16_t *__restrict__ qkv, int ldq,
+                                                      RowMap map, int64_t rows, int Hq, int Hkv,
+                                                      const uint16_t *__restrict__ q_norm,
+                                                      const uint16_t *__restrict__ k_norm,
+                                                      float eps, float theta) {
+  constexpr int P = HD / 2;     // lanes per head
+  constexpr int TPW = 64 / P;   // heads per wave
+  const int lane = threadIdx.x & 63, sub = lane / P, i = lane % P;
+  const int nh = Hq + Hkv;
+  const int64_t n_tasks = rowmap_count(map, rows) * nh;
+  const double inv_freq = theta > 0.f ? pow((double)theta, -2.0 * i / HD) : 0.0;
+  const int64_t stride = (int64_t)gridDim.x * 4 * TPW;
+  for (int64_t t0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW; t0 < n_tasks;
+       t0 += stride) {
+    const int64_t task = t0 + sub;
+    const bool valid = task < n_tasks;
+    const int64_t m = valid ? task / nh : 0;
+    const int h = valid ? (int)(task % nh) : 0;
+    const uint16_t *gain = h < Hq ? q_norm : k_norm;
+    uint16_t *z = qkv + m * ldq + (int64_t)h * HD;
+    float z1 = valid ? bf16_to_f32(z[i]) : 0.f, z2 = valid ? bf16_to_f32(z[i + P]) : 0.f;
+    float ss = z1 * z1 + z2 * z2;
+#pragma unroll
+    for (int o = P / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);  // within the head's lanes
+    if (valid && gain) {
+      const float r = 1.0f / sqrtf(ss / (float)HD + eps);
+      z1 = z1 * r * bf16_to_f32(gain[i]);
+      z2 = z2 * r * bf16_to_f32(gain[i + P]);
+    }
+    if (valid && theta > 0.f) {
+      const int64_t pos = rowmap_x(map, m) % map.T;
+      double ang = (double)pos * inv_freq;
+      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+      float sn, cs;
+      sincosf((float)ang, &sn, &cs);
+      const float r1 = z1 * cs - z2 * sn, r2 = z2 * cs + z1 * sn;
+      z1 = r1;
+      z2 = r2;
+    }
+    if (valid && (gain || theta > 0.f)) {
+      z[i] = f32_to_bf16(z1);
+      z[i + P] = f32_to_bf16(z2);
+    }
+  }
+}
+
 static int ni_for(int d) { return ((d >> 3) + 63) / 64; }
 
 #define XMOD_NI_SWITCH(ni, MACRO)                 \
@@ -201,6 +253,22 @@ hipError_t launch_scatter(uint16_t *x, const RowMap &map, const float *gate, flo
                      d, rows)
   XMOD_NI_SWITCH(ni_for(d), L_)
 #undef L_
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_form(uint16_t *qkv, int ld_qkv, const RowMap &map, int64_t rows, int Hq,
+                          int Hkv, int hd, const uint16_t *q_norm, const uint16_t *k_norm,
+                          float eps, float theta, hipStream_t s) {
+  if (rows < 1 || (!q_norm && !k_norm && !(theta > 0.f))) return hipSuccess;
+  const int64_t waves = (rows * (Hq + Hkv) * (hd / 2) + 63) / 64;
+  const int64_t wgs = (waves + 3) / 4;
+  const dim3 grid((unsigned)(wgs < 4096 ? wgs : 4096));
+  if (hd == 128)
+    hipLaunchKernelGGL(qk_form_kernel<128>, grid, dim3(256), 0, s, qkv, ld_qkv, map, rows, Hq,
+                       Hkv, q_norm, k_norm, eps, theta);
+  else
+    hipLaunchKernelGGL(qk_form_kernel<64>, grid, dim3(256), 0, s, qkv, ld_qkv, map, rows, Hq,
+                       Hkv, q_norm, k_norm, eps, theta);
   return hipGetLastError();
 }
 

@@ -74,6 +74,8 @@ bool layer_ok(const xmod_layer *L, bool sparse) {
   if (!L->g_attn || !L->w_qkv || !L->w_o || !L->g_ffn || !L->w_gate || !L->w_up || !L->w_down)
     return false;
   if (!isfinite(L->router_bias) || !isfinite(L->varsigma)) return false;
+  if (L->residual != 0 && L->residual != 1) return false;
+  if (!(L->rope_theta >= 0.f) || !isfinite(L->rope_theta)) return false;
   return true;
 }
 
@@ -133,6 +135,10 @@ xmod_status run_body(uint16_t *x, const RowMap &map, int64_t M, const int32_t *s
   g.M = (int)M; g.N = nqkv; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_STORE, s));
   phase_mark(s);
+  // optional QK-norm / rotary embedding (timed with the attention slot)
+  XMOD_HIP(launch_qk_form(qkv, nqkv, map, M, dm->n_q_heads, dm->n_kv_heads, dm->head_dim,
+                          (const uint16_t *)L->q_norm, (const uint16_t *)L->k_norm, dm->rms_eps,
+                          L->rope_theta, s));
   XMOD_HIP(launch_attention(qkv, nqkv, o, dq, B, k, dm->n_q_heads, dm->n_kv_heads, dm->head_dim,
                             seq_off, seq_len, s));
   phase_mark(s);
@@ -154,7 +160,7 @@ xmod_status run_body(uint16_t *x, const RowMap &map, int64_t M, const int32_t *s
   g.map = map;
   g.A = gbuf; g.lda = dm->ffn_hidden; g.B = (const uint16_t *)L->w_down; g.ldb = dm->ffn_hidden;
   g.ldc = d; g.M = (int)M; g.N = d; g.K = dm->ffn_hidden;
-  g.x = x; g.gate = gate; g.varsigma = L->varsigma; g.a = a;
+  g.x = x; g.gate = gate; g.varsigma = L->varsigma; g.a = a; g.residual_form = L->residual;
   XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
   phase_mark(s);
   return XMOD_OK;

@@ -41,7 +41,9 @@ class Layer(ctypes.Structure):
                 ("varsigma", ctypes.c_float), ("g_attn", ctypes.c_void_p),
                 ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("g_ffn", ctypes.c_void_p),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("residual", ctypes.c_int32),
+                ("q_norm", ctypes.c_void_p), ("k_norm", ctypes.c_void_p),
+                ("rope_theta", ctypes.c_float)]
 
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -103,11 +105,13 @@ def make_dims(B, T, d, n_q_heads, n_kv_heads, head_dim, ffn_hidden, rms_eps=1e-6
 
 def make_layer(w: dict) -> Layer:
     """w: dict of device tensors (bf16) w_router, g_attn, w_qkv, w_o, g_ffn, w_gate, w_up,
-    w_down, and host floats router_bias, varsigma."""
+    w_down, optional q_norm / k_norm, and host values router_bias, varsigma, optional residual
+    (0 or 1) and rope_theta."""
     return Layer(_ptr(w.get("w_router")), float(w.get("router_bias", 0.0)),
                  float(w.get("varsigma", 1.0)), _ptr(w["g_attn"]), _ptr(w["w_qkv"]),
                  _ptr(w["w_o"]), _ptr(w["g_ffn"]), _ptr(w["w_gate"]), _ptr(w["w_up"]),
-                 _ptr(w["w_down"]))
+                 _ptr(w["w_down"]), int(w.get("residual", 0)), _ptr(w.get("q_norm")),
+                 _ptr(w.get("k_norm")), float(w.get("rope_theta", 0.0) or 0.0))
 
 
 def workspace_bytes(dims: Dims, K: int, entry: int) -> int:

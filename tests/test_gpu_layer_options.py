@@ -1,0 +1,96 @@
+"""Layer-form options on the GPU vs the oracle: per-head QK-norm and rotary embedding at the
+tokens' original positions (the Qwen3 structure the X-MoD review's backbones follow, section
+"backbone configuration"), and MoD's Eq. (6) residual. Same bar as the plain layer."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as wl
+from parity import bf16_vals, check_values, dev_bf16, host_bits, layer_to_device, say
+from test_gpu_layer import check_sparse, run_sparse_gpu, run_dense_gpu
+from test_gpu_threshold import check_threshold, run_threshold_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def x():
+    from sparse_depth_token_amd import xmod
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return xmod
+
+
+def _gains(rng, hd, std=0.2):
+    return wl.f32_to_bf16_bits((1 + std * rng.standard_normal(hd)).astype(np.float32))
+
+
+def with_options(w, lay, qk=False, theta=0.0, residual=0, seed=0):
+    rng = np.random.default_rng(100 + seed)
+    lay = dict(lay)
+    if qk:
+        lay["q_norm"] = _gains(rng, w.head_dim)
+        lay["k_norm"] = _gains(rng, w.head_dim)
+    if theta:
+        lay["rope_theta"] = float(theta)
+    if residual:
+        lay["residual"] = residual
+    return lay
+
+
+CASES = {
+    "QK-norm + RoPE 1e4, B2 T1024 K4 d1024 GQA 8/2 hd128": (
+        wl.Workload("opt_a", 110, 2, 1024, 1024, 8, 2, 128, 2816, 4, bias_std=0.1,
+                    varsigma_range=(0.5, 1.5)), dict(qk=True, theta=1e4)),
+    "RoPE 1e6 only, B1 T4096 K8 d512 8/8 hd64 (long positions)": (
+        wl.Workload("opt_b", 111, 1, 4096, 512, 8, 8, 64, 1536, 8), dict(theta=1e6)),
+    "MoD Eq. (6) residual, B3 T700 K3 d512 GQA 8/2 hd64": (
+        wl.Workload("opt_c", 112, 3, 700, 512, 8, 2, 64, 1536, 3, bias_std=0.1,
+                    varsigma_range=(0.5, 1.5), gain_std=0.1), dict(residual=1)),
+    "all options, B2 T512 K2 d256": (
+        wl.Workload("opt_d", 113, 2, 512, 256, 4, 4, 64, 1024, 2, bias_std=0.1),
+        dict(qk=True, theta=500.0, residual=1)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_sparse_layer_options(x, name):
+    w, opts = CASES[name]
+    say(f"[layer options] {name}")
+    xb = wl.make_x(w)
+    lay = with_options(w, wl.make_layer(w, 0), seed=len(name), **opts)
+    bias = wl.make_bias(w)
+    got = run_sparse_gpu(x, w, xb, lay, bias)
+    check_sparse(w, xb, lay, bias, got)
+
+
+def test_threshold_layer_with_rope(x):
+    w = wl.Workload("opt_thr", 114, 3, 800, 512, 8, 2, 64, 1536, 1, bias_std=0.1, router_bias=0.1)
+    say("[layer options] threshold routing + QK-norm + RoPE at original positions")
+    xb = wl.make_x(w)
+    lay = with_options(w, wl.make_layer(w, 0), qk=True, theta=1e4, seed=5)
+    bias = wl.make_bias(w)
+    got = run_threshold_gpu(x, w, xb, lay, bias)
+    check_threshold(w, xb, lay, bias, got)
+
+
+def test_dense_layer_with_rope_and_qknorm(x):
+    w = wl.Workload("opt_dense", 115, 2, 333, 512, 8, 2, 64, 1024, 1, gain_std=0.1)
+    say("[layer options] dense layer + QK-norm + RoPE")
+    xb = wl.make_x(w)
+    lay = with_options(w, wl.make_layer(w, 0), qk=True, theta=1e4, seed=6)
+    y = run_dense_gpu(x, w, xb, lay)
+    ref = oracle.dense_layer(xb, lay, w)
+    check_values(bf16_vals(y), ref, "dense + options")
+
+
+def test_invalid_options_rejected(x):
+    w = wl.WORKLOADS["sparse_k2_b2x512_d256"]
+    lay = layer_to_device(wl.make_layer(w, 0))
+    dims = x.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden, w.rms_eps)
+    ws = x.alloc_workspace(dims, w.K, x.WS_SPARSE_LAYER)
+    xt = dev_bf16(wl.make_x(w))
+    for bad in (dict(residual=2), dict(rope_theta=-1.0), dict(rope_theta=float("inf"))):
+        L = x.make_layer(dict(lay, **bad))
+        with pytest.raises(x.XmodError):
+            x.sparse_layer_fwd(xt, L, dims, w.K, None, 1.0, 0.0, ws)
