@@ -18,7 +18,8 @@ cases that reduce to a textbook definition.
 from .layer import (router_logits, topk_select, sigmoid, rmsnorm, causal_attention, silu,
                     swiglu_ffn, sparse_layer, dense_layer, threshold_select,
                     sparse_layer_threshold, mask_agreement, differing_selected_share,
-                    qk_head_norm, rope)
+                    qk_head_norm, rope, attention_layer, routed_ffn_layer,
+                    sparse_layer_fullkv)
 from .stack import (stack_layer_kinds, physical_layers, active_equivalent_layers, total_params,
                     active_params, layer_params, flops_per_token_pages_convention, block_forward,
                     coverage, adjacent_jaccard, coverage_independent_reference,

@@ -343,6 +343,116 @@ def differing_selected_share(agreement, K):
     return (1.0 - float(agreement)) / 2.0 * float(K)
 
 
+# --- mechanism controls: [XMOD] "mechanism controls: conditional capacity vs attention
+#     context" (Table 7 and the two counterfactuals above it) ----------------------------------
+
+def attention_layer(x, lay, dims, sample=None):
+    """The full-sequence attention block of the Routed-FFN control: y = x + Attn(RMSNorm(x))
+    for every token (causal over the whole sequence; optional QK-norm / RoPE), no FFN.
+    sample: None or {b: positions}."""
+    x = _f64(x)
+    B, T, d = x.shape
+    Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    dq, dkv = Hq * hd, Hkv * hd
+    Wqkv = _f64(lay["w_qkv"])
+    out = x.copy() if sample is None else {}
+    for b in (range(B) if sample is None else sorted(sample)):
+        rows = np.arange(T) if sample is None else np.asarray(sample[b])
+        m = int(rows.max()) + 1
+        u = rmsnorm(x[b, :m], lay["g_attn"], dims.rms_eps)
+        Q = u[rows] @ Wqkv[:dq].T
+        Kt = u @ Wqkv[dq:dq + dkv].T
+        Vt = u @ Wqkv[dq + dkv:].T
+        Q, Kt = _qk_form(Q, Kt, lay, dims, rows, np.arange(m))
+        y = x[b, rows] + causal_attention(Q, Kt, Vt, rows, Hq, Hkv, hd) @ _f64(lay["w_o"]).T
+        if sample is None:
+            out[b] = y
+        else:
+            out[b] = (rows, y)
+    return out
+
+
+def routed_ffn_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0):
+    """A routed FFN refinement of the Routed-FFN control: the router and top-1/K selection of
+    the sparse layer, then only the FFN on the selected rows, y_S = X + varsigma * r * f with
+    f = SwiGLU(RMSNorm(X; g_ffn)) (the gated residual of Eq. (7) with no attention part);
+    unselected rows unchanged; b[S] += delta. Returns the same dict as sparse_layer (no
+    sampling: the FFN is row-local, so every row is cheap)."""
+    x = _f64(x)
+    B, T, d = x.shape
+    k = T // K
+    assert k >= 1
+    if bias is None:
+        bias = np.zeros((B, T), dtype=np.float32)
+    bias = np.asarray(bias, dtype=np.float32)
+    s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
+    idx = topk_select(ell, k)
+    bsel = np.arange(B)[:, None]
+    gate = sigmoid(ell[bsel, idx])
+    bias_out = bias.copy()
+    bias_out[bsel, idx] = (bias[bsel, idx] + np.float32(delta)).astype(np.float32)
+    vs = float(lay.get("varsigma", 1.0))
+    y = x.copy()
+    for b in range(B):
+        X = x[b, idx[b]]
+        f = swiglu_ffn(rmsnorm(X, lay["g_ffn"], dims.rms_eps), lay["w_gate"], lay["w_up"],
+                       lay["w_down"])
+        y[b, idx[b]] = X + (vs * gate[b])[:, None] * f
+    return {"s": s, "ell": ell, "idx": idx, "gate": gate, "bias_out": bias_out, "y": y}
+
+
+def sparse_layer_fullkv(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, sample=None):
+    """The Selected-Q/full-KV control: the sparse layer's router, selection, gate, FFN and
+    residual (Eq. (7)), but every token of the sequence supplies keys and values: the query of
+    a selected token at original position t attends to all tokens at positions <= t.
+
+    u = RMSNorm(x; g_attn) over all rows; K, V from every row; Q from the selected rows;
+    optional QK-norm / RoPE at original positions. sample: None or {b: packed rows}."""
+    x = _f64(x)
+    B, T, d = x.shape
+    k = T // K
+    assert k >= 1
+    if bias is None:
+        bias = np.zeros((B, T), dtype=np.float32)
+    bias = np.asarray(bias, dtype=np.float32)
+    s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
+    idx = topk_select(ell, k)
+    bsel = np.arange(B)[:, None]
+    gate = sigmoid(ell[bsel, idx])
+    bias_out = bias.copy()
+    bias_out[bsel, idx] = (bias[bsel, idx] + np.float32(delta)).astype(np.float32)
+    vs = float(lay.get("varsigma", 1.0))
+    Hq, Hkv, hd = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    dq, dkv = Hq * hd, Hkv * hd
+    Wqkv = _f64(lay["w_qkv"])
+    res = {"s": s, "ell": ell, "idx": idx, "gate": gate, "bias_out": bias_out}
+    y = x.copy() if sample is None else None
+    rows_out = {}
+    for b in (range(B) if sample is None else sorted(sample)):
+        prow = np.arange(k) if sample is None else np.asarray(sample[b])
+        pos = idx[b, prow]                                   # original positions of the queries
+        m = int(pos.max()) + 1
+        u = rmsnorm(x[b, :m], lay["g_attn"], dims.rms_eps)
+        Q = u[pos] @ Wqkv[:dq].T
+        Kt = u @ Wqkv[dq:dq + dkv].T
+        Vt = u @ Wqkv[dq + dkv:].T
+        Q, Kt = _qk_form(Q, Kt, lay, dims, pos, np.arange(m))
+        a = causal_attention(Q, Kt, Vt, pos, Hq, Hkv, hd) @ _f64(lay["w_o"]).T
+        X = x[b, pos]
+        f = swiglu_ffn(rmsnorm(X + a, lay["g_ffn"], dims.rms_eps), lay["w_gate"], lay["w_up"],
+                       lay["w_down"])
+        y_sel = X + (vs * gate[b, prow])[:, None] * (a + f)
+        if sample is None:
+            y[b, pos] = y_sel
+        else:
+            rows_out[b] = (prow, pos, y_sel)
+    if sample is None:
+        res["y"] = y
+    else:
+        res["rows"] = rows_out
+    return res
+
+
 # --- the dense layer: every token enters, no gate ---------------------------------------------
 
 def dense_layer(x, lay, dims, sample=None):

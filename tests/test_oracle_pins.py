@@ -745,3 +745,106 @@ def test_check1_with_rope_and_qknorm_equals_dense_layer():
     ys = oracle.sparse_layer(x, lay, dims, 1)["y"]
     yd = oracle.dense_layer(x, lay, dims)
     assert np.allclose(ys, yd, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# mechanism controls (Table 7): Routed-FFN and Selected-Q/full-KV
+# ---------------------------------------------------------------------------------------------
+
+def test_attention_block_then_full_ffn_refinement_is_the_dense_layer():
+    x, lay, dims = _tiny(seed=120)
+    lay = dict(lay, w_router=np.zeros_like(lay["w_router"]), router_bias=100.0, varsigma=1.0)
+    h = oracle.attention_layer(x, lay, dims)
+    y = oracle.routed_ffn_layer(h, lay, dims, 1)["y"]           # every token, r = 1
+    assert np.array_equal(y, oracle.dense_layer(x, lay, dims))
+
+
+def test_fullkv_with_every_token_selected_is_the_sparse_layer():
+    x, lay, dims = _tiny(seed=121)
+    bias = (np.random.default_rng(122).standard_normal(x.shape[:2]) * 0.1).astype(np.float32)
+    a = oracle.sparse_layer_fullkv(x, lay, dims, 1, bias=bias, delta=0.05)
+    b = oracle.sparse_layer(x, lay, dims, 1, bias=bias, delta=0.05)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["bias_out"], b["bias_out"])
+
+
+def _brute_fullkv_and_routed_ffn(x, lay, Hq, Hkv, hd, eps, K, bias, tau, delta, mode):
+    """Plain loops: mode "fullkv" (selected queries, every token's keys / values at positions
+    <= the query's) or "ffn" (the FFN alone on the selected rows)."""
+    B, T, d = x.shape
+    k = T // K
+    f64 = lambda a: bf16_to_f64(a) if np.asarray(a).dtype == np.uint16 else np.asarray(a, float)
+    wr, wqkv, wo = f64(lay["w_router"]), f64(lay["w_qkv"]), f64(lay["w_o"])
+    wg, wu, wd = f64(lay["w_gate"]), f64(lay["w_up"]), f64(lay["w_down"])
+    g1, g2 = f64(lay["g_attn"]), f64(lay["g_ffn"])
+    F = wg.shape[0]
+    dq, dkv = Hq * hd, Hkv * hd
+    y = x.copy()
+
+    def norm(vec, g):
+        r = math.sqrt(sum(v * v for v in vec) / len(vec) + eps)
+        return [vec[c] / r * g[c] for c in range(len(vec))]
+
+    def matvec(Wm, vec, rows):
+        return [sum(Wm[r, c] * vec[c] for c in range(len(vec))) for r in rows]
+
+    def ffn(v):
+        gp, up = matvec(wg, v, range(F)), matvec(wu, v, range(F))
+        return matvec(wd, [gp[n] / (1 + math.exp(-gp[n])) * up[n] for n in range(F)], range(d))
+
+    for b in range(B):
+        logit = []
+        for t in range(T):
+            s = np.float32(math.fsum([x[b, t, c] * wr[c] for c in range(d)]) + lay["router_bias"])
+            logit.append(np.float32(s - np.float32(np.float32(tau) * bias[b, t])))
+        S = sorted(sorted(range(T), key=lambda t: (-float(logit[t]), t))[:k])
+        u_all = [norm(list(x[b, t]), g1) for t in range(T)]
+        kk = [matvec(wqkv, u_all[t], range(dq, dq + dkv)) for t in range(T)]
+        vv = [matvec(wqkv, u_all[t], range(dq + dkv, dq + 2 * dkv)) for t in range(T)]
+        for t in S:
+            r = 1.0 / (1.0 + math.exp(-float(logit[t])))
+            if mode == "ffn":
+                f = ffn(norm(list(x[b, t]), g2))
+                for c in range(d):
+                    y[b, t, c] = x[b, t, c] + lay["varsigma"] * r * f[c]
+                continue
+            q = matvec(wqkv, u_all[t], range(dq))
+            o = []
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                sc = [sum(q[h * hd + c] * kk[j][g * hd + c] for c in range(hd)) / math.sqrt(hd)
+                      for j in range(t + 1)]
+                mx = max(sc)
+                w = [math.exp(v - mx) for v in sc]
+                o += [sum(w[j] * vv[j][g * hd + c] for j in range(t + 1)) / sum(w) for c in range(hd)]
+            a = matvec(wo, o, range(d))
+            f = ffn(norm([x[b, t, c] + a[c] for c in range(d)], g2))
+            for c in range(d):
+                y[b, t, c] = x[b, t, c] + lay["varsigma"] * r * (a[c] + f[c])
+    return y
+
+
+@pytest.mark.parametrize("mode", ["fullkv", "ffn"])
+def test_mechanism_controls_brute_force(mode):
+    rng = np.random.default_rng(123 if mode == "fullkv" else 124)
+    B, T, d, Hq, Hkv, hd, F, K = 2, 9, 8, 2, 1, 2, 6, 3
+    lay = _rand_layer(rng, d, Hq, Hkv, hd, F)
+    lay["router_bias"] = -0.2
+    lay["varsigma"] = 1.3
+    x = bf16_to_f64(wl.f32_to_bf16_bits(rng.standard_normal((B, T, d)).astype(np.float32)))
+    bias = (rng.standard_normal((B, T)) * 0.2).astype(np.float32)
+    dims = Dims(Hq, Hkv, hd, 1e-5)
+    if mode == "fullkv":
+        got = oracle.sparse_layer_fullkv(x, lay, dims, K, bias=bias, tau=1.0, delta=0.05)
+    else:
+        got = oracle.routed_ffn_layer(x, lay, dims, K, bias=bias, tau=1.0, delta=0.05)
+    want = _brute_fullkv_and_routed_ffn(x, lay, Hq, Hkv, hd, 1e-5, K, bias, 1.0, 0.05, mode)
+    assert np.allclose(got["y"], want, rtol=1e-11, atol=1e-12)
+
+
+def test_fullkv_sampling_matches_full():
+    x, lay, dims = _tiny(seed=125, T=32)
+    r = oracle.sparse_layer_fullkv(x, lay, dims, 4)
+    rs = oracle.sparse_layer_fullkv(x, lay, dims, 4, sample={0: np.array([0, 3, 7]), 1: np.array([5])})
+    for b, (prow, pos, ysel) in rs["rows"].items():
+        # same arithmetic on fewer rows: equal up to the blocking of the float64 products
+        assert np.allclose(ysel, r["y"][b, pos], rtol=1e-13, atol=1e-13)
