@@ -13,6 +13,8 @@
  *          and before the FFN, unselected rows passed through.
  *   [MOE]  "Beyond dense Transformers: MoE, SSMs and hybrids", bias-free SwiGLU FFN.
  *   [MODA] "Mixture-of-Depths Attention" reading notes, section 2.1: GQA head mapping.
+ *   [XMOD] section "mechanism controls" (Table 7): the Routed-FFN and Selected-Q/full-KV
+ *          counterfactuals.
  *   [XMOD] section "training-time top-k, eval-time causal threshold": at evaluation a token
  *          enters a sparse layer when its routing probability is at least 1/2; section
  *          "routing diagnostics", Table 10: agreement of the top-k and threshold masks.
@@ -111,7 +113,10 @@ enum {
   XMOD_WS_SPARSE_LAYER = 1,
   XMOD_WS_DENSE_LAYER = 2,
   XMOD_WS_BLOCK = 3,
-  XMOD_WS_SPARSE_THRESHOLD = 4
+  XMOD_WS_SPARSE_THRESHOLD = 4,
+  XMOD_WS_ROUTED_FFN = 5,
+  XMOD_WS_ATTN_LAYER = 6,
+  XMOD_WS_SPARSE_FULLKV = 7
 };
 
 /* Workspace bytes an entry point needs for these shapes (0 if none). K is ignored for the
@@ -191,6 +196,36 @@ xmod_status xmod_sparse_layer_fwd_threshold(void *x, const xmod_layer *layer,
  * *agree and may accumulate over layers; the rate is agree / (B*T*layers). */
 xmod_status xmod_mask_agreement(const float *logits, const int32_t *idx, int32_t B, int32_t T,
                                 int32_t k, uint32_t *agree, void *stream);
+
+/* --- Mechanism controls ([XMOD] "mechanism controls: conditional capacity vs attention
+ * context", Table 7). ------------------------------------------------------------------------ */
+
+/* One routed FFN refinement of the Routed-FFN control, in place on x: the sparse layer's router
+ * and top-1/K selection, then only the FFN on the selected rows,
+ *   y_S = X + (varsigma * r) * f,  f = SwiGLU(RMSNorm(X; g_ffn)),
+ * unselected rows untouched, bias[idx] += delta. Uses w_router, router_bias, varsigma, g_ffn,
+ * w_gate, w_up, w_down of the layer. Workspace: XMOD_WS_ROUTED_FFN. */
+xmod_status xmod_routed_ffn_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                int32_t K, float *bias, float tau, float delta,
+                                int32_t *idx_out, float *gate_out, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* The full-sequence attention block of the Routed-FFN control, in place on x:
+ * y = x + Attn(RMSNorm(x; g_attn)) W_o^T for every token (causal over the whole sequence, GQA,
+ * optional QK-norm / RoPE), no FFN. Uses g_attn, w_qkv, w_o and the layer-form options.
+ * Workspace: XMOD_WS_ATTN_LAYER (K ignored). */
+xmod_status xmod_attention_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/* The Selected-Q/full-KV control, in place on x: the sparse layer's router, top-1/K selection,
+ * gate, FFN and residual, but every token supplies keys and values: with u = RMSNorm(x; g_attn)
+ * over all rows, K and V come from every row and Q from the selected rows, and the selected
+ * query at original position t attends to all positions <= t. Workspace: XMOD_WS_SPARSE_FULLKV
+ * (keys and values of all B*T rows). Arguments as xmod_sparse_layer_fwd. */
+xmod_status xmod_sparse_layer_fwd_fullkv(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                         int32_t K, float *bias, float tau, float delta,
+                                         int32_t *idx_out, float *gate_out, void *ws,
+                                         size_t ws_bytes, void *stream);
 
 /* Forward of one dense layer (every token, no gate): y = x + (a + f), in place on x. */
 xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,

@@ -55,13 +55,24 @@ struct AttnCfg {
   }
 };
 
-template <int HD>
+// Keys and values of the whole sequence for the Selected-Q/full-KV control: kv rows b*T + j
+// hold [K heads | V heads] (leading dimension ldkv); qpos[b*k + q] is the original position of
+// packed query q; query q sees keys j <= qpos.
+struct FullKV {
+  const uint16_t *kv = nullptr;
+  int ldkv = 0;
+  const int32_t *qpos = nullptr;
+  int T = 0;
+};
+
+template <int HD, bool FULLKV>
 __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
                                                       uint16_t *__restrict__ o, int ldo,
                                                       int k_fixed, int Hq, int Hkv,
                                                       float scale_log2,
                                                       const int32_t *__restrict__ seq_off,
-                                                      const int32_t *__restrict__ seq_len) {
+                                                      const int32_t *__restrict__ seq_len,
+                                                      FullKV fkv) {
   using C = AttnCfg<HD>;
   constexpr int BQ = C::BQ, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
   // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
@@ -91,13 +102,26 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   const int half = wid >> 2;
   const bool active = half == 0 || p != qt_hi;
   const int qt = half == 0 ? qt_hi : p;
-  const int q_pos = qt * BQ + (wid & 3) * 32 + r32;
-  // the last query this wave owns (-1: nothing to do)
-  const int q_last_wave = active ? qt * BQ + (wid & 3) * 32 + 31 : -1;
+  const int q_pos = qt * BQ + (wid & 3) * 32 + r32;  // packed query index
+  // key positions: the packed rows themselves, or (full KV) every position of the sequence,
+  // a query at original position qpos seeing keys <= qpos
+  const int kvlen = FULLKV ? fkv.T : k;
+  auto pos_of = [&](int q) -> int {  // position of packed query q (< k) among the keys
+    return FULLKV ? fkv.qpos[(int64_t)b * k_fixed + q] : q;
+  };
+  const int q_key = FULLKV ? pos_of(min(q_pos, k - 1)) : q_pos;  // this lane's query position
+  // first and last query positions of this wave (last = -1: nothing to do)
+  const int q_first_wave = FULLKV ? pos_of(min(qt * BQ + (wid & 3) * 32, k - 1))
+                                  : qt * BQ + (wid & 3) * 32;
+  const int q_last_wave = !active ? -1
+                          : FULLKV ? pos_of(min(qt * BQ + (wid & 3) * 32 + 31, k - 1))
+                                   : qt * BQ + (wid & 3) * 32 + 31;
 
-  const int q_hi = min(qt_hi * BQ + BQ, k);
-  const int n_kv = (q_hi + BKV - 1) / BKV;
-  const char *kbase = (const char *)(qkv + row0 * ldq + Hq * HD + gkv * HD);
+  const int key_hi = FULLKV ? pos_of(min(qt_hi * BQ + BQ, k) - 1) + 1 : min(qt_hi * BQ + BQ, k);
+  const int n_kv = (key_hi + BKV - 1) / BKV;
+  const int ldk = FULLKV ? fkv.ldkv : ldq;
+  const char *kbase = FULLKV ? (const char *)(fkv.kv + (int64_t)b * fkv.T * fkv.ldkv + gkv * HD)
+                             : (const char *)(qkv + row0 * ldq + Hq * HD + gkv * HD);
   const char *vbase = kbase + (size_t)Hkv * HD * 2;
 
   // DMA: block i of a stage (i < NBLK/2: K, else V) is filled by wave i % 4; lane l lands at
@@ -112,11 +136,11 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
     const int blk = is_v ? i - C::NBLK / 2 : i;
     dma_row[n] = C::RPB * blk + lane / C::CPR;
     dma_lc[n] = (lane % C::CPR) ^ (is_v ? C::vswz(dma_row[n]) : C::kswz(dma_row[n]));
-    dma_off[n] = (uint32_t)dma_row[n] * (uint32_t)ldq * 2u + (uint32_t)dma_lc[n] * 16u;
+    dma_off[n] = (uint32_t)dma_row[n] * (uint32_t)ldk * 2u + (uint32_t)dma_lc[n] * 16u;
   }
   auto issue_tile = [&](int jt, int stage) {
-    const size_t tile_bytes = (size_t)jt * BKV * ldq * 2;
-    const bool ragged = jt * BKV + BKV > k;  // rows past the sequence read its last row
+    const size_t tile_bytes = (size_t)jt * BKV * ldk * 2;
+    const bool ragged = jt * BKV + BKV > kvlen;  // rows past the sequence read its last row
 #pragma unroll
     for (int n = 0; n < C::NDMA; ++n) {
       const int i = C::NW * n + wv;
@@ -124,8 +148,8 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
       const int blk = is_v ? i - C::NBLK / 2 : i;
       uint32_t off = dma_off[n];
       if (ragged) {
-        const int row = min(dma_row[n], k - 1 - jt * BKV);
-        off = (uint32_t)row * (uint32_t)ldq * 2u + (uint32_t)dma_lc[n] * 16u;
+        const int row = min(dma_row[n], kvlen - 1 - jt * BKV);
+        off = (uint32_t)row * (uint32_t)ldk * 2u + (uint32_t)dma_lc[n] * 16u;
       }
       attn_dma16((is_v ? vbase : kbase) + tile_bytes + off,
                  lds + stage + (is_v ? C::TILE : 0) + C::RPB * blk * HD);
@@ -214,13 +238,13 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
       issue_v(0, 0);
 
       // causal mask only where the tile reaches past the wave's first query or the sequence
-      if (key0 + BKV - 1 > q_last_wave - 31 || key0 + BKV > k) {
+      if (key0 + BKV - 1 > q_first_wave || key0 + BKV > kvlen) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + t * 32 + 8 * (e >> 2) + 4 * gq + (e & 3);
-            if (key > q_pos || key >= k) sacc[t][e] = -INFINITY;
+            if (key > q_key || key >= kvlen) sacc[t][e] = -INFINITY;
           }
       }
       // online softmax in log2 units (statistics shared by lanes l and l^32)
@@ -331,9 +355,10 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   }  // pair loop
 }
 
-hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
-                            int Hq, int Hkv, int hd, const int32_t *seq_off,
-                            const int32_t *seq_len, hipStream_t s) {
+template <bool FULLKV>
+static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
+                        int Hq, int Hkv, int hd, const int32_t *seq_off, const int32_t *seq_len,
+                        const FullKV &fkv, hipStream_t s) {
   const int nqt = (k + 127) / 128;
   // per-sequence lengths (k is then only their bound): a quarter of the pairs of a longest
   // sequence per (head, sequence), each workgroup looping over its share
@@ -341,11 +366,26 @@ hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld
   const dim3 grid((unsigned)(seq_len ? (pairs + 3) / 4 : pairs), (unsigned)Hq, (unsigned)B);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 128)
-    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
-                       scale_log2, seq_off, seq_len);
+    hipLaunchKernelGGL((attn_kernel<128, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
+                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv);
   else
-    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv,
-                       scale_log2, seq_off, seq_len);
+    hipLaunchKernelGGL((attn_kernel<64, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
+                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv);
+}
+
+hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
+                            int Hq, int Hkv, int hd, const int32_t *seq_off,
+                            const int32_t *seq_len, hipStream_t s) {
+  launch_attn<false>(qkv, ld_qkv, o, ld_o, B, k, Hq, Hkv, hd, seq_off, seq_len, FullKV{}, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_fullkv(const uint16_t *q, int ld_q, const uint16_t *kv, int ld_kv,
+                                   const int32_t *qpos, uint16_t *o, int ld_o, int B, int k,
+                                   int T, int Hq, int Hkv, int hd, hipStream_t s) {
+  FullKV f;
+  f.kv = kv; f.ldkv = ld_kv; f.qpos = qpos; f.T = T;
+  launch_attn<true>(q, ld_q, o, ld_o, B, k, Hq, Hkv, hd, nullptr, nullptr, f, s);
   return hipGetLastError();
 }
 

@@ -150,7 +150,7 @@ struct GemmArgs {
   // and workgroups past the actual tiles exit at once.
   // EPI_RESIDUAL: output row m is x row rowmap_x(map, m); the accumulator is f (kept fp32),
   // added as X + varsigma*gate[m]*(a + f), or X + (a + f) if gate == nullptr; a is fp32
-  // [M, N] with leading dimension ldc, as is x.
+  // [M, N] with leading dimension ldc, as is x, or nullptr for a = 0.
   RowMap map;
   uint16_t *x; const float *gate; float varsigma; const float *a;
   int residual_form;  // EPI_RESIDUAL with gate: 0 X + (varsigma*gate)*(a + f); 1 (X + a) + gate*f
@@ -163,5 +163,12 @@ hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s);
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
                             int Hq, int Hkv, int hd, const int32_t *seq_off,
                             const int32_t *seq_len, hipStream_t s);
+
+// Selected-Q/full-KV attention: queries q [B*k, ld_q] (packed, Hq heads), keys and values of
+// every position kv [B*T, ld_kv] ([K heads | V heads]); packed query b*k + j sits at original
+// position qpos[b*k + j] and sees keys at positions <= it.
+hipError_t launch_attention_fullkv(const uint16_t *q, int ld_q, const uint16_t *kv, int ld_kv,
+                                   const int32_t *qpos, uint16_t *o, int ld_o, int B, int k,
+                                   int T, int Hq, int Hkv, int hd, hipStream_t s);
 
 }  // namespace xmod

@@ -342,8 +342,12 @@ gemm_kernel(GemmArgs g) {
         const f32x4 f0 = *(const f32x4 *)lf, f1 = *(const f32x4 *)(lf + 4);
         const int64_t xrow = rowmap_x(g.map, m);
         uint16_t *xp = g.x + xrow * g.ldc + n;
-        const float *ap = g.a + (size_t)m * g.ldc + n;
-        const f32x4 a0 = *(const f32x4 *)ap, a1 = *(const f32x4 *)(ap + 4);
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};  // no a: a = 0
+        if (g.a) {
+          const float *ap = g.a + (size_t)m * g.ldc + n;
+          a0 = *(const f32x4 *)ap;
+          a1 = *(const f32x4 *)(ap + 4);
+        }
         const u32x4 xv = *(const u32x4 *)xp;
         const bool mod = g.gate && g.residual_form == 1;
         const float gg = g.gate ? (mod ? g.gate[m] : __fmul_rn(g.varsigma, g.gate[m])) : 0.f;

@@ -244,6 +244,62 @@ int block_sparse_per_block(float A, int32_t K, bool *ok) {
 
 extern "C" {
 
+// ---- mechanism controls of Table 7 ----------------------------------------------------------
+
+namespace {
+
+struct PlanMech {
+  size_t logits = 0, idx = 0, gate = 0, u = 0, u2 = 0, qkv = 0, kv = 0, o = 0, a = 0, g = 0;
+  size_t total = 0;
+};
+
+// kind 0: routed FFN refinement (M = B*k routed rows); 1: full-sequence attention block;
+// 2: Selected-Q/full-KV layer (M routed rows, keys / values of all B*T rows).
+PlanMech plan_mech(const xmod_dims *dm, int64_t M, int kind) {
+  PlanMech p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  const int64_t BT = (int64_t)dm->B * dm->T;
+  const int64_t dq = (int64_t)dm->n_q_heads * dm->head_dim;
+  const int64_t dkv = (int64_t)dm->n_kv_heads * dm->head_dim;
+  if (kind != 1) {
+    p.logits = take((size_t)BT * 4);
+    p.idx = take((size_t)M * 4);
+    p.gate = take((size_t)M * 4);
+  }
+  if (kind == 0) {
+    p.u = take((size_t)M * dm->d * 2);
+    p.g = take((size_t)M * dm->ffn_hidden * 2);
+  } else if (kind == 1) {
+    p.u = take((size_t)BT * dm->d * 2);
+    p.qkv = take((size_t)BT * (dq + 2 * dkv) * 2);
+    p.o = take((size_t)BT * dq * 2);
+  } else {
+    p.u = take((size_t)BT * dm->d * 2);       // RMSNorm of every row
+    p.kv = take((size_t)BT * 2 * dkv * 2);    // keys and values of every row
+    p.u2 = take((size_t)M * dm->d * 2);       // selected rows of u, later v
+    p.qkv = take((size_t)M * dq * 2);         // queries of the selected rows
+    p.o = take((size_t)M * dq * 2);
+    p.a = take((size_t)M * dm->d * 4);
+    p.g = take((size_t)M * dm->ffn_hidden * 2);
+  }
+  p.total = off;
+  return p;
+}
+
+xmod_status route_topk_into(const void *x, const xmod_layer *L, const xmod_dims *dm, int k,
+                            float *bias, float tau, float delta, float *logits, int32_t *idx,
+                            float *gate, hipStream_t s) {
+  XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)L->w_router, L->router_bias, bias,
+                         tau, logits, (int64_t)dm->B * dm->T, dm->d, s));
+  phase_mark(s);
+  XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s));
+  phase_mark(s);
+  return XMOD_OK;
+}
+
+}  // namespace
+
 size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_point) {
   if (check_dims(dims) != XMOD_OK) return 0;
   switch (entry_point) {
@@ -254,6 +310,13 @@ size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_poin
     case XMOD_WS_DENSE_LAYER: return plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
     case XMOD_WS_SPARSE_THRESHOLD:
       return plan_layer(dims, (int64_t)dims->B * dims->T, true, true).total;
+    case XMOD_WS_ROUTED_FFN:
+      if (K < 1 || dims->T / K < 1) return 0;
+      return plan_mech(dims, (int64_t)dims->B * (dims->T / K), 0).total;
+    case XMOD_WS_ATTN_LAYER: return plan_mech(dims, (int64_t)dims->B * dims->T, 1).total;
+    case XMOD_WS_SPARSE_FULLKV:
+      if (K < 1 || dims->T / K < 1) return 0;
+      return plan_mech(dims, (int64_t)dims->B * (dims->T / K), 2).total;
     case XMOD_WS_BLOCK: {
       const size_t dn = plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
       if (K < 1 || dims->T / K < 1) return dn;
@@ -496,5 +559,171 @@ xmod_status xmod_mask_agreement(const float *logits, const int32_t *idx, int32_t
   if (!logits || !idx || !agree || B < 1 || T < 1 || k < 1 || k > T) return XMOD_ERR_INVALID_ARG;
   if (T > 65536) return XMOD_ERR_UNSUPPORTED;
   XMOD_HIP(launch_mask_agreement(logits, idx, B, T, k, agree, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+
+xmod_status xmod_routed_ffn_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                int32_t K, float *bias, float tau, float delta,
+                                int32_t *idx_out, float *gate_out, void *ws, size_t ws_bytes,
+                                void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer || !layer->w_router || !layer->g_ffn || !layer->w_gate || !layer->w_up ||
+      !layer->w_down || K < 1 || dims->T / K < 1)
+    return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta) || !isfinite(layer->router_bias) ||
+      !isfinite(layer->varsigma))
+    return XMOD_ERR_INVALID_ARG;
+  const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_ROUTED_FFN);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int k = dims->T / K;
+  const int64_t M = (int64_t)dims->B * k;
+  const PlanMech p = plan_mech(dims, M, 0);
+  int32_t *idx = idx_out ? idx_out : at<int32_t>(ws, p.idx);
+  float *gate = gate_out ? gate_out : at<float>(ws, p.gate);
+  uint16_t *u = at<uint16_t>(ws, p.u), *gbuf = at<uint16_t>(ws, p.g);
+  phase_begin(s, 0);
+  const xmod_status r = route_topk_into(x, layer, dims, k, bias, tau, delta, at<float>(ws, p.logits),
+                                        idx, gate, s);
+  if (r != XMOD_OK) return r;
+  const RowMap map = topk_map(idx, dims, k);
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, (const uint16_t *)layer->g_ffn,
+                              dims->rms_eps, true, M, dims->d, u, s));
+  phase_mark(s);
+  GemmArgs g{};
+  g.map = map;
+  g.A = u; g.lda = dims->d; g.B = (const uint16_t *)layer->w_gate;
+  g.B2 = (const uint16_t *)layer->w_up; g.ldb = dims->d; g.C = gbuf; g.ldc = dims->ffn_hidden;
+  g.M = (int)M; g.N = dims->ffn_hidden; g.K = dims->d;
+  XMOD_HIP(launch_gemm(g, EPI_SWIGLU, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.map = map;
+  g.A = gbuf; g.lda = dims->ffn_hidden; g.B = (const uint16_t *)layer->w_down;
+  g.ldb = dims->ffn_hidden; g.ldc = dims->d; g.M = (int)M; g.N = dims->d; g.K = dims->ffn_hidden;
+  g.x = (uint16_t *)x; g.gate = gate; g.varsigma = layer->varsigma; g.a = nullptr;
+  XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
+  phase_mark(s);
+  return XMOD_OK;
+}
+
+xmod_status xmod_attention_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                     void *ws, size_t ws_bytes, void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer || !layer->g_attn || !layer->w_qkv || !layer->w_o) return XMOD_ERR_INVALID_ARG;
+  if (!(layer->rope_theta >= 0.f) || !isfinite(layer->rope_theta)) return XMOD_ERR_INVALID_ARG;
+  const size_t need = xmod_workspace_bytes(dims, 1, XMOD_WS_ATTN_LAYER);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t M = (int64_t)dims->B * dims->T;
+  const PlanMech p = plan_mech(dims, M, 1);
+  const int d = dims->d, dq = dims->n_q_heads * dims->head_dim;
+  const int nqkv = dq + 2 * dims->n_kv_heads * dims->head_dim;
+  uint16_t *u = at<uint16_t>(ws, p.u), *qkv = at<uint16_t>(ws, p.qkv), *o = at<uint16_t>(ws, p.o);
+  RowMap map;
+  map.T = dims->T; map.x_rows = M;
+  phase_begin(s, 2);
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, (const uint16_t *)layer->g_attn,
+                              dims->rms_eps, true, M, d, u, s));
+  phase_mark(s);
+  GemmArgs g{};
+  g.map = map;
+  g.A = u; g.lda = d; g.B = (const uint16_t *)layer->w_qkv; g.ldb = d; g.C = qkv; g.ldc = nqkv;
+  g.M = (int)M; g.N = nqkv; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, s));
+  phase_mark(s);
+  XMOD_HIP(launch_qk_form(qkv, nqkv, map, M, dims->n_q_heads, dims->n_kv_heads, dims->head_dim,
+                          (const uint16_t *)layer->q_norm, (const uint16_t *)layer->k_norm,
+                          dims->rms_eps, layer->rope_theta, s));
+  XMOD_HIP(launch_attention(qkv, nqkv, o, dq, dims->B, dims->T, dims->n_q_heads,
+                            dims->n_kv_heads, dims->head_dim, nullptr, nullptr, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.map = map;
+  g.A = o; g.lda = dq; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.ldc = d;
+  g.M = (int)M; g.N = d; g.K = dq;
+  g.x = (uint16_t *)x; g.gate = nullptr; g.a = nullptr;  // y = x + O W_o^T
+  XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
+  phase_mark(s);
+  return XMOD_OK;
+}
+
+xmod_status xmod_sparse_layer_fwd_fullkv(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                         int32_t K, float *bias, float tau, float delta,
+                                         int32_t *idx_out, float *gate_out, void *ws,
+                                         size_t ws_bytes, void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_FULLKV);
+  if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int B = dims->B, T = dims->T, d = dims->d, k = T / K;
+  const int64_t M = (int64_t)B * k, BT = (int64_t)B * T;
+  const int Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, hd = dims->head_dim;
+  const int dq = Hq * hd, dkv = Hkv * hd;
+  const PlanMech p = plan_mech(dims, M, 2);
+  int32_t *idx = idx_out ? idx_out : at<int32_t>(ws, p.idx);
+  float *gate = gate_out ? gate_out : at<float>(ws, p.gate);
+  uint16_t *u = at<uint16_t>(ws, p.u), *kv = at<uint16_t>(ws, p.kv), *u2 = at<uint16_t>(ws, p.u2);
+  uint16_t *q = at<uint16_t>(ws, p.qkv), *o = at<uint16_t>(ws, p.o), *gbuf = at<uint16_t>(ws, p.g);
+  float *a = at<float>(ws, p.a);
+  phase_begin(s, 0);
+  const xmod_status r = route_topk_into(x, layer, dims, k, bias, tau, delta,
+                                        at<float>(ws, p.logits), idx, gate, s);
+  if (r != XMOD_OK) return r;
+  RowMap all;
+  all.T = T; all.x_rows = BT;
+  const RowMap map = topk_map(idx, dims, k);
+  // RMSNorm of every row; keys and values of every row; queries of the selected rows
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, all, (const uint16_t *)layer->g_attn,
+                              dims->rms_eps, true, BT, d, u, s));
+  XMOD_HIP(launch_gather_rows(u, map, nullptr, 0.f, false, M, d, u2, s));
+  phase_mark(s);
+  GemmArgs g{};
+  g.map = all;
+  g.A = u; g.lda = d; g.B = (const uint16_t *)layer->w_qkv + (size_t)dq * d; g.ldb = d;
+  g.C = kv; g.ldc = 2 * dkv; g.M = (int)BT; g.N = 2 * dkv; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, s));
+  g = GemmArgs{};
+  g.map = map;
+  g.A = u2; g.lda = d; g.B = (const uint16_t *)layer->w_qkv; g.ldb = d; g.C = q; g.ldc = dq;
+  g.M = (int)M; g.N = dq; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, s));
+  phase_mark(s);
+  // optional QK-norm / rotary embedding: queries at their original positions, keys at theirs
+  XMOD_HIP(launch_qk_form(q, dq, map, M, Hq, 0, hd, (const uint16_t *)layer->q_norm, nullptr,
+                          dims->rms_eps, layer->rope_theta, s));
+  XMOD_HIP(launch_qk_form(kv, 2 * dkv, all, BT, 0, Hkv, hd, nullptr,
+                          (const uint16_t *)layer->k_norm, dims->rms_eps, layer->rope_theta, s));
+  XMOD_HIP(launch_attention_fullkv(q, dq, kv, 2 * dkv, idx, o, dq, B, k, T, Hq, Hkv, hd, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.map = map;
+  g.A = o; g.lda = dq; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.Cf = a; g.ldc = d;
+  g.M = (int)M; g.N = d; g.K = dq;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, s));
+  phase_mark(s);
+  XMOD_HIP(launch_residual_rmsnorm((const uint16_t *)x, map, a, (const uint16_t *)layer->g_ffn,
+                                   dims->rms_eps, M, d, u2, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.map = map;
+  g.A = u2; g.lda = d; g.B = (const uint16_t *)layer->w_gate; g.B2 = (const uint16_t *)layer->w_up;
+  g.ldb = d; g.C = gbuf; g.ldc = dims->ffn_hidden; g.M = (int)M; g.N = dims->ffn_hidden; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_SWIGLU, s));
+  phase_mark(s);
+  g = GemmArgs{};
+  g.map = map;
+  g.A = gbuf; g.lda = dims->ffn_hidden; g.B = (const uint16_t *)layer->w_down;
+  g.ldb = dims->ffn_hidden; g.ldc = d; g.M = (int)M; g.N = d; g.K = dims->ffn_hidden;
+  g.x = (uint16_t *)x; g.gate = gate; g.varsigma = layer->varsigma; g.a = a;
+  g.residual_form = layer->residual;
+  XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
+  phase_mark(s);
   return XMOD_OK;
 }

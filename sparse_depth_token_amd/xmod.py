@@ -18,11 +18,13 @@ lib = ctypes.CDLL(_LIB_PATH)
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK, WS_SPARSE_THRESHOLD = 0, 1, 2, 3, 4
+WS_ROUTED_FFN, WS_ATTN_LAYER, WS_SPARSE_FULLKV = 5, 6, 7
 
 # Every symbol include/xmod.h declares, in declaration order.
 EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", "xmod_pack",
             "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_threshold_select",
-            "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_dense_layer_fwd",
+            "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_routed_ffn_fwd",
+            "xmod_attention_layer_fwd", "xmod_sparse_layer_fwd_fullkv", "xmod_dense_layer_fwd",
             "xmod_block_fwd",
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_attention_fwd",
             "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
@@ -60,6 +62,11 @@ _sig = {
     "xmod_sparse_layer_fwd_threshold": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _f32, _f32, _vp,
                                                _vp, _vp, _vp, _sz, _vp]),
     "xmod_mask_agreement": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "xmod_routed_ffn_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp, _vp,
+                                   _vp, _sz, _vp]),
+    "xmod_attention_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _sz, _vp]),
+    "xmod_sparse_layer_fwd_fullkv": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp,
+                                            _vp, _vp, _sz, _vp]),
     "xmod_dense_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _sz, _vp]),
     "xmod_block_fwd": (_i32, [_vp, _P(Layer), _i32, _P(Dims), _i32, _i32, _f32, _i32, _vp, _f32,
                               _f32, _vp, _sz, _vp]),
@@ -106,12 +113,16 @@ def make_dims(B, T, d, n_q_heads, n_kv_heads, head_dim, ffn_hidden, rms_eps=1e-6
 def make_layer(w: dict) -> Layer:
     """w: dict of device tensors (bf16) w_router, g_attn, w_qkv, w_o, g_ffn, w_gate, w_up,
     w_down, optional q_norm / k_norm, and host values router_bias, varsigma, optional residual
-    (0 or 1) and rope_theta."""
-    return Layer(_ptr(w.get("w_router")), float(w.get("router_bias", 0.0)),
-                 float(w.get("varsigma", 1.0)), _ptr(w["g_attn"]), _ptr(w["w_qkv"]),
-                 _ptr(w["w_o"]), _ptr(w["g_ffn"]), _ptr(w["w_gate"]), _ptr(w["w_up"]),
-                 _ptr(w["w_down"]), int(w.get("residual", 0)), _ptr(w.get("q_norm")),
-                 _ptr(w.get("k_norm")), float(w.get("rope_theta", 0.0) or 0.0))
+    (0 or 1) and rope_theta. The returned struct holds raw device pointers; it keeps a
+    reference to the tensors so that they outlive it (a caller passing a temporary dict would
+    otherwise hand the library freed memory that the allocator gives to the next tensor)."""
+    L = Layer(_ptr(w.get("w_router")), float(w.get("router_bias", 0.0)),
+              float(w.get("varsigma", 1.0)), _ptr(w["g_attn"]), _ptr(w["w_qkv"]),
+              _ptr(w["w_o"]), _ptr(w["g_ffn"]), _ptr(w["w_gate"]), _ptr(w["w_up"]),
+              _ptr(w["w_down"]), int(w.get("residual", 0)), _ptr(w.get("q_norm")),
+              _ptr(w.get("k_norm")), float(w.get("rope_theta", 0.0) or 0.0))
+    L._tensors = dict(w)
+    return L
 
 
 def workspace_bytes(dims: Dims, K: int, entry: int) -> int:
@@ -177,6 +188,27 @@ def mask_agreement(logits, idx, agree, stream=None):
     B, T = logits.shape
     _check(lib.xmod_mask_agreement(_ptr(logits), _ptr(idx), B, T, idx.shape[1], _ptr(agree),
                                    _stream(stream)), "xmod_mask_agreement")
+
+
+def routed_ffn_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_out=None,
+                   gate_out=None, stream=None):
+    _check(lib.xmod_routed_ffn_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
+                                   _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "xmod_routed_ffn_fwd")
+
+
+def attention_layer_fwd(x, layer: Layer, dims: Dims, ws, stream=None):
+    _check(lib.xmod_attention_layer_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims),
+                                        _ptr(ws), ws.numel(), _stream(stream)),
+           "xmod_attention_layer_fwd")
+
+
+def sparse_layer_fwd_fullkv(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_out=None,
+                            gate_out=None, stream=None):
+    _check(lib.xmod_sparse_layer_fwd_fullkv(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
+                                            _ptr(bias), tau, delta, _ptr(idx_out),
+                                            _ptr(gate_out), _ptr(ws), ws.numel(),
+                                            _stream(stream)), "xmod_sparse_layer_fwd_fullkv")
 
 
 def dense_layer_fwd(x, layer: Layer, dims: Dims, ws, stream=None):
