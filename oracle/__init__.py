@@ -24,4 +24,6 @@ from .stack import (stack_layer_kinds, physical_layers, active_equivalent_layers
                     active_params, layer_params, flops_per_token_pages_convention, block_forward,
                     coverage, adjacent_jaccard, coverage_independent_reference,
                     jaccard_independent_reference)
+from .backward import (rmsnorm_grad, causal_attention_grad, silu_grad, route_bce,
+                       route_bce_grad, sparse_layer_grad)
 from .numerics import bf16_to_f64, round_to_bf16, f64_to_bf16_bits

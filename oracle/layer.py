@@ -48,18 +48,24 @@ def _f64(a):
 
 # --- router: [MOD] "basic architecture" (Linear(d, 1) score), [XMOD] Eq. (8) -------------------
 
-def router_logits(x, w_router, router_bias=0.0, bias=None, tau=1.0):
+def router_logits(x, w_router, router_bias=0.0, bias=None, tau=1.0, exact=False):
     """Router logit s_t = w_r . x_t + beta_r and bias-adjusted logit ell_t = s_t - tau * b_t.
 
     The dot product is taken in float64 and rounded once to fp32 ("the oracle's logit"). The
     adjustment is fp32 arithmetic: tau*b rounded, then the subtraction rounded ([XMOD] Eq. (8)
     subtracts tau*b_i before the top-1/K choice). Returns (s, ell), both float32 [B, T].
+
+    exact=True keeps both in float64 with no rounding (a smooth function of the inputs, for
+    derivative checks by finite differences); the selection is still ranked on fp32 values.
     """
     x = _f64(x)
     w = _f64(w_router)
-    s = (x @ w + float(router_bias)).astype(np.float32)
     if bias is None:
-        bias = np.zeros(s.shape, dtype=np.float32)
+        bias = np.zeros(x.shape[:2], dtype=np.float32)
+    if exact:
+        s = x @ w + float(router_bias)
+        return s, s - float(tau) * np.asarray(bias, dtype=np.float64)
+    s = (x @ w + float(router_bias)).astype(np.float32)
     tb = np.float32(tau) * np.asarray(bias, dtype=np.float32)
     ell = (s - tb).astype(np.float32)
     return s, ell
@@ -252,7 +258,8 @@ def _routed_layer(x, lay, dims, ell, sel, bias, delta, sample):
     return res
 
 
-def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None, sample=None):
+def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None, sample=None,
+                 exact_logits=False):
     """Forward of one X-MoD Sparse(K) layer with the training-time top-k selection.
 
     x: [B, T, d] bf16 bits or float64 values. lay: dict of layer weights (bf16 bits) plus
@@ -265,6 +272,7 @@ def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None
 
     sample: None for the whole output, or {b: packed rows} to evaluate only those rows of those
     sequences (each output row is computed exactly as in the full evaluation).
+    exact_logits: float64 logits with no fp32 rounding (router_logits(exact=True)).
 
     Returns a dict with s, ell (fp32), idx (int64 [B, k]), gate (float64 [B, k]), bias_out
     (fp32), and either y (float64 [B, T, d]) or rows {b: (packed rows, positions, y rows)}.
@@ -276,7 +284,8 @@ def sparse_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None
     if bias is None:
         bias = np.zeros((B, T), dtype=np.float32)
     bias = np.asarray(bias, dtype=np.float32)
-    s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
+    s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau,
+                           exact=exact_logits)
     idx = topk_select(ell, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
     res = _routed_layer(x, lay, dims, ell, [idx[b] for b in range(B)], bias, delta, sample)
     res.update({"s": s, "ell": ell, "idx": idx, "gate": np.stack(res["gate"])})
