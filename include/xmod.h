@@ -252,6 +252,21 @@ xmod_status xmod_rmsnorm_rows(const void *x, const int32_t *idx, const void *gai
 xmod_status xmod_gemm_bf16_nt(const void *A, int32_t lda, const void *Bm, int32_t ldb, void *C,
                               int32_t ldc, int32_t M, int32_t N, int32_t K, void *stream);
 
+/* The products of the layer's backward pass (and the forward's, layout NT):
+ * C[M, N] = sum_k A(m, k) B(n, k) with fp32 accumulation, where
+ *   XMOD_GEMM_NT: A is [M, K] (lda >= K) and B is [N, K] (ldb >= K)     - x W^T (forward);
+ *   XMOD_GEMM_NN: A is [M, K] (lda >= K) and B is [K, N] (ldb >= N)     - dY W (input gradient);
+ *   XMOD_GEMM_TN: A is [K, M] (lda >= M) and B is [K, N] (ldb >= N)     - dY^T X (weight
+ *                 gradient, a sum over the K token rows).
+ * All row-major bf16, leading dimensions in elements, 16-byte aligned pointers. C is bf16
+ * (round to nearest even, out_f32 = 0) or fp32 (out_f32 = 1); TN needs out_f32 = 1.
+ * UNSUPPORTED: K not a multiple of 64, N or a leading dimension not a multiple of 8, M of a
+ * k-major A not a multiple of 8, or an operand of 2^31 elements or more. */
+enum { XMOD_GEMM_NT = 0, XMOD_GEMM_NN = 1, XMOD_GEMM_TN = 2 };
+xmod_status xmod_gemm_bf16(int32_t layout, const void *A, int32_t lda, const void *Bm, int32_t ldb,
+                           void *C, int32_t ldc, int32_t out_f32, int32_t M, int32_t N,
+                           int32_t K, void *stream);
+
 /* Causal attention over packed sequences ([XMOD] Table 7 "selected subset"; [MODA] 2.1 GQA):
  * qkv [B*k, ld_qkv] bf16 holds Q (Hq*hd columns), then K and V (Hkv*hd each) per row;
  * o [B*k, ld_o] bf16 out (Hq*hd columns). Row j of a sequence attends to rows 0..j. */

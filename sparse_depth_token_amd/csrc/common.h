@@ -137,7 +137,15 @@ hipError_t launch_qk_form(uint16_t *qkv, int ld_qkv, const RowMap &map, int64_t 
                           int Hkv, int hd, const uint16_t *q_norm, const uint16_t *k_norm,
                           float eps, float theta, hipStream_t s);
 
-enum GemmEpilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2, EPI_STORE_F32 = 3 };
+enum GemmEpilogue {
+  EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2, EPI_STORE_F32 = 3,
+  EPI_SWIGLU_SAVE = 4,  // EPI_SWIGLU that also stores the pre-activations [zg | zu] to Z
+  EPI_SWIGLU_BWD = 5    // accumulator dg; reads Z = [zg | zu], writes C = [dzg | dzu]
+};
+
+// Operand layouts: A is [M, K] (k-contiguous rows) or, k-major, [K, M]; B is [N, K] or,
+// k-major, [K, N]. NT: both k-contiguous; NN: B k-major; TN: both k-major.
+enum GemmLayout { LAY_NT = 0, LAY_NN = 1, LAY_TN = 2 };
 
 struct GemmArgs {
   const uint16_t *A;  int lda;     // [M, K] activations
@@ -154,9 +162,19 @@ struct GemmArgs {
   RowMap map;
   uint16_t *x; const float *gate; float varsigma; const float *a;
   int residual_form;  // EPI_RESIDUAL with gate: 0 X + (varsigma*gate)*(a + f); 1 (X + a) + gate*f
+  float *fsave;       // EPI_RESIDUAL: when set, f is also stored (fp32 [M, N], ldc)
+  // k-major B (LAY_NN): k-rows >= K1 (when K1 > 0) are rows k - K1 of B2 (same ldb).
+  int K1;
+  // EPI_STORE_F32: output rows m >= M1 (when M1 > 0) go to row m - M1 of Cf2 (same ldc).
+  float *Cf2; int M1;
+  // EPI_SWIGLU_SAVE / EPI_SWIGLU_BWD: pre-activations, zg in columns [0, N), zu in [N, 2N).
+  uint16_t *Z; int ldz;
 };
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s);
+// Layout-aware form: k-major operands need their M / N a multiple of 8 (at least 8) and K a
+// multiple of 64; LAY_NN supports EPI_STORE, EPI_STORE_F32, EPI_SWIGLU_BWD; LAY_TN EPI_STORE_F32.
+hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, GemmLayout lay, hipStream_t s);
 
 // Causal attention over packed sequences: fixed length k (seq_len == nullptr, sequence b at
 // rows b*k) or per-sequence lengths and first rows (seq_len[b], seq_off[b], each <= max_len).

@@ -1,9 +1,17 @@
-// bf16 "NT" GEMM on CDNA4 matrix cores: C[M,N] = A[M,K] * B[N,K]^T, fp32 accumulation.
+// bf16 GEMM on CDNA4 matrix cores: C[M,N] = sum_k A(m, k) B(n, k), fp32 accumulation.
 //
 // Used for the four projections of the X-MoD layer on the packed selected rows: QKV, O
 // (fp32 output), gate/up (SwiGLU fused into the epilogue) and down (gated residual + scatter
-// into x fused into the epilogue). Both operands are K-contiguous rows, the natural operand
-// layout of v_mfma_f32_32x32x16_bf16: every lane reads 8 consecutive bf16 (16 bytes) of a row.
+// into x fused into the epilogue), and for their gradients. In the forward ("NT") both operands
+// are K-contiguous rows, the natural operand layout of v_mfma_f32_32x32x16_bf16: every lane
+// reads 8 consecutive bf16 (16 bytes) of a row. The backward multiplies by a weight read along
+// its output dimension ("NN": B stored [K, N]) and forms weight gradients as sums over tokens
+// ("TN": A stored [K, M], B stored [K, N]). A k-major operand is staged in LDS as it lies in
+// memory (k-rows of the tile's M or N extent) and its fragments are read with the transposing
+// LDS read ds_read_b64_tr_b16: within each 16-lane group, lane 4a+b receives element b of the
+// 8-byte reads of lanes 4e+a (e = 0..3), so four lanes reading 4 consecutive k-rows at 4
+// consecutive columns give each lane 4 consecutive k of one column; two such reads make the
+// 8-k fragment the MFMA expects, in the same k order as a k-contiguous fragment.
 //
 // Design (gfx950, wave64):
 //  * Workgroup tile BM x BN x BK, four or eight waves in a grid, each computing a WM x WN
@@ -46,20 +54,31 @@ __device__ __forceinline__ int swz(int r) {
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
+// Physical 16-byte chunk of logical chunk c in k-row r of a k-major tile (rows of at least 16
+// chunks): c ^ 4(r % 4). A transposing read by 32 lanes covers 4 consecutive k-rows and 4
+// consecutive chunks; the XOR spreads those 16 (row, chunk) pairs over all 64 banks.
+__device__ __forceinline__ int swz_km(int r) { return 4 * (r & 3); }
+
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY>
 struct GemmCfg {
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
   static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr bool A_KM = LAY == LAY_TN, B_KM = LAY != LAY_NT;  // k-major operands
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;            // elements per LDS stage
   static constexpr int NSTAGE = NS;                          // LDS ring depth
   static constexpr int CPR = BK / 8;                         // 16-byte chunks per LDS row
   static constexpr int RPB = 64 / CPR;                       // rows per 1 KB DMA block
-  static constexpr int NA = BM / RPB / NW, NB = BN / RPB / NW;  // DMA blocks per wave per tile
-  static constexpr int BN_OUT = EPI == EPI_SWIGLU ? BN / 2 : BN;
-  static constexpr bool F32_TILE = EPI == EPI_STORE_F32 || EPI == EPI_RESIDUAL;
+  // DMA blocks per wave per tile (1 KB each, whatever the layout)
+  static constexpr int NA = BM * BK / 512 / NW, NB = BN * BK / 512 / NW;
+  static constexpr bool SWIGLU_FWD = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
+  static constexpr int BN_OUT = SWIGLU_FWD ? BN / 2 : BN;
+  static constexpr bool F32_TILE =
+      EPI == EPI_STORE_F32 || EPI == EPI_RESIDUAL || EPI == EPI_SWIGLU_BWD;
   static constexpr int ESZ = F32_TILE ? 4 : 2;
-  static constexpr int CS = F32_TILE ? BN_OUT + 4 : BN_OUT + 8;  // C-tile row stride (elems)
+  // C-tile row stride (elements); EPI_SWIGLU_SAVE holds g, zg and zu side by side
+  static constexpr int CS = F32_TILE ? BN_OUT + 4
+                            : EPI == EPI_SWIGLU_SAVE ? 3 * BN_OUT + 8 : BN_OUT + 8;
   static constexpr int LDS_MAIN = NSTAGE * STAGE * 2;
   // C-tile rows per epilogue pass: BM / 2^j, the largest that fits in the ring's LDS
   static constexpr int RCH_FIT = LDS_MAIN / (CS * ESZ);
@@ -71,17 +90,20 @@ struct GemmCfg {
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
   static_assert(NS >= 2, "at least one k-tile in flight");
-  static_assert(NA >= 1 && NB >= 1 && BM % (NW * RPB) == 0 && BN % (NW * RPB) == 0, "DMA blocks");
-  static_assert(EPI != EPI_SWIGLU || WN % 64 == 0, "SwiGLU pairs gate/up 32-column blocks");
+  static_assert(NA >= 1 && NB >= 1 && BM * BK % (512 * NW) == 0 && BN * BK % (512 * NW) == 0,
+                "DMA blocks");
+  static_assert(!SWIGLU_FWD || WN % 64 == 0, "SwiGLU pairs gate/up 32-column blocks");
+  static_assert(!SWIGLU_FWD || LAY == LAY_NT, "the forward SwiGLU interleaves k-contiguous B rows");
+  static_assert((!A_KM || BM >= 128) && (!B_KM || BN >= 128), "k-major rows of >= 16 chunks");
   static_assert(RCH >= 32 && BM % RCH == 0 && WM % 32 == 0, "epilogue row chunks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
-__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI>::NT),
-                             (GemmCfg<BM, BN, WM, WN, BK, NS, EPI>::WAVES_PER_EU)) void
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY>
+__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>::NT),
+                             (GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>::WAVES_PER_EU)) void
 gemm_kernel(GemmArgs g) {
-  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -124,40 +146,69 @@ gemm_kernel(GemmArgs g) {
   const int nk = K / BK;
   const int nk_last = nk - 1;
   const int wv = __builtin_amdgcn_readfirstlane(wid);
+  // A k-major operand's block b holds k-rows (512/R) b .. of the tile's R columns; lane l lands
+  // at k-row (512/R) b + l / (R/8), physical chunk l % (R/8), so it fetches logical chunk
+  // (l % (R/8)) ^ swz_km(k-row) (columns past the matrix are clamped: only stores are masked).
   uint32_t a_off[C::NA], b_off[C::NB];
 #pragma unroll
   for (int i = 0; i < C::NA; ++i) {
-    const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
-    const int gm = min(m0 + row, M - 1);
-    a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+    if (C::A_KM) {
+      constexpr int CPT = BM / 8, RPT = 64 / CPT;
+      const int krow = RPT * (C::NW * i + wv) + lane / CPT;
+      const int gm = min(m0 + (((lane % CPT) ^ swz_km(krow)) << 3), M - 8);
+      a_off[i] = ((uint32_t)krow * (uint32_t)g.lda + (uint32_t)gm) * 2u;
+    } else {
+      const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
+      const int gm = min(m0 + row, M - 1);
+      a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+    }
   }
 #pragma unroll
   for (int i = 0; i < C::NB; ++i) {
-    const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
-    // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
-    int gn = EPI == EPI_SWIGLU ? n0 + (row >> 6) * 32 + (row & 31) : n0 + row;
-    gn = min(gn, g.N - 1);
-    b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+    if (C::B_KM) {
+      constexpr int CPT = BN / 8, RPT = 64 / CPT;
+      const int krow = RPT * (C::NW * i + wv) + lane / CPT;
+      const int gn = min(n0 + (((lane % CPT) ^ swz_km(krow)) << 3), g.N - 8);
+      b_off[i] = ((uint32_t)krow * (uint32_t)g.ldb + (uint32_t)gn) * 2u;
+    } else {
+      const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
+      // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
+      int gn = C::SWIGLU_FWD ? n0 + (row >> 6) * 32 + (row & 31) : n0 + row;
+      gn = min(gn, g.N - 1);
+      b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+    }
   }
   const char *a_bytes = (const char *)g.A;
-  const char *b_bytes[2] = {(const char *)g.B, (const char *)(EPI == EPI_SWIGLU ? g.B2 : g.B)};
+  const char *b_bytes[2] = {(const char *)g.B, (const char *)(C::SWIGLU_FWD ? g.B2 : g.B)};
   auto b_half = [&](int i) {  // which weight matrix DMA block i of B reads (SwiGLU: gate / up)
-    return EPI == EPI_SWIGLU ? (((C::RPB * (C::NW * i + wv)) >> 5) & 1) : 0;  // wave-uniform
+    return C::SWIGLU_FWD ? (((C::RPB * (C::NW * i + wv)) >> 5) & 1) : 0;  // wave-uniform
   };
-  // Copy k-tile kt (clamped to the last one) into the stage at element offset `stage`.
   // Copies [lo, hi) of the tile's NA + NB DMA blocks (A blocks first) of k-tile kt, clamped to
-  // the last one, into the stage at element offset `stage`.
+  // the last one, into the stage at element offset `stage`. A k-tile of a k-major operand
+  // starts BK rows further down; a k-major B switches to B2 at k-row K1 (tile-aligned).
   auto issue_part = [&](int kt, int stage, int lo, int hi) {
-    const uint32_t kb = (uint32_t)min(kt, nk_last) * (BK * 2);
+    const int ktc = min(kt, nk_last);
+    const uint32_t kb = (uint32_t)ktc * (BK * 2);
+    const uint32_t kb_a = C::A_KM ? (uint32_t)ktc * BK * (uint32_t)g.lda * 2u : kb;
+    const char *b_km = (const char *)g.B;
+    uint32_t kb_b = kb;
+    if (C::B_KM) {
+      int kr = ktc * BK;
+      if (g.K1 > 0 && kr >= g.K1) {
+        b_km = (const char *)g.B2;
+        kr -= g.K1;
+      }
+      kb_b = (uint32_t)kr * (uint32_t)g.ldb * 2u;
+    }
 #pragma unroll
     for (int i = 0; i < C::NA; ++i)
       if (i >= lo && i < hi)
-        dma16(a_bytes + (a_off[i] + kb), lds + stage + C::RPB * (C::NW * i + wv) * BK);
+        dma16(a_bytes + (a_off[i] + kb_a), lds + stage + 512 * (C::NW * i + wv));
 #pragma unroll
     for (int i = 0; i < C::NB; ++i)
       if (C::NA + i >= lo && C::NA + i < hi)
-        dma16(b_bytes[b_half(i)] + (b_off[i] + kb),
-              lds + stage + C::A_ELEMS + C::RPB * (C::NW * i + wv) * BK);
+        dma16((C::B_KM ? b_km : b_bytes[b_half(i)]) + (b_off[i] + kb_b),
+              lds + stage + C::A_ELEMS + 512 * (C::NW * i + wv));
   };
   auto issue_tile = [&](int kt, int stage) { issue_part(kt, stage, 0, C::NA + C::NB); };
 
@@ -169,6 +220,28 @@ gemm_kernel(GemmArgs g) {
   const int a_base = (wm0 + r32) * BK;
   const int b_base = C::A_ELEMS + (wn0 + r32) * BK;
   const int sw_lane = swz<BK>(r32);
+  // k-major fragments: as the source of a transposing read, lane l addresses k-row
+  // 16 ks + 8 (g >> 1) + e (+ 4 for the second read) and column 32 i + 16 (g & 1) + 4 a of the
+  // wave's rows, g = l / 16, e = l / 4 % 4, a = l % 4; it receives column 32 i + l % 32 and
+  // k 16 ks + 8 (l / 32) + 0..3 (4..7), the k-contiguous fragment's order. Byte offsets within
+  // a stage; the k-row's swizzle depends on e only, so (ks, second read) go in the immediate.
+  const int g16 = lane >> 4, e4 = (lane >> 2) & 3, a4 = lane & 3;
+  const int krow0 = 8 * (g16 >> 1) + e4;
+  uint32_t akm[C::TM], bkm[C::TN];
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int col = wm0 + 32 * i + 16 * (g16 & 1) + 4 * a4;
+    akm[i] = 2u * (uint32_t)(krow0 * BM + ((((col >> 3) ^ swz_km(krow0)) << 3) | (col & 7)));
+  }
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    const int col = wn0 + 32 * j + 16 * (g16 & 1) + 4 * a4;
+    bkm[j] = 2u * (uint32_t)(C::A_ELEMS + krow0 * BN +
+                             ((((col >> 3) ^ swz_km(krow0)) << 3) | (col & 7)));
+  }
+  auto lds_addr = [](const uint16_t *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)p;
+  };
 
   f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -181,15 +254,32 @@ gemm_kernel(GemmArgs g) {
   bf16x8 fa[2][C::TM], fb[2][C::TN];
   // Fragment f of k-step ks of stage st into buffer buf, in first-use order of the MFMA loop
   // below (row-major over (i, j)): A0, B0 .. B(TN-1), A1 .. A(TM-1).
+  // Two transposing reads (k 0..3 and 4..7 of the lane's 8) of a k-major fragment. The
+  // compiler does not see these loads: the k-step that uses the fragment waits for them.
+  auto tr_frag = [&](uint32_t addr, int ks, int R) {
+    u32x2 lo, hi;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(2 * 16 * ks * R));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(hi) : "v"(addr), "i"(2 * (16 * ks + 4) * R));
+    u32x4 w;
+    w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
+    return __builtin_bit_cast(bf16x8, w);
+  };
   auto load_frag = [&](const uint16_t *st, int ks, int buf, int f) {
     const int c_even = ((2 * ks + gq) ^ sw_lane) << 3;
     const int c_odd = BK == 64 ? c_even ^ 32 : c_even;
     if (f >= 1 && f <= C::TN) {
       const int j = f - 1;
-      fb[buf][j] = *(const bf16x8 *)(st + b_base + ((j & 1) ? c_odd : c_even) + 32 * BK * j);
+      if (C::B_KM)
+        fb[buf][j] = tr_frag(lds_addr(st) + bkm[j], ks, BN);
+      else
+        fb[buf][j] = *(const bf16x8 *)(st + b_base + ((j & 1) ? c_odd : c_even) + 32 * BK * j);
     } else {
       const int i = f == 0 ? 0 : f - C::TN;
-      fa[buf][i] = *(const bf16x8 *)(st + a_base + ((i & 1) ? c_odd : c_even) + 32 * BK * i);
+      if (C::A_KM)
+        fa[buf][i] = tr_frag(lds_addr(st) + akm[i], ks, BM);
+      else
+        fa[buf][i] = *(const bf16x8 *)(st + a_base + ((i & 1) ? c_odd : c_even) + 32 * BK * i);
     }
   };
   constexpr int NMF = C::TM * C::TN, NFR = C::TM + C::TN;
@@ -219,6 +309,15 @@ gemm_kernel(GemmArgs g) {
   // the start of every k-step, and issues the copies in one burst.
   auto kstep = [&](int buf, const uint16_t *ld_st, int ld_ks, int ld_buf, int dma_kt,
                    int dma_stage, int dma_lo, int dma_hi) {
+    if (C::A_KM || C::B_KM) {
+      // this k-step's transposed fragments (read during the previous one) have landed; the
+      // empty statements tie every fragment register to the wait
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) asm volatile("" : "+v"(fb[buf][j]));
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) asm volatile("" : "+v"(fa[buf][i]));
+    }
 #pragma unroll
     for (int t = 0; t < NMF; ++t) {
       const int i = t / C::TN, j = t % C::TN;
@@ -283,7 +382,7 @@ gemm_kernel(GemmArgs g) {
     for (int i = 0; i < C::TM; ++i) {
       const int row = wm0 + 32 * i + r32 - r_lo;  // row within this pass
       if (wm0 + 32 * i < r_lo || wm0 + 32 * i >= r_lo + C::RCH) continue;
-      if (EPI == EPI_SWIGLU) {
+      if (C::SWIGLU_FWD) {
 #pragma unroll
         for (int p = 0; p < C::TN / 2; ++p) {
           const int colblk = (wn0 / 64 + p) * 32;  // output columns of this gate/up pair
@@ -299,7 +398,16 @@ gemm_kernel(GemmArgs g) {
             u32x2 w2;
             w2[0] = pack_bf16x2(v[0], v[1]);
             w2[1] = pack_bf16x2(v[2], v[3]);
-            *(u32x2 *)(lds + row * C::CS + colblk + 8 * q4 + 4 * gq) = w2;
+            uint16_t *t = lds + row * C::CS + colblk + 8 * q4 + 4 * gq;
+            *(u32x2 *)t = w2;
+            if (EPI == EPI_SWIGLU_SAVE) {  // zg and zu beside g in the tile
+              w2[0] = pack_bf16x2(acc[i][2 * p][4 * q4], acc[i][2 * p][4 * q4 + 1]);
+              w2[1] = pack_bf16x2(acc[i][2 * p][4 * q4 + 2], acc[i][2 * p][4 * q4 + 3]);
+              *(u32x2 *)(t + C::BN_OUT) = w2;
+              w2[0] = pack_bf16x2(acc[i][2 * p + 1][4 * q4], acc[i][2 * p + 1][4 * q4 + 1]);
+              w2[1] = pack_bf16x2(acc[i][2 * p + 1][4 * q4 + 2], acc[i][2 * p + 1][4 * q4 + 3]);
+              *(u32x2 *)(t + 2 * C::BN_OUT) = w2;
+            }
           }
         }
       } else if (C::F32_TILE) {
@@ -330,12 +438,14 @@ gemm_kernel(GemmArgs g) {
     __syncthreads();
 
     // LDS C rows -> global, 8 columns per thread per step
-    constexpr int CPRO = C::BN_OUT / 8;  // chunks per output row
+    constexpr int CPO = C::BN_OUT / 8;                                // chunks per output row
+    constexpr int CPRO = (EPI == EPI_SWIGLU_SAVE ? 3 : 1) * CPO;      // chunks per tile row
     constexpr int CHUNKS = C::RCH * CPRO;
 #pragma unroll 2
     for (int id = tid; id < CHUNKS; id += C::NT) {
       const int r = id / CPRO, cc = id % CPRO;
-      const int m = m0 + r_lo + r, n = n0 + cc * 8;
+      const int part = EPI == EPI_SWIGLU_SAVE ? cc / CPO : 0;  // g, zg, zu
+      const int m = m0 + r_lo + r, n = n0 + (cc - part * CPO) * 8;
       if (m >= M || n >= n_out) continue;
       if (EPI == EPI_RESIDUAL) {
         const float *lf = (const float *)lds + r * C::CS + cc * 8;
@@ -367,11 +477,41 @@ gemm_kernel(GemmArgs g) {
           yv[h] = pack_bf16x2(ylo, yhi);
         }
         *(u32x4 *)xp = yv;
+        if (g.fsave) {
+          float *fp = g.fsave + (size_t)m * g.ldc + n;
+          *(f32x4 *)fp = f0;
+          *(f32x4 *)(fp + 4) = f1;
+        }
       } else if (EPI == EPI_STORE_F32) {
         const float *lf = (const float *)lds + r * C::CS + cc * 8;
-        float *cp = g.Cf + (size_t)m * g.ldc + n;
+        float *cp = g.M1 > 0 && m >= g.M1 ? g.Cf2 + (size_t)(m - g.M1) * g.ldc + n
+                                          : g.Cf + (size_t)m * g.ldc + n;
         *(f32x4 *)cp = *(const f32x4 *)lf;
         *(f32x4 *)(cp + 4) = *(const f32x4 *)(lf + 4);
+      } else if (EPI == EPI_SWIGLU_BWD) {
+        // dg -> dzg = dg zu SiLU'(zg), dzu = dg SiLU(zg), with SiLU'(z) = s(z)(1 + z(1 - s(z)))
+        const float *lf = (const float *)lds + r * C::CS + cc * 8;
+        const f32x4 d0 = *(const f32x4 *)lf, d1 = *(const f32x4 *)(lf + 4);
+        const uint16_t *zp = g.Z + (size_t)m * g.ldz + n;
+        float zg[8], zu[8], dg[8], og[8], ou[8];
+        unpack8(*(const uint4 *)zp, zg);
+        unpack8(*(const uint4 *)(zp + g.N), zu);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { dg[e] = d0[e]; dg[4 + e] = d1[e]; }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sg = 1.0f / (1.0f + __expf(-zg[e]));
+          ou[e] = dg[e] * (zg[e] * sg);
+          og[e] = dg[e] * zu[e] * (sg * (1.0f + zg[e] * (1.0f - sg)));
+        }
+        uint16_t *cp = g.C + (size_t)m * g.ldc + n;
+        *(uint4 *)cp = pack8(og);
+        *(uint4 *)(cp + g.N) = pack8(ou);
+      } else if (EPI == EPI_SWIGLU_SAVE) {
+        const u32x4 v = *(const u32x4 *)(lds + r * C::CS + cc * 8);
+        uint16_t *dst = part == 0 ? g.C + (size_t)m * g.ldc + n
+                                  : g.Z + (size_t)m * g.ldz + (part - 1) * g.N + n;
+        *(u32x4 *)dst = v;
       } else {
         *(u32x4 *)(g.C + (size_t)m * g.ldc + n) = *(const u32x4 *)(lds + r * C::CS + cc * 8);
       }
@@ -380,16 +520,17 @@ gemm_kernel(GemmArgs g) {
   }  // tile loop
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY = LAY_NT>
 static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
-  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + C::BN_OUT - 1) / C::BN_OUT;
   // device-side row count: a CU-sized grid walks the tiles (g.M is only the bound)
   const int tiles = tiles_m * tiles_n;
   const int wgs_per_cu = C::WAVES_PER_EU * 4 / C::NW;
   const int grid = g.map.n_dev ? min(tiles, 256 * wgs_per_cu) : tiles;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI>), dim3(grid), dim3(C::NT), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY>), dim3(grid), dim3(C::NT), 0,
+                     s, g);
   return hipGetLastError();
 }
 
@@ -401,25 +542,44 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
 //    at least 5/8 of the 256 CUs a tile, else 128x128.
 constexpr int GEMM_CUS = 256;
 
-template <int EPI>
+template <int EPI, int LAY = LAY_NT>
 static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
-  const int half = EPI == EPI_SWIGLU ? 2 : 1;
+  constexpr bool swiglu = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
+  const int half = swiglu ? 2 : 1;
   const long tm = (g.M + 255) / 256;
-  if (EPI == EPI_SWIGLU) {
+  if constexpr (swiglu) {
     const long t_256 = tm * ((g.N + 256 / half - 1) / (256 / half));
-    if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI>(g, s);
+    if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI, LAY>(g, s);
   }
   const long t_big = tm * ((g.N + 128 / half - 1) / (128 / half));
-  if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 128, 64, 64, 3, EPI>(g, s);
-  return run_gemm<128, 128, 64, 64, 64, 3, EPI>(g, s);
+  if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 128, 64, 64, 3, EPI, LAY>(g, s);
+  return run_gemm<128, 128, 64, 64, 64, 3, EPI, LAY>(g, s);
 }
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s) {
+  return launch_gemm(g, epi, LAY_NT, s);
+}
+
+hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, GemmLayout lay, hipStream_t s) {
+  if (lay == LAY_NN) {
+    switch (epi) {
+      case EPI_STORE: return dispatch<EPI_STORE, LAY_NN>(g, s);
+      case EPI_STORE_F32: return dispatch<EPI_STORE_F32, LAY_NN>(g, s);
+      case EPI_SWIGLU_BWD: return dispatch<EPI_SWIGLU_BWD, LAY_NN>(g, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (lay == LAY_TN) {
+    if (epi == EPI_STORE_F32) return dispatch<EPI_STORE_F32, LAY_TN>(g, s);
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case EPI_STORE: return dispatch<EPI_STORE>(g, s);
     case EPI_STORE_F32: return dispatch<EPI_STORE_F32>(g, s);
     case EPI_SWIGLU: return dispatch<EPI_SWIGLU>(g, s);
-    default: return dispatch<EPI_RESIDUAL>(g, s);
+    case EPI_SWIGLU_SAVE: return dispatch<EPI_SWIGLU_SAVE>(g, s);
+    case EPI_RESIDUAL: return dispatch<EPI_RESIDUAL>(g, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -471,6 +471,31 @@ xmod_status xmod_gemm_bf16_nt(const void *A, int32_t lda, const void *Bm, int32_
   return XMOD_OK;
 }
 
+xmod_status xmod_gemm_bf16(int32_t layout, const void *A, int32_t lda, const void *Bm, int32_t ldb,
+                           void *Cm, int32_t ldc, int32_t out_f32, int32_t M, int32_t N,
+                           int32_t K, void *stream) {
+  if (layout < XMOD_GEMM_NT || layout > XMOD_GEMM_TN || !A || !Bm || !Cm || M < 1 || N < 1 ||
+      K < 1 || ldc < N)
+    return XMOD_ERR_INVALID_ARG;
+  const bool a_km = layout == XMOD_GEMM_TN, b_km = layout != XMOD_GEMM_NT;
+  if (lda < (a_km ? M : K) || ldb < (b_km ? N : K)) return XMOD_ERR_INVALID_ARG;
+  if (K % 64 != 0 || N % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || ldc % 8 != 0 ||
+      (a_km && M % 8 != 0) || (layout == XMOD_GEMM_TN && !out_f32))
+    return XMOD_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)(a_km ? K : M) * lda >= lim || (int64_t)(b_km ? K : N) * ldb >= lim ||
+      (int64_t)M * ldc >= lim)
+    return XMOD_ERR_UNSUPPORTED;
+  GemmArgs g{};
+  g.A = (const uint16_t *)A; g.lda = lda; g.B = (const uint16_t *)Bm; g.ldb = ldb;
+  g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+  if (out_f32) g.Cf = (float *)Cm;
+  else g.C = (uint16_t *)Cm;
+  const GemmLayout lay = layout == XMOD_GEMM_NT ? LAY_NT : layout == XMOD_GEMM_NN ? LAY_NN : LAY_TN;
+  XMOD_HIP(launch_gemm(g, out_f32 ? EPI_STORE_F32 : EPI_STORE, lay, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
 xmod_status xmod_attention_fwd(const void *qkv, int32_t ld_qkv, void *o, int32_t ld_o, int32_t B,
                                int32_t k, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                                void *stream) {

@@ -19,6 +19,7 @@ lib = ctypes.CDLL(_LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK, WS_SPARSE_THRESHOLD = 0, 1, 2, 3, 4
 WS_ROUTED_FFN, WS_ATTN_LAYER, WS_SPARSE_FULLKV = 5, 6, 7
+GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 
 # Every symbol include/xmod.h declares, in declaration order.
 EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", "xmod_pack",
@@ -26,7 +27,7 @@ EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", 
             "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_routed_ffn_fwd",
             "xmod_attention_layer_fwd", "xmod_sparse_layer_fwd_fullkv", "xmod_dense_layer_fwd",
             "xmod_block_fwd",
-            "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_attention_fwd",
+            "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_gemm_bf16", "xmod_attention_fwd",
             "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
             "xmod_last_hip_error"]
 
@@ -72,6 +73,8 @@ _sig = {
                               _f32, _vp, _sz, _vp]),
     "xmod_rmsnorm_rows": (_i32, [_vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "xmod_gemm_bf16_nt": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_gemm_bf16": (_i32, [_i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                              _vp]),
     "xmod_attention_fwd": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "xmod_phase_timing_enable": (None, [_i32]),
     "xmod_phase_times": (_i32, [_P(_f32), _i32, _P(_i32)]),
@@ -234,6 +237,19 @@ def gemm_bf16_nt(A, Bm, C, stream=None):
     N = Bm.shape[0]
     _check(lib.xmod_gemm_bf16_nt(_ptr(A), A.stride(0), _ptr(Bm), Bm.stride(0), _ptr(C),
                                  C.stride(0), M, N, K, _stream(stream)), "xmod_gemm_bf16_nt")
+
+
+def gemm_bf16(layout, A, Bm, C, stream=None):
+    """C = A(m, k) B(n, k) summed over k; layouts as xmod_gemm_bf16 (NT: A [M,K], B [N,K];
+    NN: A [M,K], B [K,N]; TN: A [K,M], B [K,N]); C bf16 or fp32 [M, N]."""
+    if layout == GEMM_TN:
+        K, M = A.shape
+    else:
+        M, K = A.shape
+    N = Bm.shape[0] if layout == GEMM_NT else Bm.shape[1]
+    out_f32 = 1 if C.dtype == torch.float32 else 0
+    _check(lib.xmod_gemm_bf16(layout, _ptr(A), A.stride(0), _ptr(Bm), Bm.stride(0), _ptr(C),
+                              C.stride(0), out_f32, M, N, K, _stream(stream)), "xmod_gemm_bf16")
 
 
 def attention_fwd(qkv, o, B, k, Hq, Hkv, hd, stream=None):

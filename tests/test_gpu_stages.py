@@ -207,6 +207,42 @@ def test_gemm(x, M, N, K):
     assert np.all(np.abs(got - ref) <= 0.5 * ulp_bf16(ref) + acc_bound + 1e-30)
 
 
+@pytest.mark.parametrize("layout,M,N,K,f32,pad", [
+    # dY W products of the backward (B stored [K, N]); ragged rows, a K split over many tiles
+    ("NN", 512, 256, 1024, False, 0), ("NN", 700, 2048, 6144, True, 0),
+    ("NN", 4096, 5632, 2048, False, 0), ("NN", 96, 1536, 128, True, 64),
+    # weight gradients dY^T X (sums over K token rows); M and N multiples of 8, not of the tile
+    ("TN", 256, 768, 512, True, 0), ("TN", 2048, 5632, 4096, True, 0),
+    ("TN", 1544, 1032, 192, True, 32), ("TN", 11264, 2048, 256, True, 0),
+    ("NT", 640, 384, 256, True, 0)])
+def test_gemm_layouts(x, layout, M, N, K, f32, pad):
+    say(f"[gemm {layout}] M{M} N{N} K{K} f32={f32} pad={pad}")
+    rng = np.random.default_rng(14)
+    lay = {"NT": x.GEMM_NT, "NN": x.GEMM_NN, "TN": x.GEMM_TN}[layout]
+    a_shape = (K, M) if layout == "TN" else (M, K)
+    b_shape = (N, K) if layout == "NT" else (K, N)
+    A = wl.f32_to_bf16_bits(rng.standard_normal(a_shape).astype(np.float32))
+    Bw = wl.f32_to_bf16_bits((rng.standard_normal(b_shape) * 0.05).astype(np.float32))
+    # optional row padding of A: a strided view (leading dimension > its columns)
+    Ad = dev_bf16(np.pad(A, ((0, 0), (0, pad)))) [:, :a_shape[1]] if pad else dev_bf16(A)
+    C = torch.empty((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    x.gemm_bf16(lay, Ad, dev_bf16(Bw), C)
+    torch.cuda.synchronize()
+    Af, Bf = bf16_vals(A), bf16_vals(Bw)
+    Am = Af.T if layout == "TN" else Af
+    Bm = Bf if layout != "NT" else Bf.T
+    ref = Am @ Bm
+    acc_bound = K * 2.0 ** -24 * (np.abs(Am) @ np.abs(Bm))       # fp32 accumulation
+    if f32:
+        got = C.cpu().numpy().astype(np.float64)
+        out_round = np.abs(ref) * 2.0 ** -24
+    else:
+        got = bf16_vals(host_bits(C))
+        out_round = 0.5 * ulp_bf16(ref)
+    err = np.abs(got - ref) - (out_round + acc_bound + 1e-30)
+    assert np.all(err <= 0), f"worst excess {err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}"
+
+
 @pytest.mark.parametrize("B,k,Hq,Hkv,hd", [(2, 256, 4, 4, 64), (1, 333, 4, 2, 128), (3, 200, 8, 2, 64),
                                            (2, 512, 16, 16, 128), (1, 1100, 4, 1, 128),
                                            (1, 1, 2, 1, 128), (2, 65, 4, 4, 64), (1, 129, 2, 2, 128),
