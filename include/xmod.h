@@ -274,6 +274,25 @@ xmod_status xmod_attention_fwd(const void *qkv, int32_t ld_qkv, void *o, int32_t
                                int32_t B, int32_t k, int32_t n_q_heads, int32_t n_kv_heads,
                                int32_t head_dim, void *stream);
 
+/* Causal attention as xmod_attention_fwd that also stores lse [B*k, n_q_heads] fp32: for each
+ * query row and head, log2 of the softmax normaliser in units where the weight of key j is
+ * exp2(S_j * log2(e) / sqrt(head_dim) - lse). Needed by xmod_attention_bwd. */
+xmod_status xmod_attention_fwd_lse(const void *qkv, int32_t ld_qkv, void *o, int32_t ld_o,
+                                   float *lse, int32_t B, int32_t k, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, void *stream);
+
+/* Backward of xmod_attention_fwd_lse for an output gradient dO [B*k, ld_do] bf16: with
+ * D_q = sum_i dO[q][i] O[q][i], P = softmax of the scaled scores, dP = dO V^T and
+ * dS = P * (dP - D_q): dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd), dV = P^T dO, dK and dV summed
+ * over the query heads sharing a key/value head. Writes dqkv [B*k, ld_dqkv] bf16 in the [Q|K|V]
+ * column layout of qkv (every column). D [B*k, n_q_heads] fp32 is caller scratch (written).
+ * o and lse are the forward's outputs. Requirements as xmod_attention_fwd. */
+xmod_status xmod_attention_bwd(const void *qkv, int32_t ld_qkv, const void *o, int32_t ld_o,
+                               const float *lse, const void *dO, int32_t ld_do, float *D,
+                               void *dqkv, int32_t ld_dqkv, int32_t B, int32_t k,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                               void *stream);
+
 /* --- Measurement hook. ------------------------------------------------------------------------
  * While enabled, the layer and block entry points record a hipEvent on their stream before
  * their first kernel and after every kernel they launch (events are created on first use and

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
                                                       float scale_log2,
                                                       const int32_t *__restrict__ seq_off,
                                                       const int32_t *__restrict__ seq_len,
-                                                      FullKV fkv) {
+                                                      FullKV fkv, float *__restrict__ lse) {
   using C = AttnCfg<HD>;
   constexpr int BQ = C::BQ, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
   // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
@@ -331,6 +331,9 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   // touch 32 rows with 16 bytes each, which the memory system handles far below its rate.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
+  // log2 of the softmax normaliser in the weights' units: P = exp2(score * scale_log2 - lse)
+  if (lse && active && gq == 0 && q_pos < k)
+    lse[(row0 + q_pos) * Hq + h] = m_ref + __builtin_amdgcn_logf(l_tot);  // v_log_f32: log2
   if (active) {
     uint16_t *ow = lds + wid * 32 * HD;
 #pragma unroll
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
 template <bool FULLKV>
 static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
                         int Hq, int Hkv, int hd, const int32_t *seq_off, const int32_t *seq_len,
-                        const FullKV &fkv, hipStream_t s) {
+                        const FullKV &fkv, hipStream_t s, float *lse = nullptr) {
   const int nqt = (k + 127) / 128;
   // per-sequence lengths (k is then only their bound): a quarter of the pairs of a longest
   // sequence per (head, sequence), each workgroup looping over its share
@@ -367,16 +370,22 @@ static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, 
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 128)
     hipLaunchKernelGGL((attn_kernel<128, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
-                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv);
+                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse);
   else
     hipLaunchKernelGGL((attn_kernel<64, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
-                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv);
+                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse);
 }
 
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
                             int Hq, int Hkv, int hd, const int32_t *seq_off,
                             const int32_t *seq_len, hipStream_t s) {
   launch_attn<false>(qkv, ld_qkv, o, ld_o, B, k, Hq, Hkv, hd, seq_off, seq_len, FullKV{}, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_lse(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, float *lse,
+                                int B, int k, int Hq, int Hkv, int hd, hipStream_t s) {
+  launch_attn<false>(qkv, ld_qkv, o, ld_o, B, k, Hq, Hkv, hd, nullptr, nullptr, FullKV{}, s, lse);
   return hipGetLastError();
 }
 

@@ -182,6 +182,18 @@ hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld
                             int Hq, int Hkv, int hd, const int32_t *seq_off,
                             const int32_t *seq_len, hipStream_t s);
 
+// launch_attention for fixed-length sequences that also stores lse[row * Hq + h], the log2 of
+// each query's softmax normaliser in the units of the weights (P = exp2(score * scale_log2 - lse)).
+hipError_t launch_attention_lse(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, float *lse,
+                                int B, int k, int Hq, int Hkv, int hd, hipStream_t s);
+
+// Backward of launch_attention_lse for fixed-length sequences: D[row * Hq + h] (fp32 scratch)
+// and dqkv = [dQ | dK | dV] bf16 rows (ld_dqkv), every column written.
+hipError_t launch_attention_bwd(const uint16_t *qkv, int ld_qkv, const uint16_t *o, int ld_o,
+                                const float *lse, const uint16_t *dO, int ld_do, float *D,
+                                uint16_t *dqkv, int ld_dqkv, int B, int k, int Hq, int Hkv,
+                                int hd, hipStream_t s);
+
 // Selected-Q/full-KV attention: queries q [B*k, ld_q] (packed, Hq heads), keys and values of
 // every position kv [B*T, ld_kv] ([K heads | V heads]); packed query b*k + j sits at original
 // position qpos[b*k + j] and sees keys at positions <= it.

@@ -511,6 +511,44 @@ xmod_status xmod_attention_fwd(const void *qkv, int32_t ld_qkv, void *o, int32_t
   return XMOD_OK;
 }
 
+static xmod_status attn_shape_ok(int32_t B, int32_t k, int32_t Hq, int32_t Hkv, int32_t hd) {
+  if (B < 1 || k < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return XMOD_ERR_INVALID_ARG;
+  if (hd != 64 && hd != 128) return XMOD_ERR_UNSUPPORTED;
+  return XMOD_OK;
+}
+
+xmod_status xmod_attention_fwd_lse(const void *qkv, int32_t ld_qkv, void *o, int32_t ld_o,
+                                   float *lse, int32_t B, int32_t k, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int32_t head_dim, void *stream) {
+  if (!qkv || !o || !lse) return XMOD_ERR_INVALID_ARG;
+  const xmod_status st = attn_shape_ok(B, k, n_q_heads, n_kv_heads, head_dim);
+  if (st != XMOD_OK) return st;
+  const int32_t nqkv = (n_q_heads + 2 * n_kv_heads) * head_dim;
+  if (ld_qkv < nqkv || ld_o < n_q_heads * head_dim || ld_qkv % 8 != 0 || ld_o % 8 != 0)
+    return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_attention_lse((const uint16_t *)qkv, ld_qkv, (uint16_t *)o, ld_o, lse, B, k,
+                                n_q_heads, n_kv_heads, head_dim, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_attention_bwd(const void *qkv, int32_t ld_qkv, const void *o, int32_t ld_o,
+                               const float *lse, const void *dO, int32_t ld_do, float *D,
+                               void *dqkv, int32_t ld_dqkv, int32_t B, int32_t k,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                               void *stream) {
+  if (!qkv || !o || !lse || !dO || !D || !dqkv) return XMOD_ERR_INVALID_ARG;
+  const xmod_status st = attn_shape_ok(B, k, n_q_heads, n_kv_heads, head_dim);
+  if (st != XMOD_OK) return st;
+  const int32_t dq = n_q_heads * head_dim, nqkv = (n_q_heads + 2 * n_kv_heads) * head_dim;
+  if (ld_qkv < nqkv || ld_dqkv < nqkv || ld_o < dq || ld_do < dq || ld_qkv % 8 != 0 ||
+      ld_dqkv % 8 != 0 || ld_o % 8 != 0 || ld_do % 8 != 0)
+    return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_attention_bwd((const uint16_t *)qkv, ld_qkv, (const uint16_t *)o, ld_o, lse,
+                                (const uint16_t *)dO, ld_do, D, (uint16_t *)dqkv, ld_dqkv, B, k,
+                                n_q_heads, n_kv_heads, head_dim, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
 void xmod_phase_timing_enable(int32_t on) {
   g_phase.on = on != 0;
   g_phase.used = 0;

@@ -28,6 +28,7 @@ EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", 
             "xmod_attention_layer_fwd", "xmod_sparse_layer_fwd_fullkv", "xmod_dense_layer_fwd",
             "xmod_block_fwd",
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_gemm_bf16", "xmod_attention_fwd",
+            "xmod_attention_fwd_lse", "xmod_attention_bwd",
             "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
             "xmod_last_hip_error"]
 
@@ -73,6 +74,10 @@ _sig = {
                               _f32, _vp, _sz, _vp]),
     "xmod_rmsnorm_rows": (_i32, [_vp, _vp, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "xmod_gemm_bf16_nt": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_attention_fwd_lse": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                      _vp]),
+    "xmod_attention_bwd": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32,
+                                  _i32, _i32, _i32, _i32, _vp]),
     "xmod_gemm_bf16": (_i32, [_i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                               _vp]),
     "xmod_attention_fwd": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
@@ -250,6 +255,17 @@ def gemm_bf16(layout, A, Bm, C, stream=None):
     out_f32 = 1 if C.dtype == torch.float32 else 0
     _check(lib.xmod_gemm_bf16(layout, _ptr(A), A.stride(0), _ptr(Bm), Bm.stride(0), _ptr(C),
                               C.stride(0), out_f32, M, N, K, _stream(stream)), "xmod_gemm_bf16")
+
+
+def attention_fwd_lse(qkv, o, lse, B, k, Hq, Hkv, hd, stream=None):
+    _check(lib.xmod_attention_fwd_lse(_ptr(qkv), qkv.stride(0), _ptr(o), o.stride(0), _ptr(lse),
+                                      B, k, Hq, Hkv, hd, _stream(stream)), "xmod_attention_fwd_lse")
+
+
+def attention_bwd(qkv, o, lse, dO, D, dqkv, B, k, Hq, Hkv, hd, stream=None):
+    _check(lib.xmod_attention_bwd(_ptr(qkv), qkv.stride(0), _ptr(o), o.stride(0), _ptr(lse),
+                                  _ptr(dO), dO.stride(0), _ptr(D), _ptr(dqkv), dqkv.stride(0), B,
+                                  k, Hq, Hkv, hd, _stream(stream)), "xmod_attention_bwd")
 
 
 def attention_fwd(qkv, o, B, k, Hq, Hkv, hd, stream=None):
