@@ -116,7 +116,9 @@ enum {
   XMOD_WS_SPARSE_THRESHOLD = 4,
   XMOD_WS_ROUTED_FFN = 5,
   XMOD_WS_ATTN_LAYER = 6,
-  XMOD_WS_SPARSE_FULLKV = 7
+  XMOD_WS_SPARSE_FULLKV = 7,
+  XMOD_WS_TRAIN_SAVED = 8,  /* what xmod_sparse_layer_fwd_train keeps for the backward */
+  XMOD_WS_BACKWARD = 9      /* workspace of xmod_sparse_layer_bwd */
 };
 
 /* Workspace bytes an entry point needs for these shapes (0 if none). K is ignored for the
@@ -239,6 +241,57 @@ xmod_status xmod_block_fwd(void *x, const xmod_layer *layers, int32_t n_layers,
                            const xmod_dims *dims, int32_t N0, int32_t N1, float A, int32_t K,
                            float *bias, float tau, float delta, void *ws, size_t ws_bytes,
                            void *stream);
+
+/* --- Training: the sparse layer's backward pass. ----------------------------------------------
+ *
+ * [XMOD] "training-time top-k, eval-time causal threshold": the layer is trained with the
+ * top-k routing and, beside the language-model loss, a routing loss (Eq. (9)): the binary
+ * cross-entropy between the top-k decision q_i of every token and p_i = sigmoid(s_i), the
+ * router's probability (s_i = w_r . x_i + beta_r, without the carried bias), averaged over the
+ * n = B*T tokens and added with a small coefficient (the page picks 1e-4). The top-k choice and
+ * the carried bias pass no gradient; the router's weights get theirs through the gate r of the
+ * selected tokens (Eqs. (7)-(8)) and through the routing loss. Core layer form only: residual 0,
+ * no QK-norm, no RoPE (XMOD_ERR_UNSUPPORTED otherwise). */
+
+/* Gradients of one layer's parameters: device fp32 arrays with the shapes of the weights
+ * (router_bias and varsigma: one float each). The backward writes them (no accumulation). */
+typedef struct {
+  float *w_router;     /* [d] */
+  float *router_bias;  /* [1] */
+  float *varsigma;     /* [1] */
+  float *g_attn;       /* [d] */
+  float *w_qkv;        /* [Hq*hd + 2*Hkv*hd, d] */
+  float *w_o;          /* [d, Hq*hd] */
+  float *g_ffn;        /* [d] */
+  float *w_gate;       /* [F, d] */
+  float *w_up;         /* [F, d] */
+  float *w_down;       /* [d, F] */
+} xmod_layer_grads;
+
+/* xmod_sparse_layer_fwd (same arguments and results) that also keeps in `saved` (device, at
+ * least xmod_workspace_bytes(dims, K, XMOD_WS_TRAIN_SAVED) bytes, caller-owned) everything the
+ * backward reads: the router logits s, the selection and gates, the packed input rows X and
+ * every intermediate of the attention and FFN of the selected rows. The contents of `saved`
+ * are opaque and stay valid until the caller reuses the buffer. No other workspace. */
+xmod_status xmod_sparse_layer_fwd_train(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                        int32_t K, float *bias, float tau, float delta,
+                                        int32_t *idx_out, float *gate_out, void *saved,
+                                        size_t saved_bytes, void *stream);
+
+/* Backward of the layer that xmod_sparse_layer_fwd_train ran (same layer, dims, K; its `saved`
+ * unchanged since) for the objective <dy, y> + route_coef * L_route:
+ *   x    [B, T, d] bf16: the hidden state as that forward left it (its unselected rows are the
+ *        layer's input there);
+ *   dy   [B, T, d] bf16: gradient of the objective's first term with respect to the output y;
+ *   dx   [B, T, d] bf16 out: gradient with respect to the layer's input (may be dy itself);
+ *   grads: parameter gradients (written); loss_route: device float receiving L_route, or NULL.
+ * Workspace: XMOD_WS_BACKWARD. Gradients of activations are carried in bf16, weight gradients
+ * and every sum in fp32; the sums over tokens are taken in a fixed order (deterministic). */
+xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
+                                  const xmod_layer *layer, const xmod_dims *dims, int32_t K,
+                                  float route_coef, const void *saved, size_t saved_bytes,
+                                  const xmod_layer_grads *grads, float *loss_route, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* --- Stages of the path, exposed for stage-by-stage parity checks. ------------------------ */
 

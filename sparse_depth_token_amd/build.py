@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libxmod.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["route.hip", "rows.hip", "gemm.hip", "attention.hip", "attention_bwd.hip",
+SOURCES = ["route.hip", "rows.hip", "rows_bwd.hip", "gemm.hip", "attention.hip",
+           "attention_bwd.hip",
            "xmod_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -97,8 +97,10 @@ __device__ __forceinline__ int64_t rowmap_count(const RowMap &r, int64_t bound) 
 // ---- launchers (host side, defined in the .hip files) ---------------------------------------
 namespace xmod {
 
+// logits = s - tau*b in fp32; s_out (optional) receives s = w.x + beta itself.
 hipError_t launch_router(const uint16_t *x, const uint16_t *w, float beta, const float *bias,
-                         float tau, float *logits, int64_t rows, int d, hipStream_t s);
+                         float tau, float *logits, int64_t rows, int d, hipStream_t s,
+                         float *s_out = nullptr);
 
 hipError_t launch_topk(const float *logits, int B, int T, int k, int32_t *idx, float *gate,
                        float *bias, float delta, hipStream_t s);
@@ -115,10 +117,11 @@ hipError_t launch_threshold_select(const float *logits, int B, int T, int32_t *c
 hipError_t launch_mask_agreement(const float *logits, const int32_t *idx, int B, int T, int k,
                                  uint32_t *agree, hipStream_t s);
 
-// Gather rows (via the row map) and optionally RMSNorm them. rows: launch bound.
+// Gather rows (via the row map) and optionally RMSNorm them. rows: launch bound. With
+// normalize, xraw (optional) also receives the gathered rows themselves.
 hipError_t launch_gather_rows(const uint16_t *x, const RowMap &map, const uint16_t *gain,
                               float eps, bool normalize, int64_t rows, int d, uint16_t *out,
-                              hipStream_t s);
+                              hipStream_t s, uint16_t *xraw = nullptr);
 
 // v[m] = RMSNorm(X[m] + a[m]; gain), X gathered from x via the row map; a fp32.
 hipError_t launch_residual_rmsnorm(const uint16_t *x, const RowMap &map, const float *a,
@@ -193,6 +196,30 @@ hipError_t launch_attention_bwd(const uint16_t *qkv, int ld_qkv, const uint16_t 
                                 const float *lse, const uint16_t *dO, int ld_do, float *D,
                                 uint16_t *dqkv, int ld_dqkv, int B, int k, int Hq, int Hkv,
                                 int hd, hipStream_t s);
+
+// ---- backward row kernels (rows_bwd.hip) ----
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);          // bytes / 16 chunks
+hipError_t launch_copy32(void *dst, const void *src, int64_t n_words, hipStream_t s);
+int bwd_row_waves();  // waves of the row kernels = per-wave partial rows they write
+hipError_t launch_colsum(const float *part, int n_part, int n, float *tmp, float *out,
+                         float scale, hipStream_t s);  // tmp: 16 * n floats
+hipError_t launch_resid_bwd(const uint16_t *dy, const RowMap &map, const float *a, const float *f,
+                            const float *gate, float varsigma, int d, int64_t M, int64_t M_pad,
+                            uint16_t *dt, float *dell, float *dell_tok, uint8_t *q_tok,
+                            float *vs_part, hipStream_t s);
+hipError_t launch_rms2_bwd(const uint16_t *dy, const RowMap &map, const uint16_t *X,
+                           const float *a, const float *dv, const uint16_t *gain, float eps,
+                           const uint16_t *dt, int d, int64_t M, int64_t M_pad, uint16_t *da,
+                           float *dXacc, float *g_part, hipStream_t s);
+hipError_t launch_rms1_bwd(const uint16_t *X, const RowMap &map, const float *du,
+                           const uint16_t *gain, float eps, const float *dXacc,
+                           const float *s_tok, const float *dell, float coef_n,
+                           const uint16_t *w_r, int d, int64_t M, uint16_t *dx, float *g_part,
+                           float *wr_part, hipStream_t s);
+hipError_t launch_route_bwd(const uint16_t *x, const uint16_t *dy, const float *s_tok,
+                            const float *dell_tok, const uint8_t *q_tok, float coef_n,
+                            const uint16_t *w_r, int d, int64_t rows, uint16_t *dx,
+                            float *wr_part, float *beta_part, float *loss_part, hipStream_t s);
 
 // Selected-Q/full-KV attention: queries q [B*k, ld_q] (packed, Hq heads), keys and values of
 // every position kv [B*T, ld_kv] ([K heads | V heads]); packed query b*k + j sits at original

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
                                                      const uint16_t *__restrict__ w, float beta,
                                                      const float *__restrict__ bias, float tau,
                                                      float *__restrict__ logits, int64_t rows,
-                                                     int d) {
+                                                     int d, float *__restrict__ s_out) {
   const int lane = threadIdx.x & 63;
   const int nch = d >> 3;  // 8-element chunks per row
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
         const float s = __fadd_rn(acc[r], beta);
         const float tb = bias ? __fmul_rn(tau, bias[row]) : 0.f;
         logits[row] = __fsub_rn(s, tb);
+        if (s_out) s_out[row] = s;
       }
     }
   }
@@ -77,26 +78,28 @@ __global__ __launch_bounds__(256) void router_kernel(const uint16_t *__restrict_
 
 template <int NI>
 static hipError_t router_ni(const uint16_t *x, const uint16_t *w, float beta, const float *bias,
-                            float tau, float *logits, int64_t rows, int d, hipStream_t s) {
+                            float tau, float *logits, int64_t rows, int d, hipStream_t s,
+                            float *s_out) {
   constexpr int R = NI <= 2 ? 8 : (NI <= 4 ? 4 : (NI <= 8 ? 2 : 1));
   const int64_t waves = (rows + R - 1) / R;
   const int64_t blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((router_kernel<NI, R>), dim3((unsigned)blocks), dim3(256), 0, s, x, w, beta,
-                     bias, tau, logits, rows, d);
+                     bias, tau, logits, rows, d, s_out);
   return hipGetLastError();
 }
 
 hipError_t launch_router(const uint16_t *x, const uint16_t *w, float beta, const float *bias,
-                         float tau, float *logits, int64_t rows, int d, hipStream_t s) {
+                         float tau, float *logits, int64_t rows, int d, hipStream_t s,
+                         float *s_out) {
   const int ni = ((d >> 3) + 63) / 64;
   switch (ni) {
-    case 1: return router_ni<1>(x, w, beta, bias, tau, logits, rows, d, s);
-    case 2: return router_ni<2>(x, w, beta, bias, tau, logits, rows, d, s);
-    case 3: return router_ni<3>(x, w, beta, bias, tau, logits, rows, d, s);
-    case 4: return router_ni<4>(x, w, beta, bias, tau, logits, rows, d, s);
-    case 5: case 6: return router_ni<6>(x, w, beta, bias, tau, logits, rows, d, s);
-    case 7: case 8: return router_ni<8>(x, w, beta, bias, tau, logits, rows, d, s);
-    default: return router_ni<16>(x, w, beta, bias, tau, logits, rows, d, s);
+    case 1: return router_ni<1>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
+    case 2: return router_ni<2>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
+    case 3: return router_ni<3>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
+    case 4: return router_ni<4>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
+    case 5: case 6: return router_ni<6>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
+    case 7: case 8: return router_ni<8>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
+    default: return router_ni<16>(x, w, beta, bias, tau, logits, rows, d, s, s_out);
   }
 }
 

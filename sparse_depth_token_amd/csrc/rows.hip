@@ -13,7 +13,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
                                                           RowMap map,
                                                           const uint16_t *__restrict__ gain,
                                                           float eps, int d, int64_t rows,
-                                                          uint16_t *__restrict__ out) {
+                                                          uint16_t *__restrict__ out,
+                                                          uint16_t *__restrict__ xraw) {
   const int lane = threadIdx.x & 63;
   const int64_t n_rows = rowmap_count(map, rows);
   for (int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); m < n_rows;
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
     const int c = lane + 64 * i;
     if (c < nch) {
       float f[8], g[8];
+      if (xraw) *(uint4 *)(xraw + m * d + (size_t)c * 8) = v[i];  // the gathered row itself
       unpack8(v[i], f);
       unpack8(*(const uint4 *)(gain + (size_t)c * 8), g);
 #pragma unroll
@@ -215,16 +217,16 @@ static dim3 row_grid(const RowMap &map, int64_t rows) {
 
 hipError_t launch_gather_rows(const uint16_t *x, const RowMap &map, const uint16_t *gain,
                               float eps, bool normalize, int64_t rows, int d, uint16_t *out,
-                              hipStream_t s) {
+                              hipStream_t s, uint16_t *xraw) {
   if (rows < 1) return hipSuccess;
   const dim3 grid = row_grid(map, rows);
 #define L_(NI)                                                                                  \
   if (normalize)                                                                                \
     hipLaunchKernelGGL((gather_rows_kernel<NI, true>), grid, dim3(256), 0, s, x, map, gain, eps, \
-                       d, rows, out);                                                           \
+                       d, rows, out, xraw);                                                     \
   else                                                                                          \
     hipLaunchKernelGGL((gather_rows_kernel<NI, false>), grid, dim3(256), 0, s, x, map, gain,    \
-                       eps, d, rows, out)
+                       eps, d, rows, out, nullptr)
   XMOD_NI_SWITCH(ni_for(d), L_)
 #undef L_
   return hipGetLastError();

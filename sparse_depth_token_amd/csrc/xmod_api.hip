@@ -300,6 +300,8 @@ xmod_status route_topk_into(const void *x, const xmod_layer *L, const xmod_dims 
 
 }  // namespace
 
+size_t xmod_train_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry);
+
 size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_point) {
   if (check_dims(dims) != XMOD_OK) return 0;
   switch (entry_point) {
@@ -317,6 +319,9 @@ size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_poin
     case XMOD_WS_SPARSE_FULLKV:
       if (K < 1 || dims->T / K < 1) return 0;
       return plan_mech(dims, (int64_t)dims->B * (dims->T / K), 2).total;
+    case XMOD_WS_TRAIN_SAVED:
+    case XMOD_WS_BACKWARD:
+      return xmod_train_workspace_bytes(dims, K, entry_point);
     case XMOD_WS_BLOCK: {
       const size_t dn = plan_layer(dims, (int64_t)dims->B * dims->T, false).total;
       if (K < 1 || dims->T / K < 1) return dn;
@@ -788,5 +793,264 @@ xmod_status xmod_sparse_layer_fwd_fullkv(void *x, const xmod_layer *layer, const
   g.residual_form = layer->residual;
   XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
   phase_mark(s);
+  return XMOD_OK;
+}
+
+// ---- training: forward that keeps what the backward reads, and the backward -------------------
+
+namespace {
+
+// Packed rows are padded to a multiple of 64 for the weight-gradient products (sums over the
+// rows); padding rows of their operands are zero.
+int64_t pad_rows(int64_t M) { return (M + 63) / 64 * 64; }
+
+struct PlanTrain {
+  size_t s = 0, logits = 0, idx = 0, gate = 0, X = 0, u = 0, qkv = 0, o = 0, lse = 0, a = 0;
+  size_t v = 0, g = 0, z = 0, f = 0, total = 0;
+};
+
+PlanTrain plan_train(const xmod_dims *dm, int64_t M) {
+  PlanTrain p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  const int64_t BT = (int64_t)dm->B * dm->T, Mp = pad_rows(M), d = dm->d, F = dm->ffn_hidden;
+  const int64_t dq = (int64_t)dm->n_q_heads * dm->head_dim;
+  const int64_t nqkv = dq + 2LL * dm->n_kv_heads * dm->head_dim;
+  p.s = take(BT * 4);
+  p.logits = take(BT * 4);
+  p.idx = take(M * 4);
+  p.gate = take(M * 4);
+  p.X = take(Mp * d * 2);
+  p.u = take(Mp * d * 2);
+  p.qkv = take(Mp * nqkv * 2);
+  p.o = take(Mp * dq * 2);
+  p.lse = take(M * dm->n_q_heads * 4);
+  p.a = take(M * d * 4);
+  p.v = take(Mp * d * 2);
+  p.g = take(Mp * F * 2);
+  p.z = take(Mp * 2 * F * 2);
+  p.f = take(M * d * 4);
+  p.total = off;
+  return p;
+}
+
+struct PlanBwd {
+  size_t dt = 0, dz = 0, dv = 0, da = 0, dxacc = 0, dO = 0, D = 0, dqkv = 0, dell = 0;
+  size_t dell_tok = 0, q_tok = 0, part = 0, spart = 0, tmp = 0, total = 0;
+};
+
+PlanBwd plan_bwd(const xmod_dims *dm, int64_t M) {
+  PlanBwd p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes); return at; };
+  const int64_t BT = (int64_t)dm->B * dm->T, Mp = pad_rows(M), d = dm->d, F = dm->ffn_hidden;
+  const int64_t dq = (int64_t)dm->n_q_heads * dm->head_dim;
+  const int64_t nqkv = dq + 2LL * dm->n_kv_heads * dm->head_dim;
+  const int64_t waves = bwd_row_waves();
+  p.dt = take(Mp * d * 2);
+  p.dz = take(Mp * 2 * F * 2);
+  p.dv = take(M * d * 4);       // dv, later du
+  p.da = take(Mp * d * 2);
+  p.dxacc = take(M * d * 4);
+  p.dO = take(M * dq * 2);
+  p.D = take(M * dm->n_q_heads * 4);
+  p.dqkv = take(Mp * nqkv * 2);
+  p.dell = take(M * 4);
+  p.dell_tok = take(BT * 4);
+  p.q_tok = take(BT);
+  p.part = take(2 * waves * d * 4);
+  p.spart = take(3 * waves * 4);
+  p.tmp = take(16 * d * 4);
+  p.total = off;
+  return p;
+}
+
+bool core_form(const xmod_layer *L) {
+  return L->residual == 0 && !L->q_norm && !L->k_norm && L->rope_theta == 0.f;
+}
+
+// zero rows [M, Mp) of a row-major bf16 buffer with `width` columns
+xmod_status zero_pad_rows(uint16_t *buf, int64_t M, int64_t Mp, int64_t width, hipStream_t s) {
+  if (Mp > M) XMOD_HIP(launch_zero(buf + M * width, (size_t)((Mp - M) * width * 2), s));
+  return XMOD_OK;
+}
+
+}  // namespace
+
+size_t xmod_train_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry) {
+  if (check_dims(dims) != XMOD_OK || K < 1 || dims->T / K < 1) return 0;
+  const int64_t M = (int64_t)dims->B * (dims->T / K);
+  return entry == XMOD_WS_TRAIN_SAVED ? plan_train(dims, M).total : plan_bwd(dims, M).total;
+}
+
+xmod_status xmod_sparse_layer_fwd_train(void *x, const xmod_layer *layer, const xmod_dims *dims,
+                                        int32_t K, float *bias, float tau, float delta,
+                                        int32_t *idx_out, float *gate_out, void *saved,
+                                        size_t saved_bytes, void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  if (!core_form(layer)) return XMOD_ERR_UNSUPPORTED;
+  const int k = dims->T / K;
+  const int64_t M = (int64_t)dims->B * k, Mp = pad_rows(M), BT = (int64_t)dims->B * dims->T;
+  const PlanTrain p = plan_train(dims, M);
+  if (!saved || saved_bytes < p.total) return XMOD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = dims->d, F = dims->ffn_hidden, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads;
+  const int hd = dims->head_dim, dq = Hq * hd, nqkv = dq + 2 * Hkv * hd;
+  float *sv = at<float>(saved, p.s), *logits = at<float>(saved, p.logits);
+  int32_t *idx = at<int32_t>(saved, p.idx);
+  float *gate = at<float>(saved, p.gate), *lse = at<float>(saved, p.lse);
+  uint16_t *Xs = at<uint16_t>(saved, p.X), *u = at<uint16_t>(saved, p.u);
+  uint16_t *qkv = at<uint16_t>(saved, p.qkv), *o = at<uint16_t>(saved, p.o);
+  uint16_t *v = at<uint16_t>(saved, p.v), *gb = at<uint16_t>(saved, p.g);
+  uint16_t *z = at<uint16_t>(saved, p.z);
+  float *a = at<float>(saved, p.a), *f = at<float>(saved, p.f);
+
+  XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)layer->w_router,
+                         layer->router_bias, bias, tau, logits, BT, d, s, sv));
+  XMOD_HIP(launch_topk(logits, dims->B, dims->T, k, idx, gate, bias, delta, s));
+  if (idx_out) XMOD_HIP(launch_copy32(idx_out, idx, M, s));
+  if (gate_out) XMOD_HIP(launch_copy32(gate_out, gate, M, s));
+  const RowMap map = topk_map(idx, dims, k);
+  XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, (const uint16_t *)layer->g_attn,
+                              dims->rms_eps, true, M, d, u, s, Xs));
+  GemmArgs g{};
+  g.A = u; g.lda = d; g.B = (const uint16_t *)layer->w_qkv; g.ldb = d; g.C = qkv; g.ldc = nqkv;
+  g.M = (int)M; g.N = nqkv; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, s));
+  XMOD_HIP(launch_attention_lse(qkv, nqkv, o, dq, lse, dims->B, k, Hq, Hkv, hd, s));
+  g = GemmArgs{};
+  g.A = o; g.lda = dq; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.Cf = a; g.ldc = d;
+  g.M = (int)M; g.N = d; g.K = dq;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, s));
+  XMOD_HIP(launch_residual_rmsnorm((const uint16_t *)x, map, a, (const uint16_t *)layer->g_ffn,
+                                   dims->rms_eps, M, d, v, s));
+  g = GemmArgs{};
+  g.A = v; g.lda = d; g.B = (const uint16_t *)layer->w_gate; g.B2 = (const uint16_t *)layer->w_up;
+  g.ldb = d; g.C = gb; g.ldc = F; g.Z = z; g.ldz = 2 * F; g.M = (int)M; g.N = F; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_SWIGLU_SAVE, s));
+  g = GemmArgs{};
+  g.map = map;
+  g.A = gb; g.lda = F; g.B = (const uint16_t *)layer->w_down; g.ldb = F; g.ldc = d;
+  g.M = (int)M; g.N = d; g.K = F;
+  g.x = (uint16_t *)x; g.gate = gate; g.varsigma = layer->varsigma; g.a = a; g.fsave = f;
+  XMOD_HIP(launch_gemm(g, EPI_RESIDUAL, s));
+  // padding rows of the operands the weight-gradient products read
+  if (zero_pad_rows(u, M, Mp, d, s) != XMOD_OK || zero_pad_rows(o, M, Mp, dq, s) != XMOD_OK ||
+      zero_pad_rows(v, M, Mp, d, s) != XMOD_OK || zero_pad_rows(gb, M, Mp, F, s) != XMOD_OK)
+    return XMOD_ERR_HIP;
+  return XMOD_OK;
+}
+
+xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
+                                  const xmod_layer *layer, const xmod_dims *dims, int32_t K,
+                                  float route_coef, const void *saved, size_t saved_bytes,
+                                  const xmod_layer_grads *gr, float *loss_route, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !dy || !dx || !saved || !gr || !layer_ok(layer, true) || K < 1 || dims->T / K < 1)
+    return XMOD_ERR_INVALID_ARG;
+  if (!gr->w_router || !gr->router_bias || !gr->varsigma || !gr->g_attn || !gr->w_qkv ||
+      !gr->w_o || !gr->g_ffn || !gr->w_gate || !gr->w_up || !gr->w_down)
+    return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(route_coef)) return XMOD_ERR_INVALID_ARG;
+  if (!core_form(layer)) return XMOD_ERR_UNSUPPORTED;
+  const int k = dims->T / K;
+  const int64_t M = (int64_t)dims->B * k, Mp = pad_rows(M), BT = (int64_t)dims->B * dims->T;
+  const PlanTrain p = plan_train(dims, M);
+  const PlanBwd q = plan_bwd(dims, M);
+  if (saved_bytes < p.total || !ws || ws_bytes < q.total) return XMOD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void *sv_ = const_cast<void *>(saved);
+  const int d = dims->d, F = dims->ffn_hidden, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads;
+  const int hd = dims->head_dim, dq = Hq * hd, nqkv = dq + 2 * Hkv * hd;
+  const float eps = dims->rms_eps;
+  const float coef_n = (float)((double)route_coef / (double)BT);
+  const int waves = bwd_row_waves();
+  // saved by the forward
+  const float *s_tok = at<float>(sv_, p.s), *gate = at<float>(sv_, p.gate);
+  const int32_t *idx = at<int32_t>(sv_, p.idx);
+  const uint16_t *Xs = at<uint16_t>(sv_, p.X), *u = at<uint16_t>(sv_, p.u);
+  const uint16_t *qkv = at<uint16_t>(sv_, p.qkv), *o = at<uint16_t>(sv_, p.o);
+  const uint16_t *v = at<uint16_t>(sv_, p.v), *gb = at<uint16_t>(sv_, p.g);
+  uint16_t *z = at<uint16_t>(sv_, p.z);
+  const float *lse = at<float>(sv_, p.lse), *a = at<float>(sv_, p.a), *f = at<float>(sv_, p.f);
+  // workspace
+  uint16_t *dt = at<uint16_t>(ws, q.dt), *dz = at<uint16_t>(ws, q.dz), *da = at<uint16_t>(ws, q.da);
+  uint16_t *dO = at<uint16_t>(ws, q.dO), *dqkv = at<uint16_t>(ws, q.dqkv);
+  float *dv = at<float>(ws, q.dv), *dxacc = at<float>(ws, q.dxacc), *D = at<float>(ws, q.D);
+  float *dell = at<float>(ws, q.dell), *dell_tok = at<float>(ws, q.dell_tok);
+  uint8_t *q_tok = at<uint8_t>(ws, q.q_tok);
+  float *part = at<float>(ws, q.part), *spart = at<float>(ws, q.spart), *tmp = at<float>(ws, q.tmp);
+  float *vs_part = spart, *beta_part = spart + waves, *loss_part = spart + 2 * waves;
+  const RowMap map = topk_map(idx, dims, k);
+
+  // gated residual: dt, the gate's gradient, d varsigma partials; selection marks per token
+  XMOD_HIP(launch_zero(dell_tok, align_up((size_t)BT * 4), s));
+  XMOD_HIP(launch_zero(q_tok, align_up((size_t)BT), s));
+  XMOD_HIP(launch_resid_bwd((const uint16_t *)dy, map, a, f, gate, layer->varsigma, d, M, Mp, dt,
+                            dell, dell_tok, q_tok, vs_part, s));
+  // FFN: dg = dt W_down (SwiGLU backward in the epilogue), dW_down = dt^T g
+  GemmArgs g{};
+  g.A = dt; g.lda = d; g.B = (const uint16_t *)layer->w_down; g.ldb = F; g.C = dz; g.ldc = 2 * F;
+  g.Z = z; g.ldz = 2 * F; g.M = (int)M; g.N = F; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_SWIGLU_BWD, LAY_NN, s));
+  if (zero_pad_rows(dz, M, Mp, 2 * F, s) != XMOD_OK) return XMOD_ERR_HIP;
+  g = GemmArgs{};
+  g.A = dt; g.lda = d; g.B = gb; g.ldb = F; g.Cf = gr->w_down; g.ldc = F;
+  g.M = d; g.N = F; g.K = (int)Mp;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  // dv = dzg W_gate + dzu W_up; [dW_gate; dW_up] = [dzg | dzu]^T v
+  g = GemmArgs{};
+  g.A = dz; g.lda = 2 * F; g.B = (const uint16_t *)layer->w_gate; g.B2 = (const uint16_t *)layer->w_up;
+  g.K1 = F; g.ldb = d; g.Cf = dv; g.ldc = d; g.M = (int)M; g.N = d; g.K = 2 * F;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_NN, s));
+  g = GemmArgs{};
+  g.A = dz; g.lda = 2 * F; g.B = v; g.ldb = d; g.Cf = gr->w_gate; g.Cf2 = gr->w_up; g.M1 = F;
+  g.ldc = d; g.M = 2 * F; g.N = d; g.K = (int)Mp;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  // RMSNorm before the FFN: da = dt + dh, dX so far = dy + dh, d g_ffn
+  XMOD_HIP(launch_rms2_bwd((const uint16_t *)dy, map, Xs, a, dv, (const uint16_t *)layer->g_ffn,
+                           eps, dt, d, M, Mp, da, dxacc, part, s));
+  XMOD_HIP(launch_colsum(part, waves, d, tmp, gr->g_ffn, 1.0f, s));
+  // O projection: dO = da W_o, dW_o = da^T O
+  g = GemmArgs{};
+  g.A = da; g.lda = d; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.C = dO; g.ldc = dq;
+  g.M = (int)M; g.N = dq; g.K = d;
+  XMOD_HIP(launch_gemm(g, EPI_STORE, LAY_NN, s));
+  g = GemmArgs{};
+  g.A = da; g.lda = d; g.B = o; g.ldb = dq; g.Cf = gr->w_o; g.ldc = dq;
+  g.M = d; g.N = dq; g.K = (int)Mp;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  // attention
+  XMOD_HIP(launch_attention_bwd(qkv, nqkv, o, dq, lse, dO, dq, D, dqkv, nqkv, dims->B, k, Hq, Hkv,
+                                hd, s));
+  if (zero_pad_rows(dqkv, M, Mp, nqkv, s) != XMOD_OK) return XMOD_ERR_HIP;
+  // QKV projection: du = dqkv W_qkv (into dv's buffer), dW_qkv = dqkv^T u
+  g = GemmArgs{};
+  g.A = dqkv; g.lda = nqkv; g.B = (const uint16_t *)layer->w_qkv; g.ldb = d; g.Cf = dv; g.ldc = d;
+  g.M = (int)M; g.N = d; g.K = nqkv;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_NN, s));
+  g = GemmArgs{};
+  g.A = dqkv; g.lda = nqkv; g.B = u; g.ldb = d; g.Cf = gr->w_qkv; g.ldc = d;
+  g.M = nqkv; g.N = d; g.K = (int)Mp;
+  XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  // RMSNorm before attention: dx of the selected rows, d g_attn, router terms of those rows
+  XMOD_HIP(launch_rms1_bwd(Xs, map, dv, (const uint16_t *)layer->g_attn, eps, dxacc, s_tok, dell,
+                           coef_n, (const uint16_t *)layer->w_router, d, M, (uint16_t *)dx, part,
+                           part + (size_t)waves * d, s));
+  XMOD_HIP(launch_colsum(part, waves, d, tmp, gr->g_attn, 1.0f, s));
+  // router and routing loss over every token: dx of the other rows, d w_r, d beta, L_route
+  XMOD_HIP(launch_route_bwd((const uint16_t *)x, (const uint16_t *)dy, s_tok, dell_tok, q_tok,
+                            coef_n, (const uint16_t *)layer->w_router, d, BT, (uint16_t *)dx, part,
+                            beta_part, loss_part, s));
+  XMOD_HIP(launch_colsum(part, 2 * waves, d, tmp, gr->w_router, 1.0f, s));
+  XMOD_HIP(launch_colsum(beta_part, waves, 1, tmp, gr->router_bias, 1.0f, s));
+  XMOD_HIP(launch_colsum(vs_part, waves, 1, tmp, gr->varsigma, 1.0f, s));
+  if (loss_route)
+    XMOD_HIP(launch_colsum(loss_part, waves, 1, tmp, loss_route, (float)(1.0 / (double)BT), s));
   return XMOD_OK;
 }

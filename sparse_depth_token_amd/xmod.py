@@ -19,6 +19,7 @@ lib = ctypes.CDLL(_LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK, WS_SPARSE_THRESHOLD = 0, 1, 2, 3, 4
 WS_ROUTED_FFN, WS_ATTN_LAYER, WS_SPARSE_FULLKV = 5, 6, 7
+WS_TRAIN_SAVED, WS_BACKWARD = 8, 9
 GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 
 # Every symbol include/xmod.h declares, in declaration order.
@@ -26,7 +27,7 @@ EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", 
             "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_threshold_select",
             "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_routed_ffn_fwd",
             "xmod_attention_layer_fwd", "xmod_sparse_layer_fwd_fullkv", "xmod_dense_layer_fwd",
-            "xmod_block_fwd",
+            "xmod_block_fwd", "xmod_sparse_layer_fwd_train", "xmod_sparse_layer_bwd",
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_gemm_bf16", "xmod_attention_fwd",
             "xmod_attention_fwd_lse", "xmod_attention_bwd",
             "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
@@ -50,6 +51,14 @@ class Layer(ctypes.Structure):
                 ("rope_theta", ctypes.c_float)]
 
 
+GRAD_FIELDS = ("w_router", "router_bias", "varsigma", "g_attn", "w_qkv", "w_o", "g_ffn",
+               "w_gate", "w_up", "w_down")
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
+
+
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _P = ctypes.POINTER
 _sig = {
@@ -58,6 +67,10 @@ _sig = {
     "xmod_topk_from_logits": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _f32, _vp]),
     "xmod_pack": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "xmod_scatter_gated": (_i32, [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_sparse_layer_fwd_train": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp,
+                                           _vp, _vp, _sz, _vp]),
+    "xmod_sparse_layer_bwd": (_i32, [_vp, _vp, _vp, _P(Layer), _P(Dims), _i32, _f32, _vp, _sz,
+                                     _P(Grads), _vp, _vp, _sz, _vp]),
     "xmod_sparse_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp, _vp,
                                      _vp, _sz, _vp]),
     "xmod_threshold_select": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp]),
@@ -173,6 +186,39 @@ def sparse_layer_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_o
                                      _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
                                      _ptr(ws), ws.numel(), _stream(stream)),
            "xmod_sparse_layer_fwd")
+
+
+def make_grads(g: dict) -> Grads:
+    """g: dict of fp32 device tensors named as GRAD_FIELDS (the shapes of the weights;
+    router_bias and varsigma one element each). Keeps a reference to the tensors."""
+    G = Grads(*[_ptr(g[n]) for n in GRAD_FIELDS])
+    G._tensors = dict(g)
+    return G
+
+
+def alloc_grads(dims: Dims, device="cuda") -> dict:
+    d, F = dims.d, dims.ffn_hidden
+    dq, dkv = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    shapes = {"w_router": (d,), "router_bias": (1,), "varsigma": (1,), "g_attn": (d,),
+              "w_qkv": (dq + 2 * dkv, d), "w_o": (d, dq), "g_ffn": (d,), "w_gate": (F, d),
+              "w_up": (F, d), "w_down": (d, F)}
+    return {n: torch.empty(sh, dtype=torch.float32, device=device) for n, sh in shapes.items()}
+
+
+def sparse_layer_fwd_train(x, layer: Layer, dims: Dims, K, bias, tau, delta, saved, idx_out=None,
+                           gate_out=None, stream=None):
+    _check(lib.xmod_sparse_layer_fwd_train(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
+                                           _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
+                                           _ptr(saved), saved.numel(), _stream(stream)),
+           "xmod_sparse_layer_fwd_train")
+
+
+def sparse_layer_bwd(x, dy, dx, layer: Layer, dims: Dims, K, route_coef, saved, grads: Grads,
+                     ws, loss_route=None, stream=None):
+    _check(lib.xmod_sparse_layer_bwd(_ptr(x), _ptr(dy), _ptr(dx), ctypes.byref(layer),
+                                     ctypes.byref(dims), K, route_coef, _ptr(saved), saved.numel(),
+                                     ctypes.byref(grads), _ptr(loss_route), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "xmod_sparse_layer_bwd")
 
 
 def threshold_select(logits, counts, offsets, src, n_total, gate=None, bias=None, delta=0.0,

@@ -20,6 +20,7 @@ import numpy as np
 
 # Tensor ids used in the seed sequence. Never renumber: stored fixtures depend on them.
 T_X, T_BIAS, T_VARSIGMA, T_WR, T_GATTN, T_WQKV, T_WO, T_GFFN, T_WGATE, T_WUP, T_WDOWN, T_SKEW = range(12)
+T_DY = 12
 
 
 @dataclasses.dataclass(frozen=True)
@@ -135,6 +136,13 @@ def make_x(w: Workload, B: int | None = None, T: int | None = None) -> np.ndarra
         vals = bf16_bits_to_f32(flat[rows]) * np.float32(w.skew_mult)
         flat[rows] = f32_to_bf16_bits(vals)
     return x
+
+
+def make_dy(w: Workload, B: int | None = None, T: int | None = None, std: float = 1.0) -> np.ndarray:
+    """Upstream gradient of a layer's output, dy ~ N(0, std^2), as bf16 bits [B, T, d]."""
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    return _normal_bf16(w.seed, 0, T_DY, (B, T, w.d), std)
 
 
 def make_bias(w: Workload, B: int | None = None, T: int | None = None) -> np.ndarray:
