@@ -13,6 +13,7 @@ Prints one JSON line: routed tokens/s, the roofline of the dominant kernel (HIP 
 each kernel of the timed steps), and the CPU oracle timed on a bounded sample on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
+                      [--no-train]
 """
 from __future__ import annotations
 
@@ -111,6 +112,56 @@ def threshold_layer(xmod, w, xb, dl, dims, steps, warmup):
             "timing": "each call on the same input, events around each call"}
 
 
+def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4):
+    """One training step of the same layer: xmod_sparse_layer_fwd_train (the forward that keeps
+    what the backward reads) then xmod_sparse_layer_bwd (gradients of the hidden state and of
+    every parameter, with the routing loss of Eq. (9) at the page's coefficient 1e-4). Each step
+    starts from the same hidden state and bias (restored outside the events). Informational."""
+    import torch
+    L = xmod.make_layer(dl)
+    x0 = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).cuda()
+    b0 = torch.from_numpy(wl.make_bias(w)).cuda()
+    x, bias = x0.clone(), b0.clone()
+    dy = torch.from_numpy(np.ascontiguousarray(wl.make_dy(w)).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    dx = torch.empty_like(dy)
+    saved = xmod.alloc_workspace(dims, w.K, xmod.WS_TRAIN_SAVED)
+    ws = xmod.alloc_workspace(dims, w.K, xmod.WS_BACKWARD)
+    grads = xmod.make_grads(xmod.alloc_grads(dims))
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        x.copy_(x0)
+        bias.copy_(b0)
+        e = ev[i - warmup] if i >= warmup else None
+        if e:
+            e[0].record(stream)
+        xmod.sparse_layer_fwd_train(x, L, dims, w.K, bias, w.tau, w.delta, saved, stream=stream)
+        if e:
+            e[1].record(stream)
+        xmod.sparse_layer_bwd(x, dy, dx, L, dims, w.K, route_coef, saved, grads, ws,
+                              stream=stream)
+        if e:
+            e[2].record(stream)
+    torch.cuda.synchronize()
+    fwd = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
+    bwd = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+    M = w.B * w.k
+    work = algorithmic_work(w)
+    f_fwd = sum(v["flops"] for k2, v in work.items() if k2.endswith(("gemm", "attention")))
+    # backward: two products per projection (input and weight gradients) and five attention
+    # products (S, dP, dV, dK, dQ) for the forward's two
+    f_bwd = 2.0 * sum(v["flops"] for k2, v in work.items() if k2.endswith("gemm")) \
+        + 2.5 * work["attention"]["flops"]
+    return {"fwd_train_ms": round(fwd, 5), "bwd_ms": round(bwd, 5),
+            "routed_tokens_per_s": round(M / ((fwd + bwd) * 1e-3), 1),
+            "bwd_tflops": round(f_bwd / (bwd * 1e-3) / 1e12, 1),
+            "step_frac_mfma_peak": round((f_fwd + f_bwd) / ((fwd + bwd) * 1e-3) / 1e12
+                                         / PEAK_BF16_TFLOPS, 4),
+            "route_coef": route_coef,
+            "timing": "each step on the same input, events around the forward and the backward"}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle (float64 NumPy) on a bounded sample of the same workload on this host."""
     import oracle
@@ -147,6 +198,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-threshold", action="store_true",
                     help="skip the informational threshold-routing line")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the informational training-step (forward + backward) object")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -251,6 +304,8 @@ def main():
     }
     if not args.no_threshold:
         out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup)
+    if not args.no_train:
+        out["train_step"] = train_step(xmod, w, xb, dl, dims, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
