@@ -9,8 +9,12 @@ with the gated scatter back into x). Inputs are resident in HBM before timing st
 updates x and the carried bias in place, so consecutive steps act like a stack of layers that
 share weights (same shapes, same work per step).
 
-Prints one JSON line: routed tokens/s, the roofline of the dominant kernel (HIP events around
-each kernel of the timed steps), and the CPU oracle timed on a bounded sample on this host.
+Before the W warm-up steps, untimed steps run for at least 0.2 s so that the clocks settle.
+Prints one JSON line: routed tokens/s over the K timed steps; the roofline of the dominant
+kernel (the gate/up GEMM), timed by HIP events the library records around that kernel in every
+timed step (two events per step); a per-kernel breakdown from K further steps with events
+around every kernel; informational lines for the eval-time threshold rule and one training
+step (forward + backward); and the CPU oracle timed on a bounded sample on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
                       [--no-train]
@@ -240,12 +244,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # device warm-up: untimed steps for at least 0.2 s (clocks settle), then the W warm-up steps
+    t_end = time.perf_counter() + 0.2
+    for _ in range(400):
+        step()
+        torch.cuda.synchronize()
+        if time.perf_counter() > t_end:
+            break
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-kernel events recorded by the library on the same stream
-    xmod.phase_timing(True)
+    work = algorithmic_work(w)
+    # the dominant kernel: the largest algorithmic work (the gate/up GEMM with SwiGLU)
+    dom = max(work, key=lambda n: work[n]["flops"])
+
+    # timed region: K steps; the library brackets the dominant kernel with events on the same
+    # stream (two events per step)
+    xmod.phase_timing(True, slots=[dom])
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -254,7 +270,7 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    phase_ms, n_calls = xmod.phase_times()
+    dom_ms, n_calls = xmod.phase_times()
     xmod.phase_timing(False)
     assert n_calls == args.steps
     assert torch.isfinite(x.float()).all().item(), "non-finite hidden state"
@@ -263,7 +279,13 @@ def main():
     M = w.B * w.k
     value = M / (ms_per_step * 1e-3)
 
-    work = algorithmic_work(w)
+    # per-kernel breakdown: K more steps with events around every kernel (not the timed region)
+    xmod.phase_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    phase_ms, _ = xmod.phase_times()
+    xmod.phase_timing(False)
     phases = {}
     for name, ms in phase_ms.items():
         avg = ms / args.steps
@@ -275,8 +297,7 @@ def main():
             e["gbs"] = round(work[name]["bytes"] / (avg * 1e-3) / 1e9, 1)
             e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
         phases[name] = e
-    dom = max(phase_ms, key=phase_ms.get)
-    dom_avg_s = phase_ms[dom] / args.steps * 1e-3
+    dom_avg_s = dom_ms[dom] / args.steps * 1e-3
     if dom.endswith(("gemm", "attention")):
         achieved = work[dom]["flops"] / dom_avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),

@@ -348,14 +348,18 @@ xmod_status xmod_attention_bwd(const void *qkv, int32_t ld_qkv, const void *o, i
 
 /* --- Measurement hook. ------------------------------------------------------------------------
  * While enabled, the layer and block entry points record a hipEvent on their stream before
- * their first kernel and after every kernel they launch (events are created on first use and
- * kept). xmod_phase_times() waits for the last recorded event, adds the time between
- * consecutive events of every recorded call into ms[i] for kernel slot i (sparse layer slots:
+ * their first kernel and after every kernel they launch (events are created on first use, kept,
+ * and record no system-scope fence); xmod_phase_timing_slots(mask) limits the recording to the
+ * two ends of the kernel slots whose bit is set (default: every slot), so that a timed run pays
+ * for two events per call instead of one per kernel. xmod_phase_times() waits for the last
+ * recorded event, adds the time between the two events around each recorded kernel of every
+ * recorded call into ms[i] for kernel slot i (sparse layer slots:
  * 0 router, 1 top-k, 2 gather+RMSNorm, 3 QKV GEMM, 4 attention, 5 O GEMM, 6 residual+RMSNorm,
  * 7 gate/up GEMM with SwiGLU, 8 down GEMM with gated scatter; a dense layer fills slots 2-8),
  * stores the number of recorded calls in *n_calls, and forgets the recorded events.
  * Not thread safe; meant for benchmarks, not for production calls or graph capture. */
 void xmod_phase_timing_enable(int32_t on);
+void xmod_phase_timing_slots(uint32_t mask);
 xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls);
 
 const char *xmod_status_string(xmod_status st);

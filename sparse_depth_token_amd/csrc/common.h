@@ -200,9 +200,14 @@ hipError_t launch_attention_bwd(const uint16_t *qkv, int ld_qkv, const uint16_t 
 // ---- backward row kernels (rows_bwd.hip) ----
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);          // bytes / 16 chunks
 hipError_t launch_copy32(void *dst, const void *src, int64_t n_words, hipStream_t s);
-int bwd_row_waves();  // waves of the row kernels = per-wave partial rows they write
-hipError_t launch_colsum(const float *part, int n_part, int n, float *tmp, float *out,
-                         float scale, hipStream_t s);  // tmp: 16 * n floats
+int bwd_row_wgs();    // workgroups (= partial rows written) of the packed-row kernels
+int bwd_route_wgs();  // workgroups (= partial rows written) of the every-token router kernel
+// out[c] = scale * sum over p < n_part of part[p * n + c], in a fixed order; tmp: 16 * n floats.
+struct ColsumJob {
+  const float *part; int n_part; int n; float *out; float scale; float *tmp; int blk0;
+};
+struct ColsumJobs { ColsumJob job[6]; int n; };
+hipError_t launch_colsum_multi(ColsumJobs jobs, hipStream_t s);
 hipError_t launch_resid_bwd(const uint16_t *dy, const RowMap &map, const float *a, const float *f,
                             const float *gate, float varsigma, int d, int64_t M, int64_t M_pad,
                             uint16_t *dt, float *dell, float *dell_tok, uint8_t *q_tok,

@@ -19,9 +19,10 @@
 // unselected token from x (in the router kernel).
 //
 // One wave per row, 8 columns per lane per 512-column step. Column sums (gain and router-weight
-// gradients) and scalar sums are accumulated per lane over the rows a wave visits and written
-// as per-wave partial sums, which colsum adds in a fixed order: results do not depend on
-// scheduling.
+// gradients) and scalar sums are accumulated per lane over the rows a wave visits, added over
+// the workgroup's four waves in LDS and written as one partial row per workgroup; a final
+// two-level sum adds the partial rows. Every sum runs in a fixed order, so the results do not
+// depend on scheduling.
 #include "common.h"
 
 namespace xmod {
@@ -41,6 +42,36 @@ __device__ __forceinline__ void store8f(float *p, const float *f) {
 // log(1 + e^z) without overflow or cancellation
 __device__ __forceinline__ float softplus(float z) {
   return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+}
+
+// Sum of the four waves' per-lane column accumulators (columns 8 c + e for chunk c = lane +
+// 64 i), in wave order, through LDS; the workgroup's partial row goes to dst[0, d).
+template <int NI>
+__device__ __forceinline__ void wg_colsum_store(const float (&acc)[NI][8], float *red, int d,
+                                                float *__restrict__ dst) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nch = d >> 3;
+  __syncthreads();  // a previous use of `red` is complete
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    if (w == step) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) red[c * 8 + e] = (step == 0 ? 0.f : red[c * 8 + e]) + acc[i][e];
+      }
+    }
+    __syncthreads();
+  }
+  for (int c = threadIdx.x; c < d; c += 256) dst[c] = red[c];
+}
+// The same for one number per wave (lane 0's value).
+__device__ __forceinline__ void wg_sum_store(float v, float *red4, float *dst) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red4[w] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) *dst = ((red4[0] + red4[1]) + red4[2]) + red4[3];
 }
 
 __global__ __launch_bounds__(256) void zero16_kernel(uint4 *__restrict__ p, int64_t n16) {
@@ -71,6 +102,11 @@ hipError_t launch_copy32(void *dst, const void *src, int64_t n_words, hipStream_
                      (uint32_t *)dst, (const uint32_t *)src, n_words);
   return hipGetLastError();
 }
+
+// Workgroups of the row kernels over the packed rows and over every token; each writes one
+// partial row of its column sums.
+constexpr int BWD_ROW_WGS = 512;
+constexpr int BWD_ROUTE_WGS = 1024;
 
 // ---- gated residual ------------------------------------------------------------------------
 template <int NI>
@@ -120,7 +156,8 @@ __global__ __launch_bounds__(256) void resid_bwd_kernel(
       vs_acc = fmaf(r, dc, vs_acc);
     }
   }
-  if (lane == 0) vs_part[wave] = vs_acc;
+  __shared__ float red4[4];
+  wg_sum_store(vs_acc, red4, vs_part + blockIdx.x);
 }
 
 // ---- RMSNorm before the FFN ------------------------------------------------------------------
@@ -196,11 +233,8 @@ __global__ __launch_bounds__(256) void rms2_bwd_kernel(
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) store8f(g_part + (int64_t)wave * d + (size_t)c * 8, gacc[i]);
-  }
+  __shared__ float red[NI * 512];
+  wg_colsum_store<NI>(gacc, red, d, g_part + (int64_t)blockIdx.x * d);
 }
 
 // ---- RMSNorm before attention; writes the selected rows of dx ---------------------------------
@@ -267,14 +301,9 @@ __global__ __launch_bounds__(256) void rms1_bwd_kernel(
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) {
-      store8f(g_part + (int64_t)wave * d + (size_t)c * 8, gacc[i]);
-      store8f(wr_part + (int64_t)wave * d + (size_t)c * 8, wacc[i]);
-    }
-  }
+  __shared__ float red[NI * 512];
+  wg_colsum_store<NI>(gacc, red, d, g_part + (int64_t)blockIdx.x * d);
+  wg_colsum_store<NI>(wacc, red, d, wr_part + (int64_t)blockIdx.x * d);
 }
 
 // ---- router and routing loss over every token; writes the unselected rows of dx --------------
@@ -300,76 +329,108 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(
     }
   }
   float bacc = 0.f, lacc = 0.f;
-  for (int64_t t = wave; t < rows; t += (int64_t)gridDim.x * 4) {
-    const float sv = s_tok[t];
-    const bool q = q_tok[t] != 0;
-    const float p = 1.0f / (1.0f + expf(-sv));
-    const float ds = dell_tok[t] + coef_n * (p - (q ? 1.0f : 0.0f));
-    // -log p = softplus(-s), -log(1 - p) = softplus(s)
-    lacc += q ? softplus(-sv) : softplus(sv);
-    bacc += ds;
-    if (q) continue;  // a selected row: its dx and router-weight term come from the saved X
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  // two rows per step, their loads issued together
+  for (int64_t t0 = wave; t0 < rows; t0 += 2 * stride) {
+    int64_t tt[2] = {t0, t0 + stride};
+    float ds[2];
+    bool sel[2];
+    uint4 xv[2][NI], gv[2][NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nch) {
-        float Xf[8], G[8], o[8];
-        unpack8(*(const uint4 *)(x + t * d + (size_t)c * 8), Xf);
-        unpack8(*(const uint4 *)(dy + t * d + (size_t)c * 8), G);
+    for (int r = 0; r < 2; ++r) {
+      const bool ok = tt[r] < rows;
+      const int64_t t = ok ? tt[r] : t0;
+      const float sv = s_tok[t];
+      const bool q = q_tok[t] != 0;
+      const float p = 1.0f / (1.0f + expf(-sv));
+      ds[r] = dell_tok[t] + coef_n * (p - (q ? 1.0f : 0.0f));
+      sel[r] = q || !ok;  // nothing to write (a selected row's dx and router-weight term come
+                          // from the saved X)
+      if (ok) {
+        // -log p = softplus(-s), -log(1 - p) = softplus(s)
+        lacc += q ? softplus(-sv) : softplus(sv);
+        bacc += ds[r];
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          wacc[i][e] = fmaf(ds, Xf[e], wacc[i][e]);
-          o[e] = G[e] + ds * wr[i][e];
+      for (int i = 0; i < NI; ++i) {
+        const int c = lane + 64 * i;
+        xv[r][i] = gv[r][i] = make_uint4(0, 0, 0, 0);
+        if (c < nch && !sel[r]) {
+          xv[r][i] = *(const uint4 *)(x + t * d + (size_t)c * 8);
+          gv[r][i] = *(const uint4 *)(dy + t * d + (size_t)c * 8);
         }
-        *(uint4 *)(dx + t * d + (size_t)c * 8) = pack8(o);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (sel[r]) continue;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+          float Xf[8], G[8], o[8];
+          unpack8(xv[r][i], Xf);
+          unpack8(gv[r][i], G);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            wacc[i][e] = fmaf(ds[r], Xf[e], wacc[i][e]);
+            o[e] = G[e] + ds[r] * wr[i][e];
+          }
+          *(uint4 *)(dx + tt[r] * d + (size_t)c * 8) = pack8(o);
+        }
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nch) store8f(wr_part + (int64_t)wave * d + (size_t)c * 8, wacc[i]);
-  }
-  if (lane == 0) {
-    beta_part[wave] = bacc;
-    loss_part[wave] = lacc;
-  }
+  __shared__ float red[NI * 512];
+  __shared__ float red4[4];
+  wg_colsum_store<NI>(wacc, red, d, wr_part + (int64_t)blockIdx.x * d);
+  wg_sum_store(bacc, red4, beta_part + blockIdx.x);
+  __syncthreads();
+  wg_sum_store(lacc, red4, loss_part + blockIdx.x);
 }
 
 // ---- fixed-order sums of partial rows --------------------------------------------------------
-// out[c] = scale * sum over p in this chunk of part[p * n + c]; a workgroup takes 64 columns and
-// one chunk of partial rows, its four waves every fourth row, combined in LDS.
-__global__ __launch_bounds__(256) void colsum_kernel(const float *__restrict__ part, int n_part,
-                                                     int n, int chunk, float scale,
-                                                     float *__restrict__ out) {
-  __shared__ float sh[4][64];
-  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + lane;
-  const int p0 = blockIdx.y * chunk, p1 = min(p0 + chunk, n_part);
-  float acc = 0.f;
-  if (c < n)
-    for (int p = p0 + grp; p < p1; p += 4) acc += part[(int64_t)p * n + c];
-  sh[grp][lane] = acc;
-  __syncthreads();
-  if (grp == 0 && c < n)
-    out[(int64_t)blockIdx.y * n + c] = scale * (((sh[0][lane] + sh[1][lane]) + sh[2][lane]) + sh[3][lane]);
-}
-
-constexpr int BWD_ROW_WGS = 256;            // workgroups of the row kernels
+// Level 0: job j's partial rows are split in COLSUM_CHUNKS chunks; workgroup (column block,
+// chunk) sums its chunk for 64 columns (four waves take every fourth row, combined in LDS) into
+// tmp_j[chunk][c]. Level 1 sums the chunks: out_j[c] = scale_j * sum over chunks.
 constexpr int COLSUM_CHUNKS = 16;
 
-hipError_t launch_colsum(const float *part, int n_part, int n, float *tmp, float *out,
-                         float scale, hipStream_t s) {
-  const unsigned gx = (unsigned)((n + 63) / 64);
-  const int chunk = (n_part + COLSUM_CHUNKS - 1) / COLSUM_CHUNKS;
-  hipLaunchKernelGGL(colsum_kernel, dim3(gx, COLSUM_CHUNKS), dim3(256), 0, s, part, n_part, n,
-                     chunk, 1.0f, tmp);
-  hipLaunchKernelGGL(colsum_kernel, dim3(gx, 1), dim3(256), 0, s, tmp, COLSUM_CHUNKS, n,
-                     COLSUM_CHUNKS, scale, out);
+__global__ __launch_bounds__(256) void colsum_multi_kernel(ColsumJobs J, int level) {
+  __shared__ float sh[4][64];
+  int j = 0;
+  while (j + 1 < J.n && (int)blockIdx.x >= J.job[j + 1].blk0) ++j;
+  const ColsumJob &b = J.job[j];
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int c = ((int)blockIdx.x - b.blk0) * 64 + lane;
+  const float *part = level == 0 ? b.part : b.tmp;
+  const int n_part = level == 0 ? b.n_part : COLSUM_CHUNKS;
+  const int chunk = level == 0 ? (b.n_part + COLSUM_CHUNKS - 1) / COLSUM_CHUNKS : COLSUM_CHUNKS;
+  const int p0 = blockIdx.y * chunk, p1 = min(p0 + chunk, n_part);
+  float acc = 0.f;
+  if (c < b.n)
+    for (int p = p0 + grp; p < p1; p += 4) acc += part[(int64_t)p * b.n + c];
+  sh[grp][lane] = acc;
+  __syncthreads();
+  if (grp == 0 && c < b.n) {
+    const float v = ((sh[0][lane] + sh[1][lane]) + sh[2][lane]) + sh[3][lane];
+    if (level == 0) b.tmp[(int64_t)blockIdx.y * b.n + c] = v;
+    else b.out[c] = b.scale * v;
+  }
+}
+
+hipError_t launch_colsum_multi(ColsumJobs J, hipStream_t s) {
+  int blocks = 0;
+  for (int j = 0; j < J.n; ++j) {
+    J.job[j].blk0 = blocks;
+    blocks += (J.job[j].n + 63) / 64;
+  }
+  hipLaunchKernelGGL(colsum_multi_kernel, dim3(blocks, COLSUM_CHUNKS), dim3(256), 0, s, J, 0);
+  hipLaunchKernelGGL(colsum_multi_kernel, dim3(blocks, 1), dim3(256), 0, s, J, 1);
   return hipGetLastError();
 }
 
-int bwd_row_waves() { return BWD_ROW_WGS * 4; }
+int bwd_row_wgs() { return BWD_ROW_WGS; }
+int bwd_route_wgs() { return BWD_ROUTE_WGS; }
 
 static int ni_of(int d) { return ((d >> 3) + 63) / 64; }
 
@@ -426,7 +487,7 @@ hipError_t launch_route_bwd(const uint16_t *x, const uint16_t *dy, const float *
                             const uint16_t *w_r, int d, int64_t rows, uint16_t *dx,
                             float *wr_part, float *beta_part, float *loss_part, hipStream_t s) {
 #define L_(NI)                                                                                \
-  hipLaunchKernelGGL((route_bwd_kernel<NI>), dim3(BWD_ROW_WGS), dim3(256), 0, s, x, dy, s_tok, \
+  hipLaunchKernelGGL((route_bwd_kernel<NI>), dim3(BWD_ROUTE_WGS), dim3(256), 0, s, x, dy, s_tok, \
                      dell_tok, q_tok, coef_n, w_r, d, rows, dx, wr_part, beta_part, loss_part)
   XMOD_BWD_NI_SWITCH(ni_of(d), L_)
 #undef L_

@@ -25,10 +25,16 @@ thread_local int32_t g_last_hip = 0;
   } while (0)
 
 // ---- measurement hook: events between kernels (see xmod_phase_timing_enable) ----
+// Boundary b of a call lies after kernel slot first_slot + b - 1 and before slot first_slot + b;
+// an event is recorded there when either neighbouring slot is selected by the mask.
 constexpr int kSlots = 9;
-struct PhaseCall { size_t first; int first_slot; int n; };
+struct PhaseCall {
+  int first_slot = 0, n_bound = 0;
+  std::vector<std::pair<int, size_t>> ev;  // (boundary, event index)
+};
 struct PhaseLog {
   bool on = false;
+  uint32_t mask = 0xFFFFFFFFu;
   std::vector<hipEvent_t> pool;
   size_t used = 0;
   std::vector<PhaseCall> calls;
@@ -36,19 +42,25 @@ struct PhaseLog {
 PhaseLog g_phase;
 
 void phase_mark(hipStream_t s) {
-  if (!g_phase.on) return;
+  if (!g_phase.on || g_phase.calls.empty()) return;
+  PhaseCall &c = g_phase.calls.back();
+  const int b = c.n_bound++;
+  auto sel = [](int slot) { return slot >= 0 && slot < 32 && ((g_phase.mask >> slot) & 1u); };
+  if (!sel(c.first_slot + b - 1) && !sel(c.first_slot + b)) return;
   if (g_phase.used == g_phase.pool.size()) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
+    // timing only: no system-scope fence (its cache write-back would stall the next kernel)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return;
     g_phase.pool.push_back(e);
   }
   if (hipEventRecord(g_phase.pool[g_phase.used], s) != hipSuccess) return;
+  c.ev.emplace_back(b, g_phase.used);
   ++g_phase.used;
-  if (!g_phase.calls.empty()) ++g_phase.calls.back().n;
 }
 void phase_begin(hipStream_t s, int first_slot) {
   if (!g_phase.on) return;
-  g_phase.calls.push_back(PhaseCall{g_phase.used, first_slot, 0});
+  g_phase.calls.emplace_back();
+  g_phase.calls.back().first_slot = first_slot;
   phase_mark(s);
 }
 
@@ -560,16 +572,20 @@ void xmod_phase_timing_enable(int32_t on) {
   g_phase.calls.clear();
 }
 
+void xmod_phase_timing_slots(uint32_t mask) { g_phase.mask = mask; }
+
 xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls) {
   if (!ms || n_slots < 1) return XMOD_ERR_INVALID_ARG;
   for (int i = 0; i < n_slots; ++i) ms[i] = 0.f;
   if (n_calls) *n_calls = (int32_t)g_phase.calls.size();
   if (g_phase.used > 0) XMOD_HIP(hipEventSynchronize(g_phase.pool[g_phase.used - 1]));
   for (const PhaseCall &c : g_phase.calls) {
-    for (int i = 1; i < c.n; ++i) {
-      const int slot = c.first_slot + i - 1;
+    for (size_t i = 1; i < c.ev.size(); ++i) {
+      if (c.ev[i].first != c.ev[i - 1].first + 1) continue;  // not the two ends of one slot
+      const int slot = c.first_slot + c.ev[i - 1].first;
       float t = 0.f;
-      XMOD_HIP(hipEventElapsedTime(&t, g_phase.pool[c.first + i - 1], g_phase.pool[c.first + i]));
+      XMOD_HIP(hipEventElapsedTime(&t, g_phase.pool[c.ev[i - 1].second],
+                                   g_phase.pool[c.ev[i].second]));
       if (slot < n_slots) ms[slot] += t;
     }
   }
@@ -836,7 +852,8 @@ PlanTrain plan_train(const xmod_dims *dm, int64_t M) {
 
 struct PlanBwd {
   size_t dt = 0, dz = 0, dv = 0, da = 0, dxacc = 0, dO = 0, D = 0, dqkv = 0, dell = 0;
-  size_t dell_tok = 0, q_tok = 0, part = 0, spart = 0, tmp = 0, total = 0;
+  size_t dell_tok = 0, q_tok = 0, part_g2 = 0, part_g1 = 0, part_wr = 0, spart = 0, tmp = 0;
+  size_t total = 0;
 };
 
 PlanBwd plan_bwd(const xmod_dims *dm, int64_t M) {
@@ -846,7 +863,7 @@ PlanBwd plan_bwd(const xmod_dims *dm, int64_t M) {
   const int64_t BT = (int64_t)dm->B * dm->T, Mp = pad_rows(M), d = dm->d, F = dm->ffn_hidden;
   const int64_t dq = (int64_t)dm->n_q_heads * dm->head_dim;
   const int64_t nqkv = dq + 2LL * dm->n_kv_heads * dm->head_dim;
-  const int64_t waves = bwd_row_waves();
+  const int64_t R = bwd_row_wgs(), RT = bwd_route_wgs();
   p.dt = take(Mp * d * 2);
   p.dz = take(Mp * 2 * F * 2);
   p.dv = take(M * d * 4);       // dv, later du
@@ -856,11 +873,13 @@ PlanBwd plan_bwd(const xmod_dims *dm, int64_t M) {
   p.D = take(M * dm->n_q_heads * 4);
   p.dqkv = take(Mp * nqkv * 2);
   p.dell = take(M * 4);
-  p.dell_tok = take(BT * 4);
+  p.dell_tok = take(BT * 4);   // dell_tok and q_tok are adjacent: one zero fill
   p.q_tok = take(BT);
-  p.part = take(2 * waves * d * 4);
-  p.spart = take(3 * waves * 4);
-  p.tmp = take(16 * d * 4);
+  p.part_g2 = take(R * d * 4);
+  p.part_g1 = take(R * d * 4);
+  p.part_wr = take((R + RT) * d * 4);
+  p.spart = take((R + 2 * RT) * 4);
+  p.tmp = take(16 * (3 * d + 3) * 4);
   p.total = off;
   return p;
 }
@@ -969,7 +988,7 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   const int hd = dims->head_dim, dq = Hq * hd, nqkv = dq + 2 * Hkv * hd;
   const float eps = dims->rms_eps;
   const float coef_n = (float)((double)route_coef / (double)BT);
-  const int waves = bwd_row_waves();
+  const int R = bwd_row_wgs(), RT = bwd_route_wgs();
   // saved by the forward
   const float *s_tok = at<float>(sv_, p.s), *gate = at<float>(sv_, p.gate);
   const int32_t *idx = at<int32_t>(sv_, p.idx);
@@ -984,13 +1003,14 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   float *dv = at<float>(ws, q.dv), *dxacc = at<float>(ws, q.dxacc), *D = at<float>(ws, q.D);
   float *dell = at<float>(ws, q.dell), *dell_tok = at<float>(ws, q.dell_tok);
   uint8_t *q_tok = at<uint8_t>(ws, q.q_tok);
-  float *part = at<float>(ws, q.part), *spart = at<float>(ws, q.spart), *tmp = at<float>(ws, q.tmp);
-  float *vs_part = spart, *beta_part = spart + waves, *loss_part = spart + 2 * waves;
+  float *part_g2 = at<float>(ws, q.part_g2), *part_g1 = at<float>(ws, q.part_g1);
+  float *part_wr = at<float>(ws, q.part_wr), *spart = at<float>(ws, q.spart);
+  float *tmp = at<float>(ws, q.tmp);
+  float *vs_part = spart, *beta_part = spart + R, *loss_part = spart + R + RT;
   const RowMap map = topk_map(idx, dims, k);
 
   // gated residual: dt, the gate's gradient, d varsigma partials; selection marks per token
-  XMOD_HIP(launch_zero(dell_tok, align_up((size_t)BT * 4), s));
-  XMOD_HIP(launch_zero(q_tok, align_up((size_t)BT), s));
+  XMOD_HIP(launch_zero(dell_tok, align_up((size_t)BT * 4) + align_up((size_t)BT), s));
   XMOD_HIP(launch_resid_bwd((const uint16_t *)dy, map, a, f, gate, layer->varsigma, d, M, Mp, dt,
                             dell, dell_tok, q_tok, vs_part, s));
   // FFN: dg = dt W_down (SwiGLU backward in the epilogue), dW_down = dt^T g
@@ -1014,8 +1034,7 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
   // RMSNorm before the FFN: da = dt + dh, dX so far = dy + dh, d g_ffn
   XMOD_HIP(launch_rms2_bwd((const uint16_t *)dy, map, Xs, a, dv, (const uint16_t *)layer->g_ffn,
-                           eps, dt, d, M, Mp, da, dxacc, part, s));
-  XMOD_HIP(launch_colsum(part, waves, d, tmp, gr->g_ffn, 1.0f, s));
+                           eps, dt, d, M, Mp, da, dxacc, part_g2, s));
   // O projection: dO = da W_o, dW_o = da^T O
   g = GemmArgs{};
   g.A = da; g.lda = d; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.C = dO; g.ldc = dq;
@@ -1040,17 +1059,26 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
   // RMSNorm before attention: dx of the selected rows, d g_attn, router terms of those rows
   XMOD_HIP(launch_rms1_bwd(Xs, map, dv, (const uint16_t *)layer->g_attn, eps, dxacc, s_tok, dell,
-                           coef_n, (const uint16_t *)layer->w_router, d, M, (uint16_t *)dx, part,
-                           part + (size_t)waves * d, s));
-  XMOD_HIP(launch_colsum(part, waves, d, tmp, gr->g_attn, 1.0f, s));
+                           coef_n, (const uint16_t *)layer->w_router, d, M, (uint16_t *)dx,
+                           part_g1, part_wr, s));
   // router and routing loss over every token: dx of the other rows, d w_r, d beta, L_route
   XMOD_HIP(launch_route_bwd((const uint16_t *)x, (const uint16_t *)dy, s_tok, dell_tok, q_tok,
-                            coef_n, (const uint16_t *)layer->w_router, d, BT, (uint16_t *)dx, part,
-                            beta_part, loss_part, s));
-  XMOD_HIP(launch_colsum(part, 2 * waves, d, tmp, gr->w_router, 1.0f, s));
-  XMOD_HIP(launch_colsum(beta_part, waves, 1, tmp, gr->router_bias, 1.0f, s));
-  XMOD_HIP(launch_colsum(vs_part, waves, 1, tmp, gr->varsigma, 1.0f, s));
-  if (loss_route)
-    XMOD_HIP(launch_colsum(loss_part, waves, 1, tmp, loss_route, (float)(1.0 / (double)BT), s));
+                            coef_n, (const uint16_t *)layer->w_router, d, BT, (uint16_t *)dx,
+                            part_wr + (size_t)R * d, beta_part, loss_part, s));
+  // every column and scalar sum of partial rows, in one pair of launches
+  ColsumJobs J{};
+  auto job = [&](const float *part, int n_part, int n, float *out, float scale) {
+    ColsumJob &j = J.job[J.n];
+    j.part = part; j.n_part = n_part; j.n = n; j.out = out; j.scale = scale;
+    j.tmp = tmp + (size_t)16 * (J.n < 3 ? J.n * d : 3 * d + (J.n - 3));
+    ++J.n;
+  };
+  job(part_g2, R, d, gr->g_ffn, 1.0f);
+  job(part_g1, R, d, gr->g_attn, 1.0f);
+  job(part_wr, R + RT, d, gr->w_router, 1.0f);
+  job(beta_part, RT, 1, gr->router_bias, 1.0f);
+  job(vs_part, R, 1, gr->varsigma, 1.0f);
+  if (loss_route) job(loss_part, RT, 1, loss_route, (float)(1.0 / (double)BT));
+  XMOD_HIP(launch_colsum_multi(J, s));
   return XMOD_OK;
 }

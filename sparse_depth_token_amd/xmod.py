@@ -30,7 +30,8 @@ EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", 
             "xmod_block_fwd", "xmod_sparse_layer_fwd_train", "xmod_sparse_layer_bwd",
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_gemm_bf16", "xmod_attention_fwd",
             "xmod_attention_fwd_lse", "xmod_attention_bwd",
-            "xmod_phase_timing_enable", "xmod_phase_times", "xmod_status_string",
+            "xmod_phase_timing_enable", "xmod_phase_timing_slots", "xmod_phase_times",
+            "xmod_status_string",
             "xmod_last_hip_error"]
 
 
@@ -95,6 +96,7 @@ _sig = {
                               _vp]),
     "xmod_attention_fwd": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "xmod_phase_timing_enable": (None, [_i32]),
+    "xmod_phase_timing_slots": (None, [ctypes.c_uint32]),
     "xmod_phase_times": (_i32, [_P(_f32), _i32, _P(_i32)]),
     "xmod_status_string": (ctypes.c_char_p, [_i32]),
     "xmod_last_hip_error": (_i32, []),
@@ -323,7 +325,11 @@ PHASES = ["router", "topk", "gather_rmsnorm", "qkv_gemm", "attention", "o_gemm",
           "residual_rmsnorm", "gateup_swiglu_gemm", "down_scatter_gemm"]
 
 
-def phase_timing(on: bool):
+def phase_timing(on: bool, slots=None):
+    """Enable / disable the per-kernel events; slots: names (PHASES) of the kernels to bracket
+    with events, None for every kernel."""
+    mask = 0xFFFFFFFF if slots is None else sum(1 << PHASES.index(n) for n in slots)
+    lib.xmod_phase_timing_slots(mask)
     lib.xmod_phase_timing_enable(1 if on else 0)
 
 
