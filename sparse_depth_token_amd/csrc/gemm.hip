@@ -43,15 +43,18 @@ __device__ __forceinline__ void dma16(const void *gsrc, uint16_t *lds_block) {
                                    0, 0);
 }
 
-// Physical 16-byte chunk index of logical chunk c in LDS row r (rows of BK bf16).
-//  BK = 64 (8 chunks): c ^ ((r ^ (r >> 3)) & 7) - 16 consecutive rows reading one logical chunk
-//    land in distinct 4-bank groups (128-byte rows: even/odd rows cover the two 32-bank halves).
-//  BK = 32 (4 chunks): c ^ (((r >> 1) ^ (r >> 3)) & 3) - rows r..r+15 map to distinct
-//    (r % 4, chunk) pairs, i.e. distinct banks, and any aligned 8 rows to distinct 32-bank slots.
+// Physical 16-byte chunk index of logical chunk c in LDS row r (rows of BK bf16), for the
+// fragment read (32 consecutive rows, one logical chunk per half-wave). Both forms were measured
+// free of bank conflicts on gfx950 with that exact pattern (SQ_LDS_BANK_CONFLICT = 0), which
+// other candidates are not (64-byte rows swizzled by ((r >> 1) ^ (r >> 3)) & 3: two-way).
+//  BK = 64 (8 chunks, 128-byte rows): c ^ ((r ^ (r >> 3)) & 7).
+//  BK = 32 (4 chunks, 64-byte rows): c ^ ((r >> 2) & 3).
+// Neither depends on the row's 32-row block, so a fragment's chunk offsets are the same for
+// every 32-row block of a wave's tile (BK = 64: up to the XOR with 4i & 7).
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
   if (BK == 64) return (r ^ (r >> 3)) & 7;
-  return ((r >> 1) ^ (r >> 3)) & 3;
+  return (r >> 2) & 3;
 }
 
 // Physical 16-byte chunk of logical chunk c in k-row r of a k-major tile (rows of at least 16
