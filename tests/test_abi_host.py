@@ -154,3 +154,69 @@ def test_threshold_entry_points_reject_before_launch(x):
     assert h(FAKE, FAKE, 2, 10, 11, FAKE, None) == x.ERR_INVALID_ARG
     assert h(FAKE, FAKE, 2, 10, 5, None, None) == x.ERR_INVALID_ARG
     assert h(FAKE, FAKE, 1, 70000, 5, FAKE, None) == x.ERR_UNSUPPORTED
+
+
+def test_training_entry_points_reject_before_launch(x):
+    L = x.lib
+    dm = _dims(x)
+    saved = x.workspace_bytes(dm, 8, x.WS_TRAIN_SAVED)
+    bwd = x.workspace_bytes(dm, 8, x.WS_BACKWARD)
+    # the saved activations hold at least X, u, QKV, O, v, g, z = [zg | zu] (bf16), a and f
+    # (fp32) of the 4096 routed rows
+    M = 8 * 512
+    assert saved >= M * (2048 * 2 * 3 + 6144 * 2 + 2048 * 2 + 5632 * 2 * 3 + 2048 * 4 * 2)
+    assert bwd > 0
+    assert x.workspace_bytes(dm, 0, x.WS_TRAIN_SAVED) == 0
+    lay = _layer(x)
+    f = L.xmod_sparse_layer_fwd_train
+    args = lambda **o: [o.get("x", FAKE), ctypes.byref(o.get("L", lay)),
+                        ctypes.byref(o.get("dm", dm)), o.get("K", 8), None, 1.0, 0.05, None, None,
+                        o.get("saved", FAKE), o.get("sb", saved), None]
+    assert f(*args(K=0)) == x.ERR_INVALID_ARG
+    assert f(*args(x=None)) == x.ERR_INVALID_ARG
+    assert f(*args(sb=saved - 1)) == x.ERR_WORKSPACE
+    assert f(*args(saved=None)) == x.ERR_WORKSPACE
+    for field, val in (("residual", 1), ("rope_theta", 1e4)):
+        other = _layer(x)
+        setattr(other, field, val)
+        assert f(*args(L=other)) == x.ERR_UNSUPPORTED, field
+    qn = _layer(x)
+    qn.q_norm = FAKE
+    assert f(*args(L=qn)) == x.ERR_UNSUPPORTED
+    g = L.xmod_sparse_layer_bwd
+    G = x.Grads(*[FAKE] * len(x.GRAD_FIELDS))
+    bargs = lambda **o: [FAKE, o.get("dy", FAKE), FAKE, ctypes.byref(o.get("L", lay)),
+                         ctypes.byref(dm), 8, o.get("coef", 1e-4), FAKE, o.get("sb", saved),
+                         ctypes.byref(o.get("G", G)), None, FAKE, o.get("wsb", bwd), None]
+    assert g(*bargs(dy=None)) == x.ERR_INVALID_ARG
+    assert g(*bargs(coef=float("nan"))) == x.ERR_INVALID_ARG
+    assert g(*bargs(sb=saved - 1)) == x.ERR_WORKSPACE
+    assert g(*bargs(wsb=bwd - 1)) == x.ERR_WORKSPACE
+    nog = x.Grads(*[FAKE] * len(x.GRAD_FIELDS))
+    nog.w_o = None
+    assert g(*bargs(G=nog)) == x.ERR_INVALID_ARG
+    other = _layer(x)
+    other.residual = 1
+    assert g(*bargs(L=other)) == x.ERR_UNSUPPORTED
+
+
+def test_layout_gemm_and_attention_backward_reject_before_launch(x):
+    L = x.lib
+    f = L.xmod_gemm_bf16
+    # layout, A, lda, B, ldb, C, ldc, out_f32, M, N, K
+    assert f(3, FAKE, 64, FAKE, 64, FAKE, 64, 1, 64, 64, 64, None) == x.ERR_INVALID_ARG
+    assert f(x.GEMM_NN, FAKE, 64, FAKE, 32, FAKE, 64, 1, 64, 64, 64, None) == x.ERR_INVALID_ARG  # ldb < N
+    assert f(x.GEMM_TN, FAKE, 32, FAKE, 64, FAKE, 64, 1, 64, 64, 64, None) == x.ERR_INVALID_ARG  # lda < M
+    assert f(x.GEMM_TN, FAKE, 64, FAKE, 64, FAKE, 64, 0, 64, 64, 64, None) == x.ERR_UNSUPPORTED  # bf16 out
+    assert f(x.GEMM_NN, FAKE, 96, FAKE, 64, FAKE, 64, 1, 64, 64, 96, None) == x.ERR_UNSUPPORTED  # K % 64
+    assert f(x.GEMM_TN, FAKE, 68, FAKE, 64, FAKE, 64, 1, 60, 64, 64, None) == x.ERR_UNSUPPORTED  # M % 8
+    assert f(x.GEMM_NN, FAKE, 64, FAKE, 64, FAKE, 64, 1, 0, 64, 64, None) == x.ERR_INVALID_ARG
+    g = L.xmod_attention_bwd
+    assert g(FAKE, 384, FAKE, 128, FAKE, FAKE, 128, FAKE, FAKE, 384, 1, 10, 2, 1, 80,
+             None) == x.ERR_UNSUPPORTED
+    assert g(FAKE, 384, FAKE, 128, None, FAKE, 128, FAKE, FAKE, 384, 1, 10, 2, 1, 64,
+             None) == x.ERR_INVALID_ARG
+    assert g(FAKE, 384, FAKE, 128, FAKE, FAKE, 128, FAKE, FAKE, 100, 1, 10, 2, 1, 64,
+             None) == x.ERR_INVALID_ARG
+    assert L.xmod_attention_fwd_lse(FAKE, 384, FAKE, 128, None, 1, 10, 2, 1, 64,
+                                    None) == x.ERR_INVALID_ARG
