@@ -60,6 +60,32 @@ def algorithmic_work(w):
     }
 
 
+def algorithmic_work_bwd(w):
+    """Per-step algorithmic FLOPs and bytes of each kernel slot of the backward."""
+    B, T, d, k = w.B, w.T, w.d, w.k
+    M = B * k
+    dq, dkv, F = w.d_q, w.d_kv, w.ffn_hidden
+    nqkv = dq + 2 * dkv
+    att = 2.0 * B * w.n_q_heads * w.head_dim * k * (k + 1)
+    g = lambda m, n, kk: {"flops": 2.0 * m * n * kk, "bytes": 2.0 * (m * kk + n * kk) + 4.0 * m * n}
+    return {
+        "bwd_resid": {"flops": 0.0, "bytes": 12.0 * M * d},
+        "bwd_dg_gemm": dict(g(M, F, d), bytes=2.0 * (M * d + F * d) + 8.0 * M * F),
+        "bwd_dw_down_gemm": g(d, F, M),
+        "bwd_dv_gemm": g(M, d, 2 * F),
+        "bwd_dw_gateup_gemm": g(2 * F, d, M),
+        "bwd_rmsnorm2": {"flops": 0.0, "bytes": 20.0 * M * d},
+        "bwd_do_gemm": dict(g(M, dq, d), bytes=2.0 * (M * d + dq * d + M * dq)),
+        "bwd_dw_o_gemm": g(d, dq, M),
+        "bwd_attention": {"flops": 2.5 * att, "bytes": 2.0 * (M * nqkv * 2 + 2 * M * dq)},
+        "bwd_du_gemm": g(M, d, nqkv),
+        "bwd_dw_qkv_gemm": g(nqkv, d, M),
+        "bwd_rmsnorm1": {"flops": 0.0, "bytes": 12.0 * M * d},
+        "bwd_router": {"flops": 0.0, "bytes": 6.0 * (B * T - M) * d + 13.0 * B * T},
+        "bwd_sums": {"flops": 0.0, "bytes": 0.0},
+    }
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None if
     there is none or the kernel's sources changed since the counters were taken."""
@@ -76,7 +102,7 @@ def measured_traffic(kernel):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def threshold_layer(xmod, w, xb, dl, dims, steps, warmup):
+def threshold_layer(xmod, w, xb, dl, dims, steps, warmup, time_oracle=True):
     """The same layer with the eval-time causal threshold rule (ell >= 0 enters). An untrained
     router would pass half of the tokens; here its bias beta_r is set so that the expected
     share of tokens with s >= 0 is 1/K, as the rule is meant to route (s ~ N(beta_r, sigma^2),
@@ -110,34 +136,50 @@ def threshold_layer(xmod, w, xb, dl, dims, steps, warmup):
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in events) / steps
     routed = int(n_total.item())   # the same for every call
-    return {"ms_per_call": round(ms, 5), "routed_tokens": routed,
-            "routed_tokens_per_s": round(routed / (ms * 1e-3), 1),
-            "rule": "ell >= 0 (routing probability >= 1/2)", "router_bias": round(beta, 4),
-            "timing": "each call on the same input, events around each call"}
+    out = {"ms_per_call": round(ms, 5), "routed_tokens": routed,
+           "routed_tokens_per_s": round(routed / (ms * 1e-3), 1),
+           "rule": "ell >= 0 (routing probability >= 1/2)", "router_bias": round(beta, 4),
+           "timing": "each call on the same input, events around each call"}
+    if time_oracle:
+        import oracle
+        lay = dict(wl.make_layer(w, 0), router_bias=beta)
+        t0 = time.perf_counter()
+        res = oracle.sparse_layer_threshold(xb[:1], lay, w, tau=w.tau, delta=w.delta)
+        t1 = time.perf_counter() - t0
+        n = int(np.sum(res["counts"]))
+        out["cpu_baseline"] = {"value": round(n / t1, 1), "unit": "routed tokens/s",
+                               "kind": "oracle", "seconds": round(t1, 3),
+                               "sample": f"1 of the {w.B} sequences ({n} routed tokens), float64"}
+    return out
 
 
-def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4):
+def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4, oracle_budget_s=6.0):
     """One training step of the same layer: xmod_sparse_layer_fwd_train (the forward that keeps
     what the backward reads) then xmod_sparse_layer_bwd (gradients of the hidden state and of
     every parameter, with the routing loss of Eq. (9) at the page's coefficient 1e-4). Each step
-    starts from the same hidden state and bias (restored outside the events). Informational."""
+    starts from the same hidden state and bias (restored outside the events). In the timed steps
+    the library brackets only the backward's largest product with events (its roofline); a
+    further pass with events around every kernel gives the per-kernel breakdown; the backward
+    oracle is timed on one sequence. Informational."""
     import torch
     L = xmod.make_layer(dl)
     x0 = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).cuda()
-    b0 = torch.from_numpy(wl.make_bias(w)).cuda()
+    bias_np = wl.make_bias(w)
+    b0 = torch.from_numpy(bias_np).cuda()
     x, bias = x0.clone(), b0.clone()
-    dy = torch.from_numpy(np.ascontiguousarray(wl.make_dy(w)).view(np.int16)).view(
-        torch.bfloat16).cuda()
+    dy_np = wl.make_dy(w)
+    dy = torch.from_numpy(np.ascontiguousarray(dy_np).view(np.int16)).view(torch.bfloat16).cuda()
     dx = torch.empty_like(dy)
     saved = xmod.alloc_workspace(dims, w.K, xmod.WS_TRAIN_SAVED)
     ws = xmod.alloc_workspace(dims, w.K, xmod.WS_BACKWARD)
     grads = xmod.make_grads(xmod.alloc_grads(dims))
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(warmup + steps):
+    work = algorithmic_work_bwd(w)
+    dom = max(work, key=lambda n: work[n]["flops"])
+
+    def one(e=None):
         x.copy_(x0)
         bias.copy_(b0)
-        e = ev[i - warmup] if i >= warmup else None
         if e:
             e[0].record(stream)
         xmod.sparse_layer_fwd_train(x, L, dims, w.K, bias, w.tau, w.delta, saved, stream=stream)
@@ -147,23 +189,61 @@ def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4):
                               stream=stream)
         if e:
             e[2].record(stream)
+
+    for _ in range(warmup):
+        one()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    xmod.phase_timing(True, slots=[dom])
+    for i in range(steps):
+        one(ev[i])
     torch.cuda.synchronize()
+    dom_ms, _ = xmod.phase_times()
+    xmod.phase_timing(False)
     fwd = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
     bwd = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+    # breakdown
+    xmod.phase_timing(True)
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    ph, _ = xmod.phase_times()
+    xmod.phase_timing(False)
+    phases = {}
+    for name, v in work.items():
+        avg = ph[name] / steps
+        e = {"ms": round(avg, 5)}
+        if v["flops"] > 0:
+            e["tflops"] = round(v["flops"] / (avg * 1e-3) / 1e12, 1)
+        if v["bytes"] > 0 and v["flops"] == 0:
+            e["gbs"] = round(v["bytes"] / (avg * 1e-3) / 1e9, 1)
+        phases[name] = e
     M = w.B * w.k
-    work = algorithmic_work(w)
-    f_fwd = sum(v["flops"] for k2, v in work.items() if k2.endswith(("gemm", "attention")))
-    # backward: two products per projection (input and weight gradients) and five attention
-    # products (S, dP, dV, dK, dQ) for the forward's two
-    f_bwd = 2.0 * sum(v["flops"] for k2, v in work.items() if k2.endswith("gemm")) \
-        + 2.5 * work["attention"]["flops"]
-    return {"fwd_train_ms": round(fwd, 5), "bwd_ms": round(bwd, 5),
-            "routed_tokens_per_s": round(M / ((fwd + bwd) * 1e-3), 1),
-            "bwd_tflops": round(f_bwd / (bwd * 1e-3) / 1e12, 1),
-            "step_frac_mfma_peak": round((f_fwd + f_bwd) / ((fwd + bwd) * 1e-3) / 1e12
-                                         / PEAK_BF16_TFLOPS, 4),
-            "route_coef": route_coef,
-            "timing": "each step on the same input, events around the forward and the backward"}
+    fwork = algorithmic_work(w)
+    f_fwd = sum(v["flops"] for k2, v in fwork.items() if k2.endswith(("gemm", "attention")))
+    f_bwd = sum(v["flops"] for v in work.values())
+    dom_s = dom_ms[dom] / steps * 1e-3
+    ach = work[dom]["flops"] / dom_s / 1e12
+    out = {"fwd_train_ms": round(fwd, 5), "bwd_ms": round(bwd, 5),
+           "routed_tokens_per_s": round(M / ((fwd + bwd) * 1e-3), 1),
+           "bwd_tflops": round(f_bwd / (bwd * 1e-3) / 1e12, 1),
+           "step_frac_mfma_peak": round((f_fwd + f_bwd) / ((fwd + bwd) * 1e-3) / 1e12
+                                        / PEAK_BF16_TFLOPS, 4),
+           "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4)},
+           "phases": phases, "route_coef": route_coef,
+           "timing": "each step on the same input, events around the forward and the backward"}
+    if oracle_budget_s > 0:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.sparse_layer_grad(xb[:1], {k2: v for k2, v in wl.make_layer(w, 0).items()}, w,
+                                 w.K, dy_np[:1], bias=bias_np[:1], tau=w.tau,
+                                 route_coef=route_coef)
+        t1 = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(w.k / t1, 1), "unit": "routed tokens/s",
+                               "kind": "oracle", "seconds": round(t1, 3),
+                               "sample": "forward and backward of 1 of the 8 sequences, float64"}
+    return out
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -287,7 +367,8 @@ def main():
     phase_ms, _ = xmod.phase_times()
     xmod.phase_timing(False)
     phases = {}
-    for name, ms in phase_ms.items():
+    for name in xmod.FWD_PHASES:
+        ms = phase_ms[name]
         avg = ms / args.steps
         e = {"ms": round(avg, 5)}
         if work[name]["flops"] > 0 and name.endswith(("gemm", "attention")):
@@ -324,9 +405,11 @@ def main():
         "phases": phases,
     }
     if not args.no_threshold:
-        out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup)
+        out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup,
+                                                 time_oracle=not args.no_cpu_baseline)
     if not args.no_train:
-        out["train_step"] = train_step(xmod, w, xb, dl, dims, args.steps, args.warmup)
+        out["train_step"] = train_step(xmod, w, xb, dl, dims, args.steps, args.warmup,
+                                       oracle_budget_s=0.0 if args.no_cpu_baseline else 6.0)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -355,7 +355,11 @@ xmod_status xmod_attention_bwd(const void *qkv, int32_t ld_qkv, const void *o, i
  * recorded event, adds the time between the two events around each recorded kernel of every
  * recorded call into ms[i] for kernel slot i (sparse layer slots:
  * 0 router, 1 top-k, 2 gather+RMSNorm, 3 QKV GEMM, 4 attention, 5 O GEMM, 6 residual+RMSNorm,
- * 7 gate/up GEMM with SwiGLU, 8 down GEMM with gated scatter; a dense layer fills slots 2-8),
+ * 7 gate/up GEMM with SwiGLU, 8 down GEMM with gated scatter; a dense layer fills slots 2-8;
+ * the training forward uses slots 0-8 as the sparse layer; the backward fills slots 9-22:
+ * 9 gated residual, 10 dg GEMM with SwiGLU backward, 11 dW_down, 12 dv GEMM, 13 dW_gate|up,
+ * 14 RMSNorm-2, 15 dO GEMM, 16 dW_o, 17 attention, 18 du GEMM, 19 dW_qkv, 20 RMSNorm-1 with dx of
+ * the selected rows, 21 router and routing loss over every token, 22 sums of partial rows),
  * stores the number of recorded calls in *n_calls, and forgets the recorded events.
  * Not thread safe; meant for benchmarks, not for production calls or graph capture. */
 void xmod_phase_timing_enable(int32_t on);

@@ -27,7 +27,6 @@ thread_local int32_t g_last_hip = 0;
 // ---- measurement hook: events between kernels (see xmod_phase_timing_enable) ----
 // Boundary b of a call lies after kernel slot first_slot + b - 1 and before slot first_slot + b;
 // an event is recorded there when either neighbouring slot is selected by the mask.
-constexpr int kSlots = 9;
 struct PhaseCall {
   int first_slot = 0, n_bound = 0;
   std::vector<std::pair<int, size_t>> ev;  // (boundary, event index)
@@ -927,29 +926,38 @@ xmod_status xmod_sparse_layer_fwd_train(void *x, const xmod_layer *layer, const 
   uint16_t *z = at<uint16_t>(saved, p.z);
   float *a = at<float>(saved, p.a), *f = at<float>(saved, p.f);
 
+  phase_begin(s, 0);
   XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)layer->w_router,
                          layer->router_bias, bias, tau, logits, BT, d, s, sv));
+  phase_mark(s);
   XMOD_HIP(launch_topk(logits, dims->B, dims->T, k, idx, gate, bias, delta, s));
   if (idx_out) XMOD_HIP(launch_copy32(idx_out, idx, M, s));
   if (gate_out) XMOD_HIP(launch_copy32(gate_out, gate, M, s));
+  phase_mark(s);
   const RowMap map = topk_map(idx, dims, k);
   XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, (const uint16_t *)layer->g_attn,
                               dims->rms_eps, true, M, d, u, s, Xs));
+  phase_mark(s);
   GemmArgs g{};
   g.A = u; g.lda = d; g.B = (const uint16_t *)layer->w_qkv; g.ldb = d; g.C = qkv; g.ldc = nqkv;
   g.M = (int)M; g.N = nqkv; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_STORE, s));
+  phase_mark(s);
   XMOD_HIP(launch_attention_lse(qkv, nqkv, o, dq, lse, dims->B, k, Hq, Hkv, hd, s));
+  phase_mark(s);
   g = GemmArgs{};
   g.A = o; g.lda = dq; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.Cf = a; g.ldc = d;
   g.M = (int)M; g.N = d; g.K = dq;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, s));
+  phase_mark(s);
   XMOD_HIP(launch_residual_rmsnorm((const uint16_t *)x, map, a, (const uint16_t *)layer->g_ffn,
                                    dims->rms_eps, M, d, v, s));
+  phase_mark(s);
   g = GemmArgs{};
   g.A = v; g.lda = d; g.B = (const uint16_t *)layer->w_gate; g.B2 = (const uint16_t *)layer->w_up;
   g.ldb = d; g.C = gb; g.ldc = F; g.Z = z; g.ldz = 2 * F; g.M = (int)M; g.N = F; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_SWIGLU_SAVE, s));
+  phase_mark(s);
   g = GemmArgs{};
   g.map = map;
   g.A = gb; g.lda = F; g.B = (const uint16_t *)layer->w_down; g.ldb = F; g.ldc = d;
@@ -960,6 +968,7 @@ xmod_status xmod_sparse_layer_fwd_train(void *x, const xmod_layer *layer, const 
   if (zero_pad_rows(u, M, Mp, d, s) != XMOD_OK || zero_pad_rows(o, M, Mp, dq, s) != XMOD_OK ||
       zero_pad_rows(v, M, Mp, d, s) != XMOD_OK || zero_pad_rows(gb, M, Mp, F, s) != XMOD_OK)
     return XMOD_ERR_HIP;
+  phase_mark(s);
   return XMOD_OK;
 }
 
@@ -1010,61 +1019,75 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   const RowMap map = topk_map(idx, dims, k);
 
   // gated residual: dt, the gate's gradient, d varsigma partials; selection marks per token
+  phase_begin(s, 9);
   XMOD_HIP(launch_zero(dell_tok, align_up((size_t)BT * 4) + align_up((size_t)BT), s));
   XMOD_HIP(launch_resid_bwd((const uint16_t *)dy, map, a, f, gate, layer->varsigma, d, M, Mp, dt,
                             dell, dell_tok, q_tok, vs_part, s));
+  phase_mark(s);
   // FFN: dg = dt W_down (SwiGLU backward in the epilogue), dW_down = dt^T g
   GemmArgs g{};
   g.A = dt; g.lda = d; g.B = (const uint16_t *)layer->w_down; g.ldb = F; g.C = dz; g.ldc = 2 * F;
   g.Z = z; g.ldz = 2 * F; g.M = (int)M; g.N = F; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_SWIGLU_BWD, LAY_NN, s));
   if (zero_pad_rows(dz, M, Mp, 2 * F, s) != XMOD_OK) return XMOD_ERR_HIP;
+  phase_mark(s);
   g = GemmArgs{};
   g.A = dt; g.lda = d; g.B = gb; g.ldb = F; g.Cf = gr->w_down; g.ldc = F;
   g.M = d; g.N = F; g.K = (int)Mp;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  phase_mark(s);
   // dv = dzg W_gate + dzu W_up; [dW_gate; dW_up] = [dzg | dzu]^T v
   g = GemmArgs{};
   g.A = dz; g.lda = 2 * F; g.B = (const uint16_t *)layer->w_gate; g.B2 = (const uint16_t *)layer->w_up;
   g.K1 = F; g.ldb = d; g.Cf = dv; g.ldc = d; g.M = (int)M; g.N = d; g.K = 2 * F;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_NN, s));
+  phase_mark(s);
   g = GemmArgs{};
   g.A = dz; g.lda = 2 * F; g.B = v; g.ldb = d; g.Cf = gr->w_gate; g.Cf2 = gr->w_up; g.M1 = F;
   g.ldc = d; g.M = 2 * F; g.N = d; g.K = (int)Mp;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  phase_mark(s);
   // RMSNorm before the FFN: da = dt + dh, dX so far = dy + dh, d g_ffn
   XMOD_HIP(launch_rms2_bwd((const uint16_t *)dy, map, Xs, a, dv, (const uint16_t *)layer->g_ffn,
                            eps, dt, d, M, Mp, da, dxacc, part_g2, s));
+  phase_mark(s);
   // O projection: dO = da W_o, dW_o = da^T O
   g = GemmArgs{};
   g.A = da; g.lda = d; g.B = (const uint16_t *)layer->w_o; g.ldb = dq; g.C = dO; g.ldc = dq;
   g.M = (int)M; g.N = dq; g.K = d;
   XMOD_HIP(launch_gemm(g, EPI_STORE, LAY_NN, s));
+  phase_mark(s);
   g = GemmArgs{};
   g.A = da; g.lda = d; g.B = o; g.ldb = dq; g.Cf = gr->w_o; g.ldc = dq;
   g.M = d; g.N = dq; g.K = (int)Mp;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  phase_mark(s);
   // attention
   XMOD_HIP(launch_attention_bwd(qkv, nqkv, o, dq, lse, dO, dq, D, dqkv, nqkv, dims->B, k, Hq, Hkv,
                                 hd, s));
   if (zero_pad_rows(dqkv, M, Mp, nqkv, s) != XMOD_OK) return XMOD_ERR_HIP;
+  phase_mark(s);
   // QKV projection: du = dqkv W_qkv (into dv's buffer), dW_qkv = dqkv^T u
   g = GemmArgs{};
   g.A = dqkv; g.lda = nqkv; g.B = (const uint16_t *)layer->w_qkv; g.ldb = d; g.Cf = dv; g.ldc = d;
   g.M = (int)M; g.N = d; g.K = nqkv;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_NN, s));
+  phase_mark(s);
   g = GemmArgs{};
   g.A = dqkv; g.lda = nqkv; g.B = u; g.ldb = d; g.Cf = gr->w_qkv; g.ldc = d;
   g.M = nqkv; g.N = d; g.K = (int)Mp;
   XMOD_HIP(launch_gemm(g, EPI_STORE_F32, LAY_TN, s));
+  phase_mark(s);
   // RMSNorm before attention: dx of the selected rows, d g_attn, router terms of those rows
   XMOD_HIP(launch_rms1_bwd(Xs, map, dv, (const uint16_t *)layer->g_attn, eps, dxacc, s_tok, dell,
                            coef_n, (const uint16_t *)layer->w_router, d, M, (uint16_t *)dx,
                            part_g1, part_wr, s));
+  phase_mark(s);
   // router and routing loss over every token: dx of the other rows, d w_r, d beta, L_route
   XMOD_HIP(launch_route_bwd((const uint16_t *)x, (const uint16_t *)dy, s_tok, dell_tok, q_tok,
                             coef_n, (const uint16_t *)layer->w_router, d, BT, (uint16_t *)dx,
                             part_wr + (size_t)R * d, beta_part, loss_part, s));
+  phase_mark(s);
   // every column and scalar sum of partial rows, in one pair of launches
   ColsumJobs J{};
   auto job = [&](const float *part, int n_part, int n, float *out, float scale) {
@@ -1080,5 +1103,6 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   job(vs_part, R, 1, gr->varsigma, 1.0f);
   if (loss_route) job(loss_part, RT, 1, loss_route, (float)(1.0 / (double)BT));
   XMOD_HIP(launch_colsum_multi(J, s));
+  phase_mark(s);
   return XMOD_OK;
 }

@@ -322,7 +322,12 @@ def attention_fwd(qkv, o, B, k, Hq, Hkv, hd, stream=None):
 
 
 PHASES = ["router", "topk", "gather_rmsnorm", "qkv_gemm", "attention", "o_gemm",
-          "residual_rmsnorm", "gateup_swiglu_gemm", "down_scatter_gemm"]
+          "residual_rmsnorm", "gateup_swiglu_gemm", "down_scatter_gemm",
+          # backward (xmod_sparse_layer_bwd)
+          "bwd_resid", "bwd_dg_gemm", "bwd_dw_down_gemm", "bwd_dv_gemm", "bwd_dw_gateup_gemm",
+          "bwd_rmsnorm2", "bwd_do_gemm", "bwd_dw_o_gemm", "bwd_attention", "bwd_du_gemm",
+          "bwd_dw_qkv_gemm", "bwd_rmsnorm1", "bwd_router", "bwd_sums"]
+FWD_PHASES = PHASES[:9]
 
 
 def phase_timing(on: bool, slots=None):
