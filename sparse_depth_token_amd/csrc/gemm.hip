@@ -14,15 +14,16 @@
 // 8-k fragment the MFMA expects, in the same k order as a k-contiguous fragment.
 //
 // Design (gfx950, wave64):
-//  * Workgroup tile BM x BN x BK, four or eight waves in a grid, each computing a WM x WN
-//    sub-tile as (WM/32) x (WN/32) MFMA 32x32x16 tiles (fp32 accumulators in registers).
+//  * Workgroup tile BM x BN x BK, four or eight compute waves in a grid, each computing a
+//    WM x WN sub-tile as (WM/32) x (WN/32) MFMA 32x32x16 tiles (fp32 accumulators in
+//    registers), plus (optionally) four loader waves that only copy k-tiles into LDS.
 //  * The weight fragment is the MFMA's first operand and the activation fragment its second,
 //    so each lane ends with 4 consecutive output columns of one row.
 //  * k-tiles are copied global -> LDS by the DMA form of the load (global_load_lds_dwordx4:
 //    16 bytes per lane, no staging registers) into an NS-stage LDS ring: tiles kt+1 .. kt+NS-1
 //    are in flight while tile kt is multiplied. Before each barrier a wave waits only for its
-//    own loads of the next tile. The CU's vector-memory path moves 64 bytes per clock, so the
-//    copies are spread over the k-steps of a tile rather than issued in one burst.
+//    own loads of the next tile. When the compute waves copy their own tiles, the copies are
+//    spread over the k-steps (the CU's vector-memory path moves 64 bytes per clock).
 //  * Operand fragments are double-buffered in registers. Every k-step is laid out slot by slot
 //    (one MFMA per slot, scheduling barriers between slots): the next k-step's fragment reads
 //    go out in the first slots, the DMA copies in the later ones.
@@ -62,9 +63,11 @@ __device__ __forceinline__ int swz(int r) {
 // consecutive chunks; the XOR spreads those 16 (row, chunk) pairs over all 64 banks.
 __device__ __forceinline__ int swz_km(int r) { return 4 * (r & 3); }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY, int NL>
 struct GemmCfg {
-  static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
+  // NW compute waves; NL loader waves (0: the compute waves copy their own k-tiles)
+  static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = (NW + NL) * 64;
+  static constexpr int NDW = NL ? NL : NW;  // waves that issue the DMA copies
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr bool A_KM = LAY == LAY_TN, B_KM = LAY != LAY_NT;  // k-major operands
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
@@ -72,8 +75,8 @@ struct GemmCfg {
   static constexpr int NSTAGE = NS;                          // LDS ring depth
   static constexpr int CPR = BK / 8;                         // 16-byte chunks per LDS row
   static constexpr int RPB = 64 / CPR;                       // rows per 1 KB DMA block
-  // DMA blocks per wave per tile (1 KB each, whatever the layout)
-  static constexpr int NA = BM * BK / 512 / NW, NB = BN * BK / 512 / NW;
+  // DMA blocks per copying wave per tile (1 KB each, whatever the layout)
+  static constexpr int NA = BM * BK / 512 / NDW, NB = BN * BK / 512 / NDW;
   static constexpr bool SWIGLU_FWD = EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_SAVE;
   static constexpr int BN_OUT = SWIGLU_FWD ? BN / 2 : BN;
   static constexpr bool F32_TILE =
@@ -88,12 +91,13 @@ struct GemmCfg {
   static constexpr int RCH = BM <= RCH_FIT ? BM : BM / 2 <= RCH_FIT ? BM / 2 : BM / 4 <= RCH_FIT ? BM / 4 : BM / 8;
   static constexpr int NCH = BM / RCH;
   static constexpr int LDS_BYTES = LDS_MAIN;
-  // waves per SIMD: NW / 4 per workgroup, two workgroups per CU when the LDS allows it
-  static constexpr int WAVES_PER_EU = (NW / 4) * (LDS_BYTES <= 80 * 1024 ? 2 : 1);
-  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
+  // waves per SIMD: (NW + NL) / 4 per workgroup, two workgroups per CU when the LDS allows it
+  static constexpr int WAVES_PER_EU = ((NW + NL) / 4) * (LDS_BYTES <= 80 * 1024 ? 2 : 1);
+  static_assert(NW == 4 || NW == 8, "four or eight compute waves per workgroup");
+  static_assert(NL == 0 || NL == 4, "no loader waves, or one per SIMD");
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
   static_assert(NS >= 2, "at least one k-tile in flight");
-  static_assert(NA >= 1 && NB >= 1 && BM * BK % (512 * NW) == 0 && BN * BK % (512 * NW) == 0,
+  static_assert(NA >= 1 && NB >= 1 && BM * BK % (512 * NDW) == 0 && BN * BK % (512 * NDW) == 0,
                 "DMA blocks");
   static_assert(!SWIGLU_FWD || WN % 64 == 0, "SwiGLU pairs gate/up 32-column blocks");
   static_assert(!SWIGLU_FWD || LAY == LAY_NT, "the forward SwiGLU interleaves k-contiguous B rows");
@@ -102,15 +106,19 @@ struct GemmCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY>
-__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>::NT),
-                             (GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>::WAVES_PER_EU)) void
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY, int NL>
+__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>::NT),
+                             (GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>::WAVES_PER_EU)) void
 gemm_kernel(GemmArgs g) {
-  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r32 = lane & 31, gq = lane >> 5;
+  // With loader waves, waves NW .. NW+NL-1 only copy k-tiles into LDS and the compute waves
+  // issue no vector-memory instruction in the k loop: a copy held up in the memory pipeline
+  // (64 bytes per clock per CU) then stalls a wave that has no MFMA to issue.
+  const bool loader = NL > 0 && wid >= C::NW;
   // rows: the device-side count when there is one (the grid covers the bound g.M)
   const int M = g.map.n_dev ? min(*g.map.n_dev, g.M) : g.M, K = g.K;
   const int n_out = g.N;  // output columns (F for SwiGLU)
@@ -148,7 +156,7 @@ gemm_kernel(GemmArgs g) {
   // (every operand here holds fewer than 2^31 elements); the DMA takes byte offsets.
   const int nk = K / BK;
   const int nk_last = nk - 1;
-  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  const int wv = __builtin_amdgcn_readfirstlane(NL > 0 ? wid - C::NW : wid);  // copying-wave index
   // A k-major operand's block b holds k-rows (512/R) b .. of the tile's R columns; lane l lands
   // at k-row (512/R) b + l / (R/8), physical chunk l % (R/8), so it fetches logical chunk
   // (l % (R/8)) ^ swz_km(k-row) (columns past the matrix are clamped: only stores are masked).
@@ -157,11 +165,11 @@ gemm_kernel(GemmArgs g) {
   for (int i = 0; i < C::NA; ++i) {
     if (C::A_KM) {
       constexpr int CPT = BM / 8, RPT = 64 / CPT;
-      const int krow = RPT * (C::NW * i + wv) + lane / CPT;
+      const int krow = RPT * (C::NDW * i + wv) + lane / CPT;
       const int gm = min(m0 + (((lane % CPT) ^ swz_km(krow)) << 3), M - 8);
       a_off[i] = ((uint32_t)krow * (uint32_t)g.lda + (uint32_t)gm) * 2u;
     } else {
-      const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
+      const int row = C::RPB * (C::NDW * i + wv) + lane / C::CPR;
       const int gm = min(m0 + row, M - 1);
       a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
     }
@@ -170,11 +178,11 @@ gemm_kernel(GemmArgs g) {
   for (int i = 0; i < C::NB; ++i) {
     if (C::B_KM) {
       constexpr int CPT = BN / 8, RPT = 64 / CPT;
-      const int krow = RPT * (C::NW * i + wv) + lane / CPT;
+      const int krow = RPT * (C::NDW * i + wv) + lane / CPT;
       const int gn = min(n0 + (((lane % CPT) ^ swz_km(krow)) << 3), g.N - 8);
       b_off[i] = ((uint32_t)krow * (uint32_t)g.ldb + (uint32_t)gn) * 2u;
     } else {
-      const int row = C::RPB * (C::NW * i + wv) + lane / C::CPR;
+      const int row = C::RPB * (C::NDW * i + wv) + lane / C::CPR;
       // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
       int gn = C::SWIGLU_FWD ? n0 + (row >> 6) * 32 + (row & 31) : n0 + row;
       gn = min(gn, g.N - 1);
@@ -184,7 +192,7 @@ gemm_kernel(GemmArgs g) {
   const char *a_bytes = (const char *)g.A;
   const char *b_bytes[2] = {(const char *)g.B, (const char *)(C::SWIGLU_FWD ? g.B2 : g.B)};
   auto b_half = [&](int i) {  // which weight matrix DMA block i of B reads (SwiGLU: gate / up)
-    return C::SWIGLU_FWD ? (((C::RPB * (C::NW * i + wv)) >> 5) & 1) : 0;  // wave-uniform
+    return C::SWIGLU_FWD ? (((C::RPB * (C::NDW * i + wv)) >> 5) & 1) : 0;  // wave-uniform
   };
   // Copies [lo, hi) of the tile's NA + NB DMA blocks (A blocks first) of k-tile kt, clamped to
   // the last one, into the stage at element offset `stage`. A k-tile of a k-major operand
@@ -206,12 +214,12 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < C::NA; ++i)
       if (i >= lo && i < hi)
-        dma16(a_bytes + (a_off[i] + kb_a), lds + stage + 512 * (C::NW * i + wv));
+        dma16(a_bytes + (a_off[i] + kb_a), lds + stage + 512 * (C::NDW * i + wv));
 #pragma unroll
     for (int i = 0; i < C::NB; ++i)
       if (C::NA + i >= lo && C::NA + i < hi)
         dma16((C::B_KM ? b_km : b_bytes[b_half(i)]) + (b_off[i] + kb_b),
-              lds + stage + C::A_ELEMS + 512 * (C::NW * i + wv));
+              lds + stage + C::A_ELEMS + 512 * (C::NDW * i + wv));
   };
   auto issue_tile = [&](int kt, int stage) { issue_part(kt, stage, 0, C::NA + C::NB); };
 
@@ -343,12 +351,14 @@ gemm_kernel(GemmArgs g) {
   // when another wave's DMA overwrites it in the next step; after the barrier the next tile's
   // first fragments are read while the last k-step's MFMAs run from registers. The DMA copies
   // of tile dma_kt are spread over the k-steps before the barrier.
+  // (with loader waves the compute waves copy nothing and wait only for their LDS reads)
+  constexpr int WAIT_LDS0 = (15) | (7 << 4) | (0 << 8) | (3 << 14);
   auto step = [&](const uint16_t *st, const uint16_t *st_next, int dma_kt, int dma_stage) {
 #pragma unroll
     for (int ks = 0; ks < KS - 1; ++ks)
-      kstep(ks & 1, st, ks + 1, (ks + 1) & 1, dma_kt, dma_stage, ks * SH,
-            min((ks + 1) * SH, NDMA));
-    __builtin_amdgcn_s_waitcnt(WAIT_NEXT_LDS0);
+      kstep(ks & 1, st, ks + 1, (ks + 1) & 1, dma_kt, dma_stage, NL ? 0 : ks * SH,
+            NL ? 0 : min((ks + 1) * SH, NDMA));
+    __builtin_amdgcn_s_waitcnt(NL ? WAIT_LDS0 : WAIT_NEXT_LDS0);
     __builtin_amdgcn_s_barrier();
     kstep((KS - 1) & 1, st_next, 0, 0, 0, 0, 0, 0);
   };
@@ -358,20 +368,40 @@ gemm_kernel(GemmArgs g) {
   // and released by that step's barrier, with tile kt + NS - 1 (clamped to the last tile: the
   // surplus copies land in stages no later step reads, and keep the vmcnt accounting uniform).
   // One loop body with rotating stage offsets (kept in scalar registers): a single exit keeps
-  // the accumulators in one register assignment for the epilogue.
+  // the accumulators in one register assignment for the epilogue. Loader and compute waves
+  // meet at the same barriers: one after the first tile, one per k-tile, one after the loop.
+  if (loader) {
 #pragma unroll
-  for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
-  __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
-  __syncthreads();
-#pragma unroll
-  for (int f = 0; f < NFR; ++f) load_frag(lds, 0, 0, f);
-  int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
+    for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    __syncthreads();
+    int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
 #pragma unroll 1
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st_next = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
-    step(lds + st_cur, lds + st_next, kt + NS - 1, st_dma);
-    st_dma = st_cur;
-    st_cur = st_next;
+    for (int kt = 0; kt < nk; ++kt) {
+      // stage st_dma was released by the previous barrier; tile kt + 1 lands before this one
+      issue_tile(kt + NS - 1, st_dma);
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+      __builtin_amdgcn_s_barrier();
+      st_dma = st_cur;
+      st_cur = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
+    }
+  } else {
+    if (NL == 0) {
+#pragma unroll
+      for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
+      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < NFR; ++f) load_frag(lds, 0, 0, f);
+    int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
+#pragma unroll 1
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st_next = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
+      step(lds + st_cur, lds + st_next, kt + NS - 1, st_dma);
+      st_dma = st_cur;
+      st_cur = st_next;
+    }
   }
   __syncthreads();  // all DMA landed and all fragment reads done before LDS holds the C tile
 
@@ -383,6 +413,7 @@ gemm_kernel(GemmArgs g) {
     if (ch > 0) __syncthreads();  // previous pass's reads of the C tile are done
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
+      if (loader) break;  // loader waves only help with the stores below
       const int row = wm0 + 32 * i + r32 - r_lo;  // row within this pass
       if (wm0 + 32 * i < r_lo || wm0 + 32 * i >= r_lo + C::RCH) continue;
       if (C::SWIGLU_FWD) {
@@ -523,26 +554,30 @@ gemm_kernel(GemmArgs g) {
   }  // tile loop
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY = LAY_NT>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY = LAY_NT, int NL = 0>
 static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
-  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY>;
+  using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>;
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + C::BN_OUT - 1) / C::BN_OUT;
   // device-side row count: a CU-sized grid walks the tiles (g.M is only the bound)
   const int tiles = tiles_m * tiles_n;
   const int wgs_per_cu = C::WAVES_PER_EU * 4 / C::NW;
   const int grid = g.map.n_dev ? min(tiles, 256 * wgs_per_cu) : tiles;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY>), dim3(grid), dim3(C::NT), 0,
-                     s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>), dim3(grid), dim3(C::NT),
+                     0, s, g);
   return hipGetLastError();
 }
 
 // Tile choice (measured on the projections of the X-MoD layer at 4096 routed rows):
 //  * SwiGLU with at least two waves of 256x256 tiles: 256x256 (eight waves of 128x64, two per
-//    SIMD, BK = 32, four-stage ring): the halved epilogue per flop and the second wave per SIMD
-//    beat 256x128 by ~5 %.
-//  * otherwise 256x128 (four waves of 128x64, BK = 64, three-stage ring) when the grid gives
-//    at least 5/8 of the 256 CUs a tile, else 128x128.
+//    SIMD, BK = 32, four-stage ring, each wave copying its share): the halved epilogue per flop
+//    and the second wave per SIMD beat 256x128 by ~5 %.
+//  * otherwise 256x128 (four compute waves of 64x128 plus four loader waves, BK = 64,
+//    three-stage ring) when the grid gives at least 5/8 of the 256 CUs a tile, else 128x128
+//    (four compute waves of 64x64 plus four loader waves). Loader waves took 8 % off the
+//    down projection and 1-3 % off the others; a 64x128 wave tile (two activation by four
+//    weight fragments per k-step) sustains more MFMA work per LDS read than 128x64 with one
+//    wave per SIMD (1.72 against 1.48 PFLOP/s in a register-fed probe).
 constexpr int GEMM_CUS = 256;
 
 template <int EPI, int LAY = LAY_NT>
@@ -555,8 +590,8 @@ static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
     if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI, LAY>(g, s);
   }
   const long t_big = tm * ((g.N + 128 / half - 1) / (128 / half));
-  if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 128, 64, 64, 3, EPI, LAY>(g, s);
-  return run_gemm<128, 128, 64, 64, 64, 3, EPI, LAY>(g, s);
+  if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 64, 128, 64, 3, EPI, LAY, 4>(g, s);
+  return run_gemm<128, 128, 64, 64, 64, 3, EPI, LAY, 4>(g, s);
 }
 
 hipError_t launch_gemm(const GemmArgs &g, GemmEpilogue epi, hipStream_t s) {
