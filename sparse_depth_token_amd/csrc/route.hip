@@ -114,27 +114,41 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Add each candidate lane's digit to the LDS histogram. LDS atomics on the same address
-// within one instruction are serialised by the LDS itself, which is far cheaper than
-// aggregating equal digits in the wave first (a ballot / shuffle round per distinct digit).
-__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t dg, bool cand) {
-  if (cand) atomicAdd(&hist[dg], 1u);
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row operations (no LDS round trip):
+// shifts by 1, 2, 4, 8 within each row of 16 lanes (Hillis-Steele, vacated lanes add 0), then
+// the last lane of row 0 (2) into row 1 (3), and the last lane of row 1 into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
 }
+
+// Histogram copies of the first pass: that pass sees the top byte of every key (the sign and
+// the high exponent bits, shared by all values of similar magnitude), so a wave's lanes pile
+// onto a few bins; LDS atomics to one address within an instruction are serialised, and
+// spreading the lanes over 4 copies (by lane % 4) cuts that serialisation fourfold. Later
+// passes see spread digits of fewer candidates and use one copy.
+constexpr int TOPK_COPIES0 = 4;
 
 template <int KPT>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ logits, int T, int k,
                                                     int32_t *__restrict__ idx,
                                                     float *__restrict__ gate,
                                                     float *__restrict__ bias, float delta) {
-  __shared__ uint32_t hist[4][256];  // one histogram per pass: a single barrier per pass
-  __shared__ unsigned long long s_wave_tot[16];
+  // pass 0: TOPK_COPIES0 copies; passes 1-3: one each (a single barrier per pass)
+  __shared__ uint32_t hist[(TOPK_COPIES0 + 3) * 256];
+  __shared__ uint32_t s_wave_gt[16], s_wave_eq[16];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float *L = logits + (int64_t)b * T;
   const int p0 = tid * KPT;
 
-  hist[tid >> 8][tid & 255] = 0u;
+  for (int i = tid; i < (TOPK_COPIES0 + 3) * 256; i += 1024) hist[i] = 0u;
   // The logits (for the gate) and carried bias values of this thread's positions are loaded
   // up front, so the output phase waits on no global read.
   float* const Bi = bias ? bias + (int64_t)b * T : nullptr;
@@ -155,25 +169,24 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
+    const int ncopy = pass == 0 ? TOPK_COPIES0 : 1;
+    uint32_t *h = hist + (pass == 0 ? 0 : (TOPK_COPIES0 + pass - 1) * 256);
+    uint32_t *hc = h + (pass == 0 ? (lane % TOPK_COPIES0) * 256 : 0);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const bool cand = (p0 + j < T) && ((key[j] & pmask) == prefix);
-      hist_add(hist[pass], (key[j] >> shift) & 255u, cand);
+      if (cand) atomicAdd(&hc[(key[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
     // lane l owns bins 255-4l .. 252-4l, scanned from the top (largest digit first)
     uint32_t c[4], tot = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      c[q] = hist[pass][255 - 4 * lane - q];
+      c[q] = 0u;
+      for (int cp = 0; cp < ncopy; ++cp) c[q] += h[cp * 256 + 255 - 4 * lane - q];
       tot += c[q];
     }
-    uint32_t incl = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const uint32_t incl = wave_incl_scan(tot);
     const uint32_t excl = incl - tot;
     // exactly one lane holds the bin where the running count reaches `remaining`
     uint32_t digit = 0u, rem_new = 0u;
@@ -191,9 +204,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
         if (!found) above += c[q];
       }
     }
-    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-    digit = __shfl(digit, src, 64);
-    remaining = __shfl(rem_new, src, 64);
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;  // wave-uniform
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+    remaining = (uint32_t)__builtin_amdgcn_readlane((int)rem_new, src);
     prefix |= digit << shift;
     pmask |= 255u << shift;
   }
@@ -209,20 +222,19 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
       eq += key[j] == thr;
     }
   }
-  const unsigned long long v = (unsigned long long)gt | ((unsigned long long)eq << 32);
-  unsigned long long incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+  const uint32_t gt_incl = wave_incl_scan(gt), eq_incl = wave_incl_scan(eq);
+  if (lane == 63) {
+    s_wave_gt[wid] = gt_incl;
+    s_wave_eq[wid] = eq_incl;
   }
-  if (lane == 63) s_wave_tot[wid] = incl;
   __syncthreads();
-  unsigned long long base = 0;
-  for (int w2 = 0; w2 < wid; ++w2) base += s_wave_tot[w2];
-  const unsigned long long excl = base + incl - v;
-  const uint32_t gt_before = (uint32_t)(excl & 0xFFFFFFFFull);
-  uint32_t eq_seen = (uint32_t)(excl >> 32);
+  uint32_t gt_base = 0, eq_base = 0;
+  for (int w2 = 0; w2 < wid; ++w2) {
+    gt_base += s_wave_gt[w2];
+    eq_base += s_wave_eq[w2];
+  }
+  const uint32_t gt_before = gt_base + gt_incl - gt;
+  uint32_t eq_seen = eq_base + eq_incl - eq;
   uint32_t pos = gt_before + (eq_seen < need ? eq_seen : need);
 
   int32_t *I = idx + (int64_t)b * k;
