@@ -123,32 +123,48 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // passes see spread digits of fewer candidates and use one copy.
 constexpr int TOPK_COPIES0 = 4;
 
+// Key ownership: with up to 4 keys per thread, thread t owns the consecutive positions
+// 4t .. 4t+3 (one 16-byte span per lane, so every access is coalesced anyway). With 8 or
+// more, thread t owns positions t, t + 1024, t + 2048, ... ("rows" of 1024 positions): a
+// consecutive span per thread would make every load and store instruction touch 64 cache
+// lines, which took most of the kernel's time (32768 positions: 68 -> 37 us per call;
+// 65536: 148 -> 97 us, where 64 keys per thread spill registers either way).
 template <int KPT>
 __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ logits, int T, int k,
                                                     int32_t *__restrict__ idx,
                                                     float *__restrict__ gate,
                                                     float *__restrict__ bias, float delta) {
+  constexpr bool STRIDED = KPT >= 8;
   // pass 0: TOPK_COPIES0 copies; passes 1-3: one each (a single barrier per pass)
   __shared__ uint32_t hist[(TOPK_COPIES0 + 3) * 256];
   __shared__ uint32_t s_wave_gt[16], s_wave_eq[16];
+  // strided ownership: per (row, wave) counts of keys above / equal to the threshold, then
+  // their exclusive prefix in position order
+  __shared__ uint32_t s_tab_gt[STRIDED ? KPT * 16 : 1], s_tab_eq[STRIDED ? KPT * 16 : 1];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float *L = logits + (int64_t)b * T;
   const int p0 = tid * KPT;
+  auto pos_of = [&](int j) { return STRIDED ? j * 1024 + tid : p0 + j; };
 
   for (int i = tid; i < (TOPK_COPIES0 + 3) * 256; i += 1024) hist[i] = 0u;
-  // The logits (for the gate) and carried bias values of this thread's positions are loaded
-  // up front, so the output phase waits on no global read.
+  // The logits (for the gate) and, with consecutive ownership, the carried bias values of this
+  // thread's positions are loaded up front, so the output phase waits on no global read.
   float* const Bi = bias ? bias + (int64_t)b * T : nullptr;
+  // (with strided ownership only the keys stay in registers; the few selected logits and
+  // bias values are read again, coalesced, when the output is written)
   uint32_t key[KPT];
-  float lv[KPT], bv[KPT];
+  float lv[STRIDED ? 1 : KPT], bv[STRIDED ? 1 : KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int p = p0 + j;
-    lv[j] = p < T ? L[p] : 0.f;
-    bv[j] = (Bi && p < T) ? Bi[p] : 0.f;
-    key[j] = p < T ? order_key(lv[j]) : 0u;
+    const int p = pos_of(j);
+    const float l = p < T ? L[p] : 0.f;
+    if (!STRIDED) {
+      lv[j] = l;
+      bv[j] = (Bi && p < T) ? Bi[p] : 0.f;
+    }
+    key[j] = p < T ? order_key(l) : 0u;
   }
   __syncthreads();
 
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
     uint32_t *hc = h + (pass == 0 ? (lane % TOPK_COPIES0) * 256 : 0);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool cand = (p0 + j < T) && ((key[j] & pmask) == prefix);
+      const bool cand = (pos_of(j) < T) && ((key[j] & pmask) == prefix);
       if (cand) atomicAdd(&hc[(key[j] >> shift) & 255u], 1u);
     }
     __syncthreads();
@@ -202,49 +218,125 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
   const uint32_t thr = prefix;     // key of the k-th largest
   const uint32_t need = remaining; // how many keys equal to thr are taken (lowest positions)
 
-  // Block-wide exclusive prefix over (count > thr, count == thr) in position order.
-  uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if (p0 + j < T) {
-      gt += key[j] > thr;
-      eq += key[j] == thr;
-    }
-  }
-  const uint32_t gt_incl = wave_incl_scan(gt), eq_incl = wave_incl_scan(eq);
-  if (lane == 63) {
-    s_wave_gt[wid] = gt_incl;
-    s_wave_eq[wid] = eq_incl;
-  }
-  __syncthreads();
-  uint32_t gt_base = 0, eq_base = 0;
-  for (int w2 = 0; w2 < wid; ++w2) {
-    gt_base += s_wave_gt[w2];
-    eq_base += s_wave_eq[w2];
-  }
-  const uint32_t gt_before = gt_base + gt_incl - gt;
-  uint32_t eq_seen = eq_base + eq_incl - eq;
-  uint32_t pos = gt_before + (eq_seen < need ? eq_seen : need);
-
   int32_t *I = idx + (int64_t)b * k;
   float *G = gate ? gate + (int64_t)b * k : nullptr;
+  // The selected keys: all above the threshold key, plus the first `need` equal to it in
+  // position order. Output slot of a selected key = the number of selected keys before it.
+  if (!STRIDED) {
+    // Block-wide exclusive prefix over (count > thr, count == thr) in position order.
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (p0 + j < T) {
+        gt += key[j] > thr;
+        eq += key[j] == thr;
+      }
+    }
+    const uint32_t gt_incl = wave_incl_scan(gt), eq_incl = wave_incl_scan(eq);
+    if (lane == 63) {
+      s_wave_gt[wid] = gt_incl;
+      s_wave_eq[wid] = eq_incl;
+    }
+    __syncthreads();
+    uint32_t gt_base = 0, eq_base = 0;
+    for (int w2 = 0; w2 < wid; ++w2) {
+      gt_base += s_wave_gt[w2];
+      eq_base += s_wave_eq[w2];
+    }
+    const uint32_t gt_before = gt_base + gt_incl - gt;
+    uint32_t eq_seen = eq_base + eq_incl - eq;
+    uint32_t pos = gt_before + (eq_seen < need ? eq_seen : need);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int p = p0 + j;
+      if (p < T) {
+        bool sel = key[j] > thr;
+        if (key[j] == thr) {
+          sel = eq_seen < need;
+          ++eq_seen;
+        }
+        // Exactly k keys of the sequence pass, so pos < k; the bound is a cheap guarantee that
+        // idx is never overrun, not a selection rule.
+        if (sel && pos < (uint32_t)k) {
+          I[pos] = p;
+          if (G) G[pos] = 1.0f / (1.0f + expf(-lv[j]));
+          if (Bi) Bi[p] = __fadd_rn(bv[j], delta);
+          ++pos;
+        }
+      }
+    }
+    return;
+  }
+
+  // Strided ownership: position order is (row j, wave, lane), and each lane holds one key
+  // per row, so a row's counts in a wave are ballot popcounts and a lane's offset within them
+  // is the number of set ballot bits below it. The (row, wave) totals get one block-wide
+  // exclusive scan.
+  auto row_masks = [&](int j, unsigned long long &gm, unsigned long long &em) {
+    const bool valid = pos_of(j) < T;
+    gm = __ballot(valid && key[j] > thr);
+    em = __ballot(valid && key[j] == thr);
+  };
+  auto below = [&](unsigned long long m) {  // set bits of m in lanes below this one
+    return (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  };
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int p = p0 + j;
-    if (p < T) {
-      bool sel = key[j] > thr;
-      if (key[j] == thr) {
-        sel = eq_seen < need;
-        ++eq_seen;
-      }
-      // Exactly k keys of the sequence pass (all keys above the threshold key, plus the first
-      // `need` equal to it), so pos < k; the bound is a cheap guarantee that idx is never
-      // overrun, not a selection rule.
-      if (sel && pos < (uint32_t)k) {
+    unsigned long long gm, em;
+    row_masks(j, gm, em);
+    if (lane == 0) {
+      s_tab_gt[j * 16 + wid] = (uint32_t)__popcll(gm);
+      s_tab_eq[j * 16 + wid] = (uint32_t)__popcll(em);
+    }
+  }
+  __syncthreads();
+  {
+    // entry e = (row e / 16, wave e % 16), KPT * 16 <= 1024 entries, one per thread
+    const bool has = tid < KPT * 16;
+    const uint32_t g = has ? s_tab_gt[tid] : 0u, q = has ? s_tab_eq[tid] : 0u;
+    const uint32_t g_incl = wave_incl_scan(g), q_incl = wave_incl_scan(q);
+    if (lane == 63) {
+      s_wave_gt[wid] = g_incl;
+      s_wave_eq[wid] = q_incl;
+    }
+    __syncthreads();
+    uint32_t g_base = 0, q_base = 0;
+    for (int w2 = 0; w2 < wid; ++w2) {
+      g_base += s_wave_gt[w2];
+      q_base += s_wave_eq[w2];
+    }
+    if (has) {  // each thread rewrites only the entry it read above
+      s_tab_gt[tid] = g_base + g_incl - g;
+      s_tab_eq[tid] = q_base + q_incl - q;
+    }
+  }
+  __syncthreads();
+  // Output, 8 rows at a time: the rows' logits (for the gate) and bias values are read first
+  // (coalesced, every position), so a batch waits for one round trip rather than one per row.
+  constexpr int RB = KPT < 8 ? KPT : 8;
+#pragma unroll
+  for (int j0 = 0; j0 < KPT; j0 += RB) {
+    float lc[RB], bc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int p = pos_of(j0 + r);
+      lc[r] = p < T ? L[p] : 0.f;
+      bc[r] = (Bi && p < T) ? Bi[p] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int j = j0 + r, p = pos_of(j);
+      unsigned long long gm, em;
+      row_masks(j, gm, em);
+      const uint32_t gt_before = s_tab_gt[j * 16 + wid] + below(gm);
+      const uint32_t eq_before = s_tab_eq[j * 16 + wid] + below(em);
+      const bool sel = p < T && (key[j] > thr || (key[j] == thr && eq_before < need));
+      const uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+      if (sel && pos < (uint32_t)k) {  // pos < k always holds; the bound only guards idx
         I[pos] = p;
-        if (G) G[pos] = 1.0f / (1.0f + expf(-lv[j]));
-        if (Bi) Bi[p] = __fadd_rn(bv[j], delta);
-        ++pos;
+        if (G) G[pos] = 1.0f / (1.0f + expf(-lc[r]));
+        if (Bi) Bi[p] = __fadd_rn(bc[r], delta);
       }
     }
   }
