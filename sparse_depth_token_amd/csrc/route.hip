@@ -152,8 +152,8 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float *__restrict__ lo
   // The logits (for the gate) and, with consecutive ownership, the carried bias values of this
   // thread's positions are loaded up front, so the output phase waits on no global read.
   float* const Bi = bias ? bias + (int64_t)b * T : nullptr;
-  // (with strided ownership only the keys stay in registers; the few selected logits and
-  // bias values are read again, coalesced, when the output is written)
+  // (with strided ownership only the keys stay in registers; the logits and bias values are
+  // read again, coalesced, a batch of rows at a time, when the output is written)
   uint32_t key[KPT];
   float lv[STRIDED ? 1 : KPT], bv[STRIDED ? 1 : KPT];
 #pragma unroll
