@@ -42,6 +42,12 @@ def _logit_cases():
     big[0, ::7] = np.inf
     big[1, ::5] = -np.inf
     cases.append(("huge and infinite", big, 600))
+    # long sequences (8 to 32 keys per thread: the strided key layout) with ties across
+    # rows of 1024 positions and across waves, where the first `need` equal keys must win
+    for B, T, k, levels in [(3, 6000, 1500, 4), (2, 32768, 8192, 3), (1, 20000, 7777, 1)]:
+        lv = rng.integers(0, levels, (B, T)).astype(np.float32) - 1.0
+        lv[rng.random(lv.shape) < 0.2] = -0.0
+        cases.append((f"{levels}-level ties B{B} T{T} k{k}", lv, k))
     return cases
 
 
