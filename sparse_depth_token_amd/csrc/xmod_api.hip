@@ -253,7 +253,6 @@ int block_sparse_per_block(float A, int32_t K, bool *ok) {
 
 }  // namespace
 
-extern "C" {
 
 // ---- mechanism controls of Table 7 ----------------------------------------------------------
 
@@ -310,6 +309,8 @@ xmod_status route_topk_into(const void *x, const xmod_layer *L, const xmod_dims 
 }
 
 }  // namespace
+
+extern "C" {
 
 size_t xmod_train_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry);
 
