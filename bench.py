@@ -14,10 +14,11 @@ Prints one JSON line: routed tokens/s over the K timed steps; the roofline of th
 kernel (the gate/up GEMM), timed by HIP events the library records around that kernel in every
 timed step (two events per step); a per-kernel breakdown from K further steps with events
 around every kernel; informational lines for the eval-time threshold rule and one training
-step (forward + backward); and the CPU oracle timed on a bounded sample on this host.
+step (forward + backward); the copy bandwidth and vendor-library GEMM rates this GPU
+sustains (context for the fractions); and the CPU oracle timed on a bounded sample on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
-                      [--no-train]
+                      [--no-train] [--no-ceilings]
 """
 from __future__ import annotations
 
@@ -246,6 +247,45 @@ def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4, oracle_bud
     return out
 
 
+def measured_ceilings(w, reps=10):
+    """What this GPU sustains on plain work, beside the vendor peaks the fractions use: HBM copy
+    bandwidth (read + write of a 1 GiB buffer by torch's copy kernel) and the vendor GEMM library
+    (torch.matmul, i.e. hipBLASLt) on the layer's gate/up shape and on 8192^3, bf16. Context
+    for the roofline fractions; no part of the layer runs here."""
+    import torch
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    M = w.B * w.k
+    out = {"hbm_copy_gbs": round(2 * n / t_copy / 1e9, 1)}
+    gemms = {}
+    for name, (m, nn, kk) in {"gateup_shape": (M, 2 * w.ffn_hidden, w.d),
+                              "square_8192": (8192, 8192, 8192)}.items():
+        a = torch.randn(m, kk, device="cuda").to(torch.bfloat16)
+        bw = torch.randn(nn, kk, device="cuda").to(torch.bfloat16)
+        t = timed(lambda: torch.matmul(a, bw.t()))
+        gemms[name] = round(2.0 * m * nn * kk / t / 1e12, 1)
+        del a, bw
+    out["library_gemm_tflops"] = gemms
+    out["note"] = ("torch copy and torch.matmul (vendor library) on this GPU; the "
+                   "roofline fractions use the vendor peaks (8 TB/s, 2.5 PFLOP/s)")
+    return out
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle (float64 NumPy) on a bounded sample of the same workload on this host."""
     import oracle
@@ -284,6 +324,8 @@ def main():
                     help="skip the informational threshold-routing line")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the informational training-step (forward + backward) object")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy bandwidth and library GEMM rates")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -410,6 +452,8 @@ def main():
     if not args.no_train:
         out["train_step"] = train_step(xmod, w, xb, dl, dims, args.steps, args.warmup,
                                        oracle_budget_s=0.0 if args.no_cpu_baseline else 6.0)
+    if not args.no_ceilings:
+        out["measured_ceilings"] = measured_ceilings(w)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
