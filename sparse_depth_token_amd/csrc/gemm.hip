@@ -561,7 +561,7 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
   const int tiles_n = (g.N + C::BN_OUT - 1) / C::BN_OUT;
   // device-side row count: a CU-sized grid walks the tiles (g.M is only the bound)
   const int tiles = tiles_m * tiles_n;
-  const int wgs_per_cu = C::WAVES_PER_EU * 4 / C::NW;
+  const int wgs_per_cu = C::WAVES_PER_EU * 4 / (C::NW + NL);  // resident workgroups per CU
   const int grid = g.map.n_dev ? min(tiles, 256 * wgs_per_cu) : tiles;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>), dim3(grid), dim3(C::NT),
                      0, s, g);
