@@ -10,11 +10,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "sparse_depth_token_amd", "libxmod.so")
 HEADER = os.path.join(ROOT, "include", "xmod.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libxmod.so not built")
 
 
 @pytest.fixture(scope="module")
 def x():
+    # a fresh checkout has no library (built files are not versioned): build it, so that these
+    # checks never pass by being skipped (hipcc cross-compiles gfx950 without a GPU)
+    if not os.path.exists(LIB):
+        from sparse_depth_token_amd import build
+        build.build()
     from sparse_depth_token_amd import xmod
     return xmod
 
