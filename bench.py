@@ -14,8 +14,9 @@ Prints one JSON line: routed tokens/s over the K timed steps; the roofline of th
 kernel (the gate/up GEMM), timed by HIP events the library records around that kernel in every
 timed step (two events per step); a per-kernel breakdown from K further steps with events
 around every kernel; informational lines for the eval-time threshold rule and one training
-step (forward + backward); the copy bandwidth and vendor-library GEMM rates this GPU
-sustains (context for the fractions); and the CPU oracle timed on a bounded sample on this host.
+step (forward + backward); the copy and read bandwidth, MFMA rate and vendor-library GEMM rates
+this GPU sustains (context for the fractions); and the CPU oracle timed on a bounded sample on
+this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
                       [--no-train] [--no-ceilings]
@@ -249,7 +250,9 @@ def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4, oracle_bud
 
 def measured_ceilings(w, reps=10):
     """What this GPU sustains on plain work, beside the vendor peaks the fractions use: HBM copy
-    bandwidth (read + write of a 1 GiB buffer by torch's copy kernel) and the vendor GEMM library
+    bandwidth (read + write of a 1 GiB buffer by torch's copy kernel), the library's ceiling
+    probes (a streaming read of the same 1 GiB; back-to-back bf16 MFMAs on every SIMD, no memory
+    traffic) and the vendor GEMM library
     (torch.matmul, i.e. hipBLASLt) on the layer's gate/up shape and on 8192^3, bf16. Context
     for the roofline fractions; no part of the layer runs here."""
     import torch
@@ -265,13 +268,24 @@ def measured_ceilings(w, reps=10):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / reps
 
+    from sparse_depth_token_amd import xmod
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     t_copy = timed(lambda: dst.copy_(src))
-    del src, dst
+    del dst
+    # the library's own probes: a streaming read of the same 1 GiB, back-to-back MFMAs
+    sums = torch.empty(xmod.PROBE_THREADS, dtype=torch.int32, device="cuda")
+    t_read = timed(lambda: xmod.probe_read(src, sums))
+    del src
+    acc = torch.empty(xmod.PROBE_THREADS, dtype=torch.float32, device="cuda")
+    iters = 4096
+    t_mfma = timed(lambda: xmod.probe_mfma(acc, iters))
+    mfma_flops = 4096 * 4 * iters * 32768
     M = w.B * w.k
-    out = {"hbm_copy_gbs": round(2 * n / t_copy / 1e9, 1)}
+    out = {"hbm_copy_gbs": round(2 * n / t_copy / 1e9, 1),
+           "hbm_read_gbs": round(n / t_read / 1e9, 1),
+           "mfma_bf16_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
     gemms = {}
     for name, (m, nn, kk) in {"gateup_shape": (M, 2 * w.ffn_hidden, w.d),
                               "square_8192": (8192, 8192, 8192)}.items():
@@ -281,8 +295,9 @@ def measured_ceilings(w, reps=10):
         gemms[name] = round(2.0 * m * nn * kk / t / 1e12, 1)
         del a, bw
     out["library_gemm_tflops"] = gemms
-    out["note"] = ("torch copy and torch.matmul (vendor library) on this GPU; the "
-                   "roofline fractions use the vendor peaks (8 TB/s, 2.5 PFLOP/s)")
+    out["note"] = ("torch copy (read + write), the library's streaming-read and back-to-back "
+                   "MFMA probes, and torch.matmul (vendor library) on this GPU; the roofline "
+                   "fractions use the vendor peaks (8 TB/s, 2.5 PFLOP/s)")
     return out
 
 
@@ -325,7 +340,7 @@ def main():
     ap.add_argument("--no-train", action="store_true",
                     help="skip the informational training-step (forward + backward) object")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the measured copy bandwidth and library GEMM rates")
+                    help="skip the measured bandwidth, MFMA and library GEMM ceilings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counters)")

@@ -366,6 +366,21 @@ void xmod_phase_timing_enable(int32_t on);
 void xmod_phase_timing_slots(uint32_t mask);
 xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls);
 
+/* --- Ceiling probes (measurement only; no part of the layer). ----------------------------------
+ * What the part sustains on the two kinds of work the layer's kernels are bound by, for a
+ * benchmark to print beside the vendor peaks. Both enqueue one kernel of 1024 workgroups of 256
+ * threads on the stream and write one value per thread to out (caller-owned device memory of
+ * 1024 * 256 elements).
+ * xmod_probe_mfma: every wave issues 4 * iters independent v_mfma_f32_32x32x16_bf16 on all-ones
+ *   operands back to back (32768 flops each, 4 waves per workgroup); out[t] = 64 * iters
+ *   (4 accumulators of 16 per product). INVALID_ARG: out NULL or iters outside [1, 2^18].
+ * xmod_probe_read: reads `bytes` (a multiple of 16, 16-byte aligned) of src with 16-byte loads in
+ *   a grid-stride pass; out[t] = the 32-bit wrap-around sum of the words thread t read, so the
+ *   sum over t equals that of every 32-bit word of src. INVALID_ARG: NULL pointer, bytes 0 or
+ *   not a multiple of 16. */
+xmod_status xmod_probe_mfma(float *out, int32_t iters, void *stream);
+xmod_status xmod_probe_read(const void *src, size_t bytes, uint32_t *out, void *stream);
+
 const char *xmod_status_string(xmod_status st);
 int32_t xmod_last_hip_error(void);
 

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libxmod.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["route.hip", "rows.hip", "rows_bwd.hip", "gemm.hip", "attention.hip",
-           "attention_bwd.hip",
+           "attention_bwd.hip", "probe.hip",
            "xmod_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

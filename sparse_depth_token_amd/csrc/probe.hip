@@ -1,0 +1,63 @@
+// Ceiling probes for the measurement: what this part sustains on the two kinds of work the
+// layer's kernels are bound by, measured in the same run as the layer, beside the vendor peaks.
+//  * MFMA: every wave issues independent v_mfma_f32_32x32x16_bf16 back to back (four
+//    accumulators, no memory traffic in the loop).
+//  * HBM read: a grid-stride pass of 16-byte loads over a buffer, every 32-bit word added into
+//    a per-thread sum (kept, so that nothing is skipped; the sums are checkable on the host).
+#include "common.h"
+
+namespace xmod {
+
+__global__ __launch_bounds__(256) void probe_mfma_kernel(float *__restrict__ out, int iters) {
+  // all-ones operands: every MFMA adds 16 to each accumulator element (exact below 2^24)
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)1.0f;
+    b[e] = (__bf16)1.0f;
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s += acc[t][0];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *__restrict__ src, int64_t n16,
+                                                         uint32_t *__restrict__ out) {
+  uint32_t s = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // four 16-byte loads in flight per thread
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    s += v0.x + v0.y + v0.z + v0.w + v1.x + v1.y + v1.z + v1.w;
+    s += v2.x + v2.y + v2.z + v2.w + v3.x + v3.y + v3.z + v3.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    s += v.x + v.y + v.z + v.w;
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+hipError_t launch_probe_mfma(float *out, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3(PROBE_WGS), dim3(256), 0, s, out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(probe_read_kernel, dim3(PROBE_WGS), dim3(256), 0, s, (const uint4 *)src,
+                     (int64_t)(bytes / 16), out);
+  return hipGetLastError();
+}
+
+}  // namespace xmod

@@ -566,6 +566,19 @@ xmod_status xmod_attention_bwd(const void *qkv, int32_t ld_qkv, const void *o, i
   return XMOD_OK;
 }
 
+xmod_status xmod_probe_mfma(float *out, int32_t iters, void *stream) {
+  if (!out || iters < 1 || iters > (1 << 18)) return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_probe_mfma(out, iters, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_probe_read(const void *src, size_t bytes, uint32_t *out, void *stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0)
+    return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_probe_read(src, bytes, out, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
 void xmod_phase_timing_enable(int32_t on) {
   g_phase.on = on != 0;
   g_phase.used = 0;

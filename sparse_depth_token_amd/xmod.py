@@ -31,6 +31,7 @@ EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", 
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_gemm_bf16", "xmod_attention_fwd",
             "xmod_attention_fwd_lse", "xmod_attention_bwd",
             "xmod_phase_timing_enable", "xmod_phase_timing_slots", "xmod_phase_times",
+            "xmod_probe_mfma", "xmod_probe_read",
             "xmod_status_string",
             "xmod_last_hip_error"]
 
@@ -328,6 +329,27 @@ PHASES = ["router", "topk", "gather_rmsnorm", "qkv_gemm", "attention", "o_gemm",
           "bwd_rmsnorm2", "bwd_do_gemm", "bwd_dw_o_gemm", "bwd_attention", "bwd_du_gemm",
           "bwd_dw_qkv_gemm", "bwd_rmsnorm1", "bwd_router", "bwd_sums"]
 FWD_PHASES = PHASES[:9]
+
+
+PROBE_THREADS = 1024 * 256  # values the ceiling probes write (one per thread)
+
+
+def probe_mfma(out, iters, stream=None):
+    """Back-to-back bf16 MFMAs on every SIMD (4 * iters per wave, 4096 waves); out: fp32
+    tensor of PROBE_THREADS, each set to 64 * iters. Returns the flops enqueued."""
+    _check(lib.xmod_probe_mfma(_ptr(out), int(iters), _stream(stream)), "xmod_probe_mfma")
+    return 4096 * 4 * int(iters) * 32768
+
+
+def probe_read(src, out, stream=None):
+    """Streaming read of every byte of the contiguous tensor src; out: int32 tensor of
+    PROBE_THREADS whose 32-bit wrap-around sum equals that of src's 32-bit words. Returns the
+    bytes read."""
+    nbytes = src.numel() * src.element_size()
+    lib.xmod_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    _check(lib.xmod_probe_read(_ptr(src), nbytes, _ptr(out), _stream(stream)), "xmod_probe_read")
+    return nbytes
 
 
 def phase_timing(on: bool, slots=None):
