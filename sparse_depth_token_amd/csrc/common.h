@@ -199,12 +199,6 @@ hipError_t launch_attention_bwd(const uint16_t *qkv, int ld_qkv, const uint16_t 
 
 // ---- backward row kernels (rows_bwd.hip) ----
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);          // bytes / 16 chunks
-
-// Ceiling probes (probe.hip): PROBE_WGS workgroups of 256 threads (4 per CU, one wave per
-// SIMD each), out[PROBE_WGS * 256].
-constexpr int PROBE_WGS = 1024;
-hipError_t launch_probe_mfma(float *out, int iters, hipStream_t s);
-hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *out, hipStream_t s);
 hipError_t launch_copy32(void *dst, const void *src, int64_t n_words, hipStream_t s);
 int bwd_row_wgs();    // workgroups (= partial rows written) of the packed-row kernels
 int bwd_route_wgs();  // workgroups (= partial rows written) of the every-token router kernel

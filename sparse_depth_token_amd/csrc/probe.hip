@@ -8,6 +8,9 @@
 
 namespace xmod {
 
+// PROBE_WGS workgroups of 256 threads (4 per CU, one wave per SIMD each), out[PROBE_WGS * 256]
+constexpr int PROBE_WGS = 1024;
+
 __global__ __launch_bounds__(256) void probe_mfma_kernel(float *__restrict__ out, int iters) {
   // all-ones operands: every MFMA adds 16 to each accumulator element (exact below 2^24)
   bf16x8 a, b;

@@ -310,6 +310,12 @@ xmod_status route_topk_into(const void *x, const xmod_layer *L, const xmod_dims 
 
 }  // namespace
 
+namespace xmod {
+// ceiling probes (probe.hip)
+hipError_t launch_probe_mfma(float *out, int iters, hipStream_t s);
+hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *out, hipStream_t s);
+}  // namespace xmod
+
 extern "C" {
 
 size_t xmod_train_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry);
