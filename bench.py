@@ -14,12 +14,12 @@ Prints one JSON line: routed tokens/s over the K timed steps; the roofline of th
 kernel (the gate/up GEMM), timed by HIP events the library records around that kernel in every
 timed step (two events per step); a per-kernel breakdown from K further steps with events
 around every kernel; informational lines for the eval-time threshold rule and one training
-step (forward + backward); the copy and read bandwidth, MFMA rate and vendor-library GEMM rates
-this GPU sustains (context for the fractions); and the CPU oracle timed on a bounded sample on
-this host.
+step (forward + backward); the two stack workloads through the block entry point; the copy
+and read bandwidth, MFMA rate and vendor-library GEMM rates this GPU sustains (context for the
+fractions); and the CPU oracle timed on a bounded sample on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
-                      [--no-train] [--no-ceilings]
+                      [--no-train] [--no-blocks] [--no-ceilings]
 """
 from __future__ import annotations
 
@@ -248,6 +248,79 @@ def train_step(xmod, w, xb, dl, dims, steps, warmup, route_coef=1e-4, oracle_bud
     return out
 
 
+def layer_flops(w, sparse):
+    """Algorithmic matrix-core flops of one layer: the projections on its rows and the causal
+    attention over them (a sparse layer: the B*k routed rows; a dense layer: all B*T)."""
+    P = w.d * (w.d_q + 2 * w.d_kv) + w.d_q * w.d + 3 * w.d * w.ffn_hidden
+    n = w.k if sparse else w.T
+    return 2.0 * w.B * n * P + 2.0 * w.B * w.n_q_heads * w.head_dim * n * (n + 1)
+
+
+def blocks(xmod, steps=5, warmup=2, seed=7):
+    """The two stack workloads through xmod_block_fwd: the original MoD alternation
+    ([Sparse(8)] + [Dense]) x 4 at B4 x T4096, d 1536, and the X-MoD A3K16 block (one dense
+    prefix layer, 48 Sparse(16) layers, one dense anchor) at B4 x T4096, d 1024. Weights are
+    drawn on the device (N(0, 0.02), gains 1), activations N(0, 1); each timed call starts from
+    the same hidden state. Reports the block's time and flop rate, and one sparse and one dense
+    layer of the same shapes timed alone (routed tokens/s of the sparse layer; the ratio of the
+    two layers' times). Informational."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    bf = torch.bfloat16
+    out = {}
+    for name in ("mod_pairs_k8_b4x4096_d1536", "a3k16_block_b4x4096_d1024"):
+        w = wl.WORKLOADS[name]
+        n_layers = w.N0 + w.N1 * (w.AK + 1)
+        rnd = lambda *shape: (torch.randn(*shape, device="cuda", generator=g) * 0.02).to(bf)
+        one = lambda *shape: torch.ones(*shape, device="cuda", dtype=bf)
+        Ls = [xmod.make_layer({"w_router": rnd(w.d), "g_attn": one(w.d),
+                               "w_qkv": rnd(w.d_q + 2 * w.d_kv, w.d), "w_o": rnd(w.d, w.d_q),
+                               "g_ffn": one(w.d), "w_gate": rnd(w.ffn_hidden, w.d),
+                               "w_up": rnd(w.ffn_hidden, w.d), "w_down": rnd(w.d, w.ffn_hidden)})
+              for _ in range(n_layers)]
+        dims = xmod.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden,
+                              w.rms_eps)
+        x0 = torch.randn(w.B, w.T, w.d, device="cuda", generator=g).to(bf)
+        x = x0.clone()
+        bias = torch.zeros(w.B, w.T, device="cuda")
+        ws = xmod.alloc_workspace(dims, w.K, xmod.WS_BLOCK)
+        A = w.AK / w.K
+
+        def timed(fn):
+            for _ in range(warmup):
+                x.copy_(x0)
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for e0, e1 in ev:
+                x.copy_(x0)
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+        t_block = timed(lambda: xmod.block_fwd(x, Ls, dims, w.N0, w.N1, A, w.K, bias, w.tau,
+                                               w.delta, ws))
+        t_sparse = timed(lambda: xmod.sparse_layer_fwd(x, Ls[w.N0], dims, w.K, bias, w.tau,
+                                                       w.delta, ws))
+        t_dense = timed(lambda: xmod.dense_layer_fwd(x, Ls[0], dims, ws))
+        n_sparse = w.N1 * w.AK
+        n_dense = n_layers - n_sparse
+        f_block = n_sparse * layer_flops(w, True) + n_dense * layer_flops(w, False)
+        out[name] = {"layers": n_layers, "sparse_layers": n_sparse, "block_ms": round(t_block, 4),
+                     "block_tflops": round(f_block / (t_block * 1e-3) / 1e12, 1),
+                     "sparse_layer_ms": round(t_sparse, 5), "dense_layer_ms": round(t_dense, 5),
+                     "sparse_routed_tokens_per_s": round(w.B * w.k / (t_sparse * 1e-3), 1),
+                     "sparse_layer_tflops": round(layer_flops(w, True) / (t_sparse * 1e-3) / 1e12, 1),
+                     "dense_layer_tflops": round(layer_flops(w, False) / (t_dense * 1e-3) / 1e12, 1),
+                     "sparse_over_dense_time": round(t_sparse / t_dense, 4)}
+        del Ls, ws, x, x0
+        torch.cuda.empty_cache()
+    out["timing"] = "events around each call, each call from the same hidden state"
+    return out
+
+
 def measured_ceilings(w, reps=10):
     """What this GPU sustains on plain work, beside the vendor peaks the fractions use: HBM copy
     bandwidth (read + write of a 1 GiB buffer by torch's copy kernel), the library's ceiling
@@ -339,6 +412,8 @@ def main():
                     help="skip the informational threshold-routing line")
     ap.add_argument("--no-train", action="store_true",
                     help="skip the informational training-step (forward + backward) object")
+    ap.add_argument("--no-blocks", action="store_true",
+                    help="skip the informational stack workloads (MoD pairs, A3K16 block)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured bandwidth, MFMA and library GEMM ceilings")
     ap.add_argument("--copy-probe", action="store_true",
@@ -467,6 +542,8 @@ def main():
     if not args.no_train:
         out["train_step"] = train_step(xmod, w, xb, dl, dims, args.steps, args.warmup,
                                        oracle_budget_s=0.0 if args.no_cpu_baseline else 6.0)
+    if not args.no_blocks:
+        out["blocks"] = blocks(xmod)
     if not args.no_ceilings:
         out["measured_ceilings"] = measured_ceilings(w)
     if not args.no_cpu_baseline:
