@@ -306,10 +306,8 @@ gemm_kernel(GemmArgs g) {
   constexpr int WAIT_NEXT = (VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14);
   constexpr int WAIT_NEXT_LDS0 = (VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14);
   constexpr int KS = BK / 16;  // k-steps per tile
-#ifndef XMOD_DMA_SPLIT
-#define XMOD_DMA_SPLIT (KS - 1)
-#endif
-  constexpr int SH = (NDMA + XMOD_DMA_SPLIT - 1) / XMOD_DMA_SPLIT;  // DMA blocks per k-step
+  // the copies of a k-tile are spread over the first KS - 1 k-steps of the tile before it
+  constexpr int SH = (NDMA + KS - 2) / (KS - 1);  // DMA blocks per k-step
 
   // One k-step as NMF slots of one MFMA each, in a fixed order (a scheduling barrier closes
   // every slot; each MFMA takes 8 passes, during which the wave issues the slot's other
