@@ -6,8 +6,16 @@
 // 0-based). Softmax uses the scale 1/sqrt(head_dim) and the usual online recurrence (running
 // max, rescaled running sum and output), so the k x k score matrix is never stored.
 //
-// Work split: one workgroup = (pair of q-tiles of 128 packed rows, query head, sequence); its
-// 8 waves own 32 query rows each and share key/value tiles of 64 rows.
+// Work split: 8 waves per workgroup, 32 query rows per wave, key/value tiles of 64 rows shared
+// by the workgroup. The register footprint allows one workgroup per CU (two waves per SIMD).
+// Two ways of giving a workgroup its 256 query rows, chosen at launch:
+//  * one q-tile of 256 packed rows, last tile first in dispatch order: every wave stays busy
+//    to the last key tiles, so each SIMD keeps two waves whose MFMA and softmax work overlap.
+//    Used when the grid holds more workgroups than there are CUs.
+//  * a pair of q-tiles of 128 rows (tile nqt-1-p for waves 0-3, tile p for waves 4-7): every
+//    workgroup has the same causal work, and the earlier tile's key/value tiles are a prefix
+//    of the later one's. Used when each CU gets at most one workgroup: the longest workgroup
+//    then holds half as many long rows.
 //
 //  * K and V tiles are copied global -> LDS by the DMA form of the load (no staging registers)
 //    into a two-stage ring: tile j+1 is in flight while tile j is used. Both stay row-major
@@ -34,7 +42,7 @@ __device__ __forceinline__ void attn_dma16(const void *gsrc, uint16_t *lds_block
 
 template <int HD>
 struct AttnCfg {
-  static constexpr int BQ = 128, BKV = 64, NW = 8, NT = 64 * NW;
+  static constexpr int BQ = 256, BQP = 128, BKV = 64, NW = 8, NT = 64 * NW;
   static constexpr int CPR = HD / 8;              // 16-byte chunks per row
   static constexpr int RPB = 64 / CPR;            // rows per 1 KB DMA block
   static constexpr int TILE = BKV * HD;           // elements of one K (or V) tile
@@ -72,37 +80,48 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
                                                       float scale_log2,
                                                       const int32_t *__restrict__ seq_off,
                                                       const int32_t *__restrict__ seq_len,
-                                                      FullKV fkv, float *__restrict__ lse) {
+                                                      FullKV fkv, float *__restrict__ lse,
+                                                      int paired) {
   using C = AttnCfg<HD>;
-  constexpr int BQ = C::BQ, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
+  constexpr int BQ = C::BQ, BQP = C::BQP, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
   // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
   // it by more than 2^RESCALE_LOG2 (log2 units), so weights exp2(x - M) stay below 2^8 and most
   // tiles skip the rescale of the running sum and output.
   constexpr float RESCALE_LOG2 = 8.0f;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
 
-  // Workgroup = pair (q-tile nqt-1-p, q-tile p): waves 0-3 take the later tile, waves 4-7 the
-  // earlier one (none when both are the same middle tile). Every workgroup then has the same
-  // causal work, each SIMD runs one wave of each tile, and the earlier tile's key/value tiles
-  // are a prefix of the later one's, so the pair loads them once.
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x, b = blockIdx.y;
   // sequence length and first packed row: fixed, or per sequence (the grid covers the longest)
   const int k = seq_len ? seq_len[b] : k_fixed;
   const int64_t row0 = seq_len ? (int64_t)seq_off[b] : (int64_t)b * k_fixed;
-  const int nqt = (k + BQ - 1) / BQ;
-  // Pairs in a grid-stride loop: one per workgroup when the grid covers the sequence's pairs,
-  // several when it was sized below the longest possible sequence (per-sequence lengths).
-  for (int p = blockIdx.x; p < (nqt + 1) / 2; p += gridDim.x) {
-  if (p != (int)blockIdx.x) __syncthreads();  // the previous pair's epilogue is done with LDS
-  const int qt_hi = nqt - 1 - p;
+  const int nqt = paired ? (k + BQP - 1) / BQP : (k + BQ - 1) / BQ;
+  const int n_units = paired ? (nqt + 1) / 2 : nqt;  // q-tile pairs or q-tiles
+  // units in a grid-stride loop: one per workgroup when the grid covers the sequence's units,
+  // several when it was sized below the longest possible sequence (per-sequence lengths)
+  for (int it = blockIdx.z; it < n_units; it += gridDim.z) {
+  if (it != (int)blockIdx.z) __syncthreads();  // the previous unit's epilogue is done with LDS
   const int gkv = (h * Hkv) / Hq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int gq = lane >> 5, r32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wid);
-  const int half = wid >> 2;
-  const bool active = half == 0 || p != qt_hi;
-  const int qt = half == 0 ? qt_hi : p;
-  const int q_pos = qt * BQ + (wid & 3) * 32 + r32;  // packed query index
+  // this wave's first packed query, whether it has a share, and the end of the workgroup's
+  // query rows (its last key)
+  int q_row0, q_end;
+  bool active;
+  if (paired) {
+    const int qt_hi = nqt - 1 - it;
+    const bool later = wid < 4;
+    q_row0 = (later ? qt_hi : it) * BQP + (wid & 3) * 32;
+    active = later || it != qt_hi;  // the middle tile of an odd count: waves 0-3 only
+    q_end = min(qt_hi * BQP + BQP, k);
+  } else {
+    const int qt = nqt - 1 - it;
+    q_row0 = qt * BQ + wid * 32;
+    active = true;
+    q_end = min(qt * BQ + BQ, k);
+  }
+  active = active && q_row0 < k;  // a ragged last tile leaves later waves empty
+  const int q_pos = q_row0 + r32;  // packed query index
   // key positions: the packed rows themselves, or (full KV) every position of the sequence,
   // a query at original position qpos seeing keys <= qpos
   const int kvlen = FULLKV ? fkv.T : k;
@@ -111,13 +130,11 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   };
   const int q_key = FULLKV ? pos_of(min(q_pos, k - 1)) : q_pos;  // this lane's query position
   // first and last query positions of this wave (last = -1: nothing to do)
-  const int q_first_wave = FULLKV ? pos_of(min(qt * BQ + (wid & 3) * 32, k - 1))
-                                  : qt * BQ + (wid & 3) * 32;
+  const int q_first_wave = FULLKV ? pos_of(min(q_row0, k - 1)) : q_row0;
   const int q_last_wave = !active ? -1
-                          : FULLKV ? pos_of(min(qt * BQ + (wid & 3) * 32 + 31, k - 1))
-                                   : qt * BQ + (wid & 3) * 32 + 31;
+                          : FULLKV ? pos_of(min(q_row0 + 31, k - 1)) : q_row0 + 31;
 
-  const int key_hi = FULLKV ? pos_of(min(qt_hi * BQ + BQ, k) - 1) + 1 : min(qt_hi * BQ + BQ, k);
+  const int key_hi = FULLKV ? pos_of(q_end - 1) + 1 : q_end;
   const int n_kv = (key_hi + BKV - 1) / BKV;
   const int ldk = FULLKV ? fkv.ldkv : ldq;
   const char *kbase = FULLKV ? (const char *)(fkv.kv + (int64_t)b * fkv.T * fkv.ldkv + gkv * HD)
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
       }
     // the same wave reads back: LDS operations of one wave complete in order
     constexpr int RPI = 64 / C::CPR;  // rows per store instruction
-    const int q0 = qt * BQ + (wid & 3) * 32;
+    const int q0 = q_row0;
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = RPI * i + lane / C::CPR, c = lane % C::CPR;
@@ -355,25 +372,30 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
       if (q0 + r < k) *(uint4 *)(o + (row0 + q0 + r) * ldo + h * HD + c * 8) = v;
     }
   }
-  }  // pair loop
+  }  // unit loop
 }
+
+constexpr int ATTN_CUS = 256;  // MI355X
 
 template <bool FULLKV>
 static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
                         int Hq, int Hkv, int hd, const int32_t *seq_off, const int32_t *seq_len,
                         const FullKV &fkv, hipStream_t s, float *lse = nullptr) {
-  const int nqt = (k + 127) / 128;
-  // per-sequence lengths (k is then only their bound): a quarter of the pairs of a longest
-  // sequence per (head, sequence), each workgroup looping over its share
-  const int pairs = (nqt + 1) / 2;
-  const dim3 grid((unsigned)(seq_len ? (pairs + 3) / 4 : pairs), (unsigned)Hq, (unsigned)B);
+  // (head, sequence, unit): the unit index is the slowest, so in the one-tile split every
+  // head's and sequence's longest tiles are dispatched first. Per-sequence lengths (k is then
+  // only their bound): a quarter of the units of a longest sequence per (head, sequence), each
+  // workgroup looping over its share.
+  const int nqt = (k + AttnCfg<128>::BQ - 1) / AttnCfg<128>::BQ;
+  const int paired = (long)Hq * B * nqt <= ATTN_CUS;
+  const int units = paired ? ((k + AttnCfg<128>::BQP - 1) / AttnCfg<128>::BQP + 1) / 2 : nqt;
+  const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)(seq_len ? (units + 3) / 4 : units));
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 128)
     hipLaunchKernelGGL((attn_kernel<128, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
-                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse);
+                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse, paired);
   else
     hipLaunchKernelGGL((attn_kernel<64, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
-                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse);
+                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse, paired);
 }
 
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,

@@ -114,6 +114,9 @@ FULLKV = {
                                                           4, bias_std=0.1, gain_std=0.1), {}),
     "B1 T2048 K8 d1024 GQA 8/2 hd128 + RoPE": (wl.Workload("fkv_c", 138, 1, 2048, 1024, 8, 2, 128,
                                                            2816, 8, bias_std=0.1), {"rope_theta": 1e4}),
+    # 16 heads x 4 sequences x 5 q-tiles of 256: more workgroups than CUs (one tile each)
+    "B4 T2100 K2 d1024 GQA 16/4 hd64 (ragged, one-tile split)": (
+        wl.Workload("fkv_d", 139, 4, 2100, 1024, 16, 4, 64, 1024, 2, bias_std=0.1), {}),
 }
 
 

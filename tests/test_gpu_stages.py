@@ -252,7 +252,10 @@ def test_gemm_layouts(x, layout, M, N, K, f32, pad):
 @pytest.mark.parametrize("B,k,Hq,Hkv,hd", [(2, 256, 4, 4, 64), (1, 333, 4, 2, 128), (3, 200, 8, 2, 64),
                                            (2, 512, 16, 16, 128), (1, 1100, 4, 1, 128),
                                            (1, 1, 2, 1, 128), (2, 65, 4, 4, 64), (1, 129, 2, 2, 128),
-                                           (1, 64, 2, 2, 64)])
+                                           (1, 64, 2, 2, 64),
+                                           # more workgroups than CUs: one 256-row q-tile per
+                                           # workgroup, ragged last tiles
+                                           (1, 1100, 64, 8, 64), (2, 700, 48, 6, 128)])
 def test_attention(x, B, k, Hq, Hkv, hd):
     say(f"[attention] B{B} k{k} Hq{Hq} Hkv{Hkv} hd{hd}")
     rng = np.random.default_rng(13)
