@@ -10,8 +10,11 @@
 // with dK and dV summed over the query heads that share a key/value head (grouped-query
 // attention). Two kernels, no atomics:
 //  * dQ: one wave per 32 queries, the forward's layout (the lane owns a query and 16 scores of
-//    each 32-key block); key/value tiles of 64 rows stream through a two-stage LDS ring; workgroups
-//    pair an early and a late query tile so every workgroup has the same causal work.
+//    each 32-key block); key/value tiles of 64 rows stream through a two-stage LDS ring. A
+//    workgroup's 256 queries are one tile of 256 rows (latest tiles dispatched first) when the
+//    grid holds more workgroups than CUs, so both waves of every SIMD stay busy to the last key
+//    tile; else an early and a late tile of 128 rows, so every workgroup has the same causal
+//    work and the longest one holds half as many long rows.
 //  * dK/dV: one wave per 32 keys (the lane owns a key and 16 scores of each 32-query block); the
 //    wave's key and value fragments stay in registers while query and dO tiles of 64 rows (with
 //    their lse and D) stream through the ring, over every query head of the group.
@@ -130,29 +133,38 @@ template <int HD>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(
     const uint16_t *__restrict__ qkv, int ldq, const uint16_t *__restrict__ dO, int lddo,
     const float *__restrict__ lse, const float *__restrict__ Dl, uint16_t *__restrict__ dqkv,
-    int ldd, int k, int Hq, int Hkv, float scale_log2, float scale) {
+    int ldd, int k, int Hq, int Hkv, float scale_log2, float scale, int paired) {
   using C = BwdCfg<HD>;
-  constexpr int BQ = 128, BKV = 64, KS = C::KS, NT_HD = C::NT_HD;
+  constexpr int BQ = 256, BQP = 128, BKV = 64, KS = C::KS, NT_HD = C::NT_HD;
   constexpr int TILE = BKV * HD, STAGE = 2 * TILE;       // K tile, then V tile
   constexpr int NBLK = 2 * TILE * 2 / 1024, NDMA = NBLK / 8;
   static_assert(NBLK % 8 == 0, "DMA blocks split over the eight waves");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
 
-  const int h = blockIdx.y, b = blockIdx.z, p = blockIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y, u = blockIdx.z;
   const int64_t row0 = (int64_t)b * k;
-  const int nqt = (k + BQ - 1) / BQ;
-  const int qt_hi = nqt - 1 - p;
   const int gkv = (h * Hkv) / Hq;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int gq = lane >> 5, r32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(wid);
-  const int half = wid >> 2;
-  const bool active = half == 0 || p != qt_hi;
-  const int qt = half == 0 ? qt_hi : p;
-  const int q_first = qt * BQ + (wid & 3) * 32;
+  // this wave's first query, whether it has a share, and the workgroup's last query + 1
+  int q_first, key_hi;
+  bool active;
+  if (paired) {
+    const int nqt = (k + BQP - 1) / BQP, qt_hi = nqt - 1 - u;
+    const bool later = wid < 4;
+    q_first = (later ? qt_hi : u) * BQP + (wid & 3) * 32;
+    active = later || u != qt_hi;  // the middle tile of an odd count: waves 0-3 only
+    key_hi = min(qt_hi * BQP + BQP, k);
+  } else {
+    const int qt = (k + BQ - 1) / BQ - 1 - u;
+    q_first = qt * BQ + wid * 32;
+    active = true;
+    key_hi = min(qt * BQ + BQ, k);
+  }
+  active = active && q_first < k;  // a ragged last tile leaves later waves empty
   const int q_pos = q_first + r32;
   const int q_last = active ? q_first + 31 : -1;
-  const int key_hi = min(qt_hi * BQ + BQ, k);
   const int n_kv = (key_hi + BKV - 1) / BKV;
   const char *kbase = (const char *)(qkv + row0 * ldq + Hq * HD + gkv * HD);
   const char *vbase = kbase + (size_t)Hkv * HD * 2;
@@ -464,21 +476,24 @@ hipError_t launch_attention_bwd(const uint16_t *qkv, int ld_qkv, const uint16_t 
   const float scale = 1.0f / sqrtf((float)hd);
   const float scale_log2 = 1.4426950408889634f * scale;
   const dim3 g_delta((unsigned)((rows + 3) / 4));
-  const int nqt = (k + 127) / 128;
-  const dim3 g_dq((unsigned)((nqt + 1) / 2), (unsigned)Hq, (unsigned)B);
+  // dQ grid (head, sequence, unit), the unit slowest: 256-row q-tiles when there are more of
+  // them than CUs, else pairs of 128-row tiles
+  const int nqt = (k + 255) / 256;
+  const int paired = (long)Hq * B * nqt <= 256;  // MI355X: 256 CUs
+  const dim3 g_dq((unsigned)Hq, (unsigned)B, (unsigned)(paired ? ((k + 127) / 128 + 1) / 2 : nqt));
   const dim3 g_kv((unsigned)((k + 127) / 128), (unsigned)Hkv, (unsigned)B);
   if (hd == 128) {
     hipLaunchKernelGGL(attn_bwd_delta_kernel<128>, g_delta, dim3(256), 0, s, o, ld_o, dO, ld_do, D,
                        rows, Hq);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g_dq, dim3(512), 0, s, qkv, ld_qkv, dO, ld_do, lse,
-                       D, dqkv, ld_dqkv, k, Hq, Hkv, scale_log2, scale);
+                       D, dqkv, ld_dqkv, k, Hq, Hkv, scale_log2, scale, paired);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, g_kv, dim3(256), 0, s, qkv, ld_qkv, dO, ld_do,
                        lse, D, dqkv, ld_dqkv, k, Hq, Hkv, scale_log2, scale);
   } else {
     hipLaunchKernelGGL(attn_bwd_delta_kernel<64>, g_delta, dim3(256), 0, s, o, ld_o, dO, ld_do, D,
                        rows, Hq);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g_dq, dim3(512), 0, s, qkv, ld_qkv, dO, ld_do, lse,
-                       D, dqkv, ld_dqkv, k, Hq, Hkv, scale_log2, scale);
+                       D, dqkv, ld_dqkv, k, Hq, Hkv, scale_log2, scale, paired);
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g_kv, dim3(256), 0, s, qkv, ld_qkv, dO, ld_do,
                        lse, D, dqkv, ld_dqkv, k, Hq, Hkv, scale_log2, scale);
   }

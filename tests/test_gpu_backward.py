@@ -48,7 +48,10 @@ def _attn_terms(Q, Kt, Vt, dO, Hq, Hkv, hd):
 @pytest.mark.parametrize("B,k,Hq,Hkv,hd", [(2, 256, 4, 4, 64), (1, 333, 4, 2, 128),
                                            (3, 200, 8, 2, 64), (2, 512, 16, 16, 128),
                                            (1, 1, 2, 1, 128), (2, 65, 4, 4, 64),
-                                           (1, 129, 2, 2, 128), (1, 700, 8, 2, 128)])
+                                           (1, 129, 2, 2, 128), (1, 700, 8, 2, 128),
+                                           # more dQ workgroups than CUs: one 256-row q-tile
+                                           # per workgroup, ragged last tiles
+                                           (1, 600, 96, 8, 64), (2, 300, 96, 12, 128)])
 def test_attention_backward(x, B, k, Hq, Hkv, hd):
     say(f"[attention bwd] B{B} k{k} Hq{Hq} Hkv{Hkv} hd{hd}")
     rng = np.random.default_rng(21)
