@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   static_assert(NBLK % 4 == 0, "DMA blocks split over the four waves");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * STAGE];
 
-  const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y, kb = blockIdx.z;
   const int G = Hq / Hkv;
   const int64_t row0 = (int64_t)b * k;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -481,7 +481,9 @@ hipError_t launch_attention_bwd(const uint16_t *qkv, int ld_qkv, const uint16_t 
   const int nqt = (k + 255) / 256;
   const int paired = (long)Hq * B * nqt <= 256;  // MI355X: 256 CUs
   const dim3 g_dq((unsigned)Hq, (unsigned)B, (unsigned)(paired ? ((k + 127) / 128 + 1) / 2 : nqt));
-  const dim3 g_kv((unsigned)((k + 127) / 128), (unsigned)Hkv, (unsigned)B);
+  // dK/dV grid (key/value head, sequence, key block), the key block slowest: the first key
+  // blocks see the most queries, so every head's and sequence's longest workgroups go first
+  const dim3 g_kv((unsigned)Hkv, (unsigned)B, (unsigned)((k + 127) / 128));
   if (hd == 128) {
     hipLaunchKernelGGL(attn_bwd_delta_kernel<128>, g_delta, dim3(256), 0, s, o, ld_o, dO, ld_do, D,
                        rows, Hq);
