@@ -104,9 +104,11 @@ hipError_t launch_copy32(void *dst, const void *src, int64_t n_words, hipStream_
 }
 
 // Workgroups of the row kernels over the packed rows and over every token; each writes one
-// partial row of its column sums.
+// partial row of its column sums. The router pass over every token is HBM-bound: its grid is
+// what stays resident at once (three workgroups per CU at d = 2048), so no second, thinly
+// occupied round of workgroups trails the first.
 constexpr int BWD_ROW_WGS = 512;
-constexpr int BWD_ROUTE_WGS = 1024;
+constexpr int BWD_ROUTE_WGS = 768;
 
 // ---- gated residual ------------------------------------------------------------------------
 template <int NI>
