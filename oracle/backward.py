@@ -16,7 +16,7 @@ Sources (cited by page title and section / equation):
          only through the router weights that multiply the block output (top-k is a discrete
          choice and passes no gradient).
 
-Readings (listed in DESIGN.md):
+Readings:
   * The training objective of one layer is  <dy, y> + route_coef * L_route  for an upstream
     gradient dy of the hidden state; the top-k choice and the carried bias b receive no
     gradient (b is state, not a parameter); ell = s - tau*b, so d ell / d s = 1.

@@ -16,7 +16,7 @@ Sources (cited by page title and section / equation):
   [MODA] "Mixture-of-Depths Attention" reading notes, section 2.1 (GQA: query head h reads
          key/value head ceil(h/G), 1-based, G = Hq/Hkv).
 
-Readings taken where the pages are silent or ambiguous (all listed in the design doc):
+Readings taken where the pages are silent or ambiguous:
   * ell = s - tau*b, with the gate r = sigmoid(ell) taken from the biased logit (Eq. (8)).
   * Selection ranks fp32 ell, ties to the lower position; -0 equals +0. k = floor(T/K).
   * Selected rows are packed in ascending position; attention is causal over the selected

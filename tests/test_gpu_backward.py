@@ -110,7 +110,7 @@ def test_attention_backward(x, B, k, Hq, Hkv, hd):
 # ---------------------------------------------------------------------------------------------
 
 GRAD_NAMES = ("w_router", "g_attn", "w_qkv", "w_o", "g_ffn", "w_gate", "w_up", "w_down")
-# Tolerance (derivation in the design doc): gradients pass through at most eight bf16 roundings in
+# Tolerance: gradients pass through at most eight bf16 roundings in
 # series (saved activations, activation gradients, P and dS), each relative 2^-9, against two
 # for the forward's output; the forward's 5e-3 relative L2 scales to 2e-2, and no element may
 # stray further than 5e-2 of the tensor's largest magnitude.
