@@ -306,12 +306,15 @@ def threshold_select(ell):
     return [np.nonzero(ell[b] >= 0)[0].astype(np.int64) for b in range(ell.shape[0])]
 
 
-def sparse_layer_threshold(x, lay, dims, bias=None, tau=1.0, delta=0.0, sample=None):
+def sparse_layer_threshold(x, lay, dims, bias=None, tau=1.0, delta=0.0, sample=None,
+                           forced_sel=None):
     """Forward of one sparse layer with the eval-time causal threshold rule.
 
     Identical to sparse_layer except for the selection: every token with ell = s - tau*b >= 0
     enters (Eq. (8)'s r = sigmoid(ell) >= 1/2), so each sequence routes its own number of
     tokens k_b (0 .. T). The carried bias is updated on the selected tokens as in training.
+    forced_sel: a given selection (list of ascending position arrays, one per sequence) used
+    instead of the rule, as sparse_layer's forced_idx.
 
     Returns a dict with s, ell, idx (list of int64 arrays), counts (int64 [B]), gate (list),
     bias_out, and y or rows (as sparse_layer; sample: {b: packed rows of that sequence}).
@@ -322,7 +325,8 @@ def sparse_layer_threshold(x, lay, dims, bias=None, tau=1.0, delta=0.0, sample=N
         bias = np.zeros((B, T), dtype=np.float32)
     bias = np.asarray(bias, dtype=np.float32)
     s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
-    sel = threshold_select(ell)
+    sel = threshold_select(ell) if forced_sel is None else [np.asarray(v, dtype=np.int64)
+                                                             for v in forced_sel]
     res = _routed_layer(x, lay, dims, ell, sel, bias, delta, sample)
     res.update({"s": s, "ell": ell, "idx": sel,
                 "counts": np.array([len(v) for v in sel], dtype=np.int64)})
@@ -381,12 +385,13 @@ def attention_layer(x, lay, dims, sample=None):
     return out
 
 
-def routed_ffn_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0):
+def routed_ffn_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, forced_idx=None):
     """A routed FFN refinement of the Routed-FFN control: the router and top-1/K selection of
     the sparse layer, then only the FFN on the selected rows, y_S = X + varsigma * r * f with
     f = SwiGLU(RMSNorm(X; g_ffn)) (the gated residual of Eq. (7) with no attention part);
     unselected rows unchanged; b[S] += delta. Returns the same dict as sparse_layer (no
-    sampling: the FFN is row-local, so every row is cheap)."""
+    sampling: the FFN is row-local, so every row is cheap). forced_idx: a given selection
+    [B, k] instead of the top-k, as in sparse_layer."""
     x = _f64(x)
     B, T, d = x.shape
     k = T // K
@@ -395,7 +400,7 @@ def routed_ffn_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0):
         bias = np.zeros((B, T), dtype=np.float32)
     bias = np.asarray(bias, dtype=np.float32)
     s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
-    idx = topk_select(ell, k)
+    idx = topk_select(ell, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
     bsel = np.arange(B)[:, None]
     gate = sigmoid(ell[bsel, idx])
     bias_out = bias.copy()
@@ -410,13 +415,15 @@ def routed_ffn_layer(x, lay, dims, K, bias=None, tau=1.0, delta=0.0):
     return {"s": s, "ell": ell, "idx": idx, "gate": gate, "bias_out": bias_out, "y": y}
 
 
-def sparse_layer_fullkv(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, sample=None):
+def sparse_layer_fullkv(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, sample=None,
+                        forced_idx=None):
     """The Selected-Q/full-KV control: the sparse layer's router, selection, gate, FFN and
     residual (Eq. (7)), but every token of the sequence supplies keys and values: the query of
     a selected token at original position t attends to all tokens at positions <= t.
 
     u = RMSNorm(x; g_attn) over all rows; K, V from every row; Q from the selected rows;
-    optional QK-norm / RoPE at original positions. sample: None or {b: packed rows}."""
+    optional QK-norm / RoPE at original positions. sample: None or {b: packed rows};
+    forced_idx: a given selection [B, k] instead of the top-k, as in sparse_layer."""
     x = _f64(x)
     B, T, d = x.shape
     k = T // K
@@ -425,7 +432,7 @@ def sparse_layer_fullkv(x, lay, dims, K, bias=None, tau=1.0, delta=0.0, sample=N
         bias = np.zeros((B, T), dtype=np.float32)
     bias = np.asarray(bias, dtype=np.float32)
     s, ell = router_logits(x, lay["w_router"], lay.get("router_bias", 0.0), bias, tau)
-    idx = topk_select(ell, k)
+    idx = topk_select(ell, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
     bsel = np.arange(B)[:, None]
     gate = sigmoid(ell[bsel, idx])
     bias_out = bias.copy()

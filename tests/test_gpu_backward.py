@@ -125,7 +125,7 @@ LAYER_CASES = {
         varsigma_range=(0.5, 1.5)), 0.5),
     "B2 T1024 K4 d1024 GQA 8/2 hd128 F2816": (wl.Workload(
         "bw_gqa", 33, 2, 1024, 1024, 8, 2, 128, 2816, 4, gain_std=0.1), 1e-4),
-    "bench shape B8 T4096 K8 d2048": (wl.WORKLOADS[wl.BENCH_WORKLOAD], 1e-4),
+    "bench shape B8 T4096 K8 d2048": (wl.WORKLOADS["sparse_k8_b8x4096_d2048"], 1e-4),
     # degenerate cases: one routed token per sequence (62 zero padding rows in the
     # weight-gradient sums), every token routed (no unselected rows), no routing loss
     "k = 1 (B2 T50 K50 d256)": (wl.Workload("bw_k1", 34, 2, 50, 256, 4, 4, 64, 512, 50,

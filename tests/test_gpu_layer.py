@@ -1,10 +1,11 @@
 """End-to-end parity of one sparse layer and one dense layer: HIP path vs the oracle.
 
 Checks: selection equal to the oracle's (swaps allowed only between tokens whose oracle logits
-differ by < 1e-5; rows of a sequence after a swap are not compared, their attention context
-differs), unselected rows bit-identical, selected rows within max |diff| <= 2e-2 (+ half a bf16
-spacing) and relative L2 <= 5e-3, carried bias updated exactly. Full-size workloads are checked
-on sampled sequences / rows the oracle computes exactly, plus properties that hold at any size.
+differ by < 1e-5; a sequence holding a swap is compared in full against the oracle re-run with
+the GPU's selection), unselected rows bit-identical, selected rows within max |diff| <= 2e-2
+(+ half a bf16 spacing) and relative L2 <= 5e-3, gate and carried bias exact. Full-size
+workloads are checked on sampled sequences / rows the oracle computes exactly, plus properties
+that hold at any size.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 import oracle
 import workload as wl
 from parity import (bf16_vals, check_values, compare_selection, dev_bf16, host_bits, layer_to_device,
-                    say)
+                    max_swapped, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,40 +46,48 @@ def run_sparse_gpu(x, w, xb, lay, bias):
             None if bt is None else bt.cpu().numpy())
 
 
-def check_sparse(w, xb, lay, bias, got, sample=None, abs_tol=2e-2):
-    """Compare a GPU sparse-layer result with the oracle (full, or sampled sequences/rows)."""
+def check_sparse(w, xb, lay, bias, got, sample=None, abs_tol=2e-2, values=True):
+    """Compare a GPU sparse-layer result with the oracle (full, or sampled sequences/rows).
+
+    The GPU's selection must equal the oracle's up to swaps between near-tied logits (at most
+    a quarter of the sequences may hold one). Gate, carried bias and every output row are then
+    compared with the oracle evaluated on the GPU's own selection (forced_idx), which is the
+    oracle's result itself in every sequence without a swap; so no routed row goes unchecked.
+    Returns the oracle's result for the GPU's selection and the first differing packed position
+    of each sequence (k where the selections agree).
+    """
     y_bits, idx_g, gate_g, bias_g = got
     B, T, k = w.B, w.T, w.k
-    ref = oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=sample)
-    ell = ref["ell"]
-    first = compare_selection(idx_g, ref["idx"], ell)
+    sel_ref = oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
+                                  sample={})
+    first = compare_selection(idx_g, sel_ref["idx"], sel_ref["ell"])
+    n_swapped = int(np.sum(first < k))
+    assert n_swapped <= max_swapped(B), f"{n_swapped} of {B} sequences hold selection swaps"
     # every row the GPU did not select is bit-identical to the input
     sel = np.zeros((B, T), bool)
     sel[np.arange(B)[:, None], idx_g] = True
     assert np.array_equal(y_bits[~sel], xb[~sel]), "unselected rows changed"
+    ref = oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
+                              forced_idx=idx_g, sample=sample)
     # gate and bias follow the GPU's selection exactly (fp32 decisions on its own logits)
-    same = first == k
-    if same.any():
-        assert np.allclose(gate_g[same], ref["gate"][same], rtol=2e-6, atol=2e-6)
-        if bias_g is not None:
-            assert np.array_equal(bias_g[same], ref["bias_out"][same])
+    assert np.allclose(gate_g, ref["gate"], rtol=2e-6, atol=2e-6), "gate"
+    if bias_g is not None:
+        assert np.array_equal(bias_g, ref["bias_out"]), "carried bias"
+    if not values:
+        return ref, first
     yv = bf16_vals(y_bits)
     stats = []
     if sample is None:
         for b in range(B):
-            rows = idx_g[b, :first[b]]
-            if len(rows):
-                stats.append(check_values(yv[b, rows], ref["y"][b, rows], f"seq {b}", abs_tol=abs_tol))
+            stats.append(check_values(yv[b, idx_g[b]], ref["y"][b, idx_g[b]], f"seq {b}",
+                                      abs_tol=abs_tol))
     else:
         for b, (prow, pos, ysel) in ref["rows"].items():
-            keep = prow < first[b]
-            assert np.array_equal(pos[keep], idx_g[b, prow[keep]])
-            if keep.any():
-                stats.append(check_values(yv[b, pos[keep]], ysel[keep], f"seq {b} sampled",
-                                          abs_tol=abs_tol))
-    say(f"    swaps in {int(np.sum(first < k))} of {B} sequences; max|diff|, relL2 = "
-        f"{max(s[0] for s in stats):.3g}, {max(s[1] for s in stats):.3g}")
-    return ref
+            assert np.array_equal(pos, idx_g[b, prow])
+            stats.append(check_values(yv[b, pos], ysel, f"seq {b} sampled", abs_tol=abs_tol))
+    say(f"    swaps in {n_swapped} of {B} sequences (compared under the GPU's selection); "
+        f"max|diff|, relL2 = {max(s[0] for s in stats):.3g}, {max(s[1] for s in stats):.3g}")
+    return ref, first
 
 
 SMALL = {
@@ -158,8 +167,11 @@ def test_check4_varsigma_zero_is_identity(x):
 # full-size workloads: the launch configuration the benchmark times
 # ---------------------------------------------------------------------------------------------
 
+BENCH_LAYER = "sparse_k8_b8x4096_d2048"
+
+
 def test_bench_workload_full_size_sampled(x):
-    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    w = wl.WORKLOADS[BENCH_LAYER]
     say(f"[full size] {w.name}: GPU layer, oracle on sequences 0 and 5")
     xb = wl.make_x(w)
     lay = wl.make_layer(w, 0)
@@ -173,7 +185,7 @@ def test_bench_workload_full_size_sampled(x):
 
 
 def test_bench_workload_deterministic(x):
-    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    w = wl.WORKLOADS[BENCH_LAYER]
     say(f"[determinism] {w.name}: two runs, bitwise")
     xb = wl.make_x(w)
     lay = wl.make_layer(w, 0)
@@ -184,20 +196,32 @@ def test_bench_workload_deterministic(x):
         assert np.array_equal(u, v)
 
 
-# Long-context workload (d = 4096, F = 14336): here the bf16 rounding of the matrix-core
-# operands (u, Q/K/V, O, v, g) alone moves outputs by up to 0.05-0.07 from the float64 result on
-# these rows (a float64 model of the layer with exactly those roundings, and nothing else, shows
-# it), so the 2e-2 absolute bar is out of reach for any bf16-operand implementation. The stated
-# relative-L2 bar (5e-3) is kept; the absolute bar is 8e-2 + half a bf16 spacing of the output.
-LONG_CONTEXT_ABS_TOL = 8e-2
-
-
+# Long-context workload (d = 4096, F = 14336, 8192 routed rows): here the bf16 rounding of the
+# matrix-core operands (u, Q/K/V, P, O, v, g) alone moves the sampled outputs by about 0.05
+# from the float64 result (tests/bf16_model.py, measured in tests/test_bf16_model.py), so no
+# bf16-operand implementation meets 2e-2 against the oracle there. The GPU is held to 2e-2
+# (+ half a bf16 spacing) against that model, and to the model's own distance plus 2e-2 against
+# the oracle; the relative-L2 bar (5e-3) against the oracle is kept as stated.
 def test_long_context_gqa_full_size_sampled(x):
+    import bf16_model
     w = wl.WORKLOADS["sparse_k4_gqa_b1x32768_d4096"]
-    say(f"[full size] {w.name}: oracle on 128 sampled packed rows")
+    say(f"[full size] {w.name}: oracle and bf16-operand model on 128 sampled packed rows")
     xb = wl.make_x(w)
     lay = wl.make_layer(w, 0)
     got = run_sparse_gpu(x, w, xb, lay, None)
     assert np.all(np.isfinite(bf16_vals(got[0])))
     rows = np.concatenate([np.arange(0, 48), np.arange(4090, 4106), np.arange(w.k - 64, w.k)])
-    check_sparse(w, xb, lay, None, got, sample={0: rows}, abs_tol=LONG_CONTEXT_ABS_TOL)
+    sample = {0: rows}
+    ref, first = check_sparse(w, xb, lay, None, got, sample=sample, values=False)
+    prow, pos, y_ref = ref["rows"][0]
+    model = bf16_model.sparse_layer_rows(xb, lay, w, w.K, sample=sample, round_p=True,
+                                         forced_idx=got[1])
+    m_rows, m_pos, y_mod = model[0]
+    assert np.array_equal(m_pos, pos)
+    model_gap = float(np.max(np.abs(y_mod - y_ref)))
+    yv = bf16_vals(got[0])[0, pos]
+    strict = float(np.max(np.abs(yv - y_ref)))
+    say(f"    bf16-operand model vs oracle max|diff| {model_gap:.4g}; GPU vs oracle strict "
+        f"max|diff| {strict:.4g} (swap-free: {bool(first[0] == w.k)})")
+    check_values(yv, y_mod, "GPU vs bf16-operand model", abs_tol=2e-2)
+    check_values(yv, y_ref, "GPU vs oracle", abs_tol=model_gap + 2e-2)

@@ -2,7 +2,8 @@
 attention context", Table 7) on the GPU vs the oracle: the Routed-FFN control's routed FFN
 refinement and full-sequence attention block, and the Selected-Q/full-KV layer. Same bar as
 the sparse layer (selection swaps only at oracle logit gaps < 1e-5; unselected rows
-bit-identical; max |diff| <= 2e-2 + half a bf16 spacing, relative L2 <= 5e-3)."""
+bit-identical; max |diff| <= 2e-2 + half a bf16 spacing, relative L2 <= 5e-3; a sequence
+holding a swap is compared in full against the oracle re-run with the GPU's selection)."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +11,7 @@ import torch
 import oracle
 import workload as wl
 from parity import (bf16_vals, check_values, compare_selection, dev_bf16, host_bits,
-                    layer_to_device, say)
+                    layer_to_device, max_swapped, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,25 +43,31 @@ def _run(x, w, xb, lay, bias, entry, ws_id, K):
     return host_bits(xt), idx.cpu().numpy(), None if bt is None else bt.cpu().numpy()
 
 
-def _check_routed(w, xb, got, ref, what):
+def _check_routed(w, xb, got, ref, what, rerun=None, sample=None):
+    """rerun(b, idx_b, sample_b): the oracle on sequence b alone with the given selection; a
+    sequence holding a selection swap is compared in full under the GPU's selection."""
     y_bits, idx_g, bias_g = got
     k = w.T // w.K
     first = compare_selection(idx_g, ref["idx"], ref["ell"])
+    assert int(np.sum(first < k)) <= max_swapped(w.B)
     sel = np.zeros((w.B, w.T), bool)
     sel[np.arange(w.B)[:, None], idx_g] = True
     assert np.array_equal(y_bits[~sel], xb[~sel]), "unselected rows changed"
     yv = bf16_vals(y_bits)
     for b in range(w.B):
-        if bias_g is not None and first[b] == k:
-            assert np.array_equal(bias_g[b], ref["bias_out"][b])
-        rows = idx_g[b, :first[b]]
-        if len(rows):
-            if "rows" in ref:
-                prow, pos, ysel = ref["rows"][b]
-                keep = prow < first[b]
-                check_values(yv[b, pos[keep]], ysel[keep], f"{what} seq {b}")
-            else:
-                check_values(yv[b, rows], ref["y"][b, rows], f"{what} seq {b}")
+        r, bb, tag = ref, b, f"{what} seq {b}"
+        if first[b] < k:
+            sb = None if sample is None else {0: sample[b]} if b in sample else {}
+            r, bb, tag = rerun(b, idx_g[b:b + 1], sb), 0, tag + " (GPU selection)"
+        if bias_g is not None:
+            assert np.array_equal(bias_g[b], r["bias_out"][bb]), f"{tag}: carried bias"
+        if "rows" in r:
+            if bb in r["rows"]:
+                prow, pos, ysel = r["rows"][bb]
+                assert np.array_equal(pos, idx_g[b, prow])
+                check_values(yv[b, pos], ysel, tag + " sampled")
+        else:
+            check_values(yv[b, idx_g[b]], r["y"][bb, idx_g[b]], tag)
 
 
 ROUTED = {
@@ -80,7 +87,8 @@ def test_routed_ffn(x, name):
     bias = wl.make_bias(w)
     got = _run(x, w, xb, lay, bias, x.routed_ffn_fwd, x.WS_ROUTED_FFN, w.K)
     ref = oracle.routed_ffn_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta)
-    _check_routed(w, xb, got, ref, "routed FFN")
+    _check_routed(w, xb, got, ref, "routed FFN", rerun=lambda b, i, sb: oracle.routed_ffn_layer(
+        xb[b:b + 1], lay, w, w.K, bias=bias[b:b + 1], tau=w.tau, delta=w.delta, forced_idx=i))
 
 
 @pytest.mark.parametrize("w", [
@@ -129,11 +137,12 @@ def test_selected_q_full_kv(x, name):
     bias = wl.make_bias(w)
     got = _run(x, w, xb, lay, bias, x.sparse_layer_fwd_fullkv, x.WS_SPARSE_FULLKV, w.K)
     ref = oracle.sparse_layer_fullkv(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta)
-    _check_routed(w, xb, got, ref, "full KV")
+    _check_routed(w, xb, got, ref, "full KV", rerun=lambda b, i, sb: oracle.sparse_layer_fullkv(
+        xb[b:b + 1], lay, w, w.K, bias=bias[b:b + 1], tau=w.tau, delta=w.delta, forced_idx=i))
 
 
 def test_selected_q_full_kv_bench_shape_sampled(x):
-    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
+    w = wl.WORKLOADS["sparse_k8_b8x4096_d2048"]
     say(f"[Selected-Q/full-KV, full size] {w.name}: oracle on sequences 2 and 7")
     xb = wl.make_x(w)
     lay = wl.make_layer(w, 0)
@@ -141,11 +150,9 @@ def test_selected_q_full_kv_bench_shape_sampled(x):
     got = _run(x, w, xb, lay, bias, x.sparse_layer_fwd_fullkv, x.WS_SPARSE_FULLKV, w.K)
     k = w.T // w.K
     rows = np.concatenate([np.arange(24), np.arange(k - 24, k)])
+    sample = {2: rows, 7: rows}
     ref = oracle.sparse_layer_fullkv(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
-                                     sample={2: rows, 7: rows})
-    first = compare_selection(got[1], ref["idx"], ref["ell"])
-    yv = bf16_vals(got[0])
-    for b, (prow, pos, ysel) in ref["rows"].items():
-        keep = prow < first[b]
-        assert np.array_equal(pos[keep], got[1][b, prow[keep]])
-        check_values(yv[b, pos[keep]], ysel[keep], f"full KV seq {b} sampled")
+                                     sample=sample)
+    _check_routed(w, xb, got, ref, "full KV", sample=sample, rerun=lambda b, i, sb:
+                  oracle.sparse_layer_fullkv(xb[b:b + 1], lay, w, w.K, bias=bias[b:b + 1],
+                                             tau=w.tau, delta=w.delta, sample=sb, forced_idx=i))
