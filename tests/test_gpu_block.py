@@ -2,7 +2,10 @@
 
 * Lock-step: the oracle walks the whole stack on its own; every GPU layer is then fed the
   oracle's state at that layer's input (hidden state and carried bias) and compared with the
-  oracle's output of that layer. No GPU value ever enters the oracle.
+  oracle's output of that layer. No GPU value ever enters the oracle. Small stacks are walked
+  in full; the two stack workloads at their own shapes on one sequence (the oracle's cost),
+  with the GPU running the whole batch in the launch configuration the benchmark times.
+* A sequence's output does not depend on the batch it runs in (bitwise).
 * The block entry point equals the same layers called one by one (bitwise), at full size.
 * Free-running properties: with varsigma = 0 in the sparse layers (x frozen) and a bias step
   far above the logit range, the carried bias rotates the selection so each token is chosen
@@ -15,7 +18,7 @@ import torch
 import oracle
 import workload as wl
 from parity import (bf16_vals, check_values, compare_selection, dev_bf16, host_bits,
-                    layer_to_device, say)
+                    layer_to_device, max_swapped, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +40,26 @@ REDUCED = {
     "A1.5K4 block: D + ([S(4)]x6 + D)x2, B2 T512 d256 GQA 4/2": wl.Workload(
         "xmod_small", 32, 2, 512, 256, 4, 2, 64, 512, 4, N0=1, N1=2, AK=6, delta=0.05),
 }
+
+
+def check_lockstep_sparse(w, l, lay, e, seqs, y_bits, idx_g, bias_g, xin):
+    """One GPU sparse layer fed the oracle's state e (x_in, bias_in) against the oracle's output
+    of that layer, on sequences seqs (y_bits, idx_g, bias_g, xin: those sequences' rows). The
+    selection follows the swap rule; a sequence holding a swap is compared in full against the
+    oracle re-run on the GPU's selection (forced_idx), so every routed row is checked."""
+    first = compare_selection(idx_g, e["idx"][seqs], e["ell"][seqs])
+    assert int(np.sum(first < w.k)) <= max_swapped(len(seqs)), f"layer {l}: selection swaps"
+    sel = np.zeros((len(seqs), w.T), bool)
+    sel[np.arange(len(seqs))[:, None], idx_g] = True
+    assert np.array_equal(y_bits[~sel], xin[~sel]), f"layer {l}: unselected rows changed"
+    for i, b in enumerate(seqs):
+        y_ref, b_ref, tag = e["y"][b], e["bias_out"][b], f"layer {l} seq {b}"
+        if first[i] < w.k:
+            r = oracle.sparse_layer(e["x_in"][b:b + 1], lay, w, w.K, bias=e["bias_in"][b:b + 1],
+                                    tau=w.tau, delta=w.delta, forced_idx=idx_g[i:i + 1])
+            y_ref, b_ref, tag = r["y"][0], r["bias_out"][0], tag + " (GPU selection)"
+        assert np.array_equal(bias_g[i], b_ref), f"{tag}: carried bias"
+        check_values(bf16_vals(y_bits[i, idx_g[i]]), y_ref[idx_g[i]], tag)
 
 
 @pytest.mark.parametrize("name", list(REDUCED))
@@ -63,17 +86,81 @@ def test_block_lockstep(x, name):
         idx = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
         x.sparse_layer_fwd(xt, L, dims, w.K, bt, w.tau, w.delta, ws, idx, None)
         torch.cuda.synchronize()
-        idx_g = idx.cpu().numpy()
-        first = compare_selection(idx_g, e["idx"], e["ell"])
-        y = host_bits(xt)
-        sel = np.zeros((w.B, w.T), bool)
-        sel[np.arange(w.B)[:, None], idx_g] = True
-        assert np.array_equal(y[~sel], xin[~sel]), f"layer {l}: unselected rows changed"
-        same = first == w.k
-        assert np.array_equal(bt.cpu().numpy()[same], e["bias_out"][same]), f"layer {l}: bias"
-        for b in range(w.B):
-            rows = idx_g[b, :first[b]]
-            check_values(bf16_vals(y[b, rows]), e["y"][b, rows], f"layer {l} seq {b}")
+        check_lockstep_sparse(w, l, layers[l], e, np.arange(w.B), host_bits(xt),
+                              idx.cpu().numpy(), bt.cpu().numpy(), xin)
+
+
+FULL_STACKS = ["mod_pairs_k8_b4x4096_d1536", "a3k16_block_b4x4096_d1024"]
+
+
+@pytest.mark.parametrize("name", FULL_STACKS)
+def test_block_lockstep_full_shape(x, name):
+    """Lock-step at the stack workloads' own shapes and launch configuration: the oracle walks
+    sequence 0 of the workload's inputs through every layer; the GPU runs every layer on the
+    whole batch, sequence 0 fed the oracle's hidden state and carried bias at that layer's
+    input, the other sequences carrying the GPU's own state from layer to layer. Every layer's
+    output for sequence 0 is compared with the oracle's (for the MoD pairs: after each sparse
+    and each dense layer, so after each pair; for the A3K16 block: the dense prefix, all 48
+    sparse layers and the anchor)."""
+    w = wl.WORKLOADS[name]
+    kinds = w.layer_kinds()
+    say(f"[lock-step, full size] {name}: {''.join(kinds)}; oracle on sequence 0")
+    xb = wl.make_x(w)
+    layers = [wl.make_layer(w, l) for l in range(len(kinds))]
+    _, trace = oracle.block_forward(xb[:1], layers, w, kinds, w.K, tau=w.tau, delta=w.delta,
+                                    record=True)
+    say(f"    oracle walk done ({len(trace)} layers)")
+    dims = _dims(x, w)
+    ws = x.alloc_workspace(dims, w.K, x.WS_BLOCK)
+    xt = dev_bf16(xb)
+    bt = torch.zeros((w.B, w.T), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    for l, (kind, e) in enumerate(zip(kinds, trace)):
+        if l >= w.N0 and (l - w.N0) % (w.AK + 1) == 0:
+            bt.zero_()                                   # start of a block (the library's rule)
+        xin0 = oracle.f64_to_bf16_bits(e["x_in"])       # [1, T, d]
+        xt[0].copy_(dev_bf16(xin0[0]))
+        bt[0].copy_(torch.from_numpy(e["bias_in"][0].copy()))
+        dl = layer_to_device(layers[l])
+        L = x.make_layer(dl)
+        if kind == "D":
+            x.dense_layer_fwd(xt, L, dims, ws)
+            torch.cuda.synchronize()
+            check_values(bf16_vals(host_bits(xt[0])), e["y"][0], f"layer {l} (dense) seq 0")
+        else:
+            x.sparse_layer_fwd(xt, L, dims, w.K, bt, w.tau, w.delta, ws, idx, None)
+            torch.cuda.synchronize()
+            check_lockstep_sparse(w, l, layers[l], e, np.array([0]), host_bits(xt[:1]),
+                                  idx.cpu().numpy()[:1], bt.cpu().numpy()[:1], xin0)
+        assert np.all(np.isfinite(bf16_vals(host_bits(xt[1:])))), f"layer {l}: other sequences"
+        del dl, L
+
+
+@pytest.mark.parametrize("name", FULL_STACKS)
+def test_block_sequence_independent_of_batch(x, name):
+    """A sequence's block output does not depend on the batch it runs in (bitwise): sequence 0
+    of the full-batch block equals the block on sequence 0 alone, although the two launch
+    different grids (and, for the pairs' dense layers, a different attention work split). With
+    the full-batch block equal to the layers called one by one (the next test), the per-sequence
+    lock-step above covers every sequence of the full-size block."""
+    w = wl.WORKLOADS[name]
+    say(f"[batch independence] {name}")
+    kinds, _, dev, Ls = _gpu_layers(x, w)
+    xb = wl.make_x(w)
+    A = w.AK / w.K
+    outs = []
+    for B in (w.B, 1):
+        wb = wl.scaled(w, B=B)
+        dims = _dims(x, wb)
+        ws = x.alloc_workspace(dims, w.K, x.WS_BLOCK)
+        xt = dev_bf16(xb[:B])
+        bt = torch.empty((B, w.T), dtype=torch.float32, device="cuda")
+        x.block_fwd(xt, Ls, dims, w.N0, w.N1, A, w.K, bt, w.tau, w.delta, ws)
+        torch.cuda.synchronize()
+        outs.append((host_bits(xt[:1]), bt[:1].cpu().numpy()))
+        del ws
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
 
 
 def _gpu_layers(x, w, seed_shift=0):
