@@ -125,6 +125,87 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# Every tensor handed to the library lives on the ROCm device ("cuda" in torch's naming).
+_DEVICE_TYPE = "cuda"
+_BF16, _F32, _I32, _U8 = torch.bfloat16, torch.float32, torch.int32, torch.uint8
+
+
+def _arg(t, name, dtype, n=None, at_least=None, optional=False):
+    """Raw device pointer of tensor t, after the host checks the C ABI cannot make behind a bare
+    pointer: a device tensor of the expected dtype, contiguous, with exactly n (or at least
+    at_least) elements. A wrong buffer raises here, before any kernel is launched."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.device.type != _DEVICE_TYPE:
+        raise ValueError(f"{name}: expected a {_DEVICE_TYPE} tensor, got {t.device}")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name}: expected dtype {' or '.join(map(str, dts))}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+    if at_least is not None and t.numel() < at_least:
+        raise ValueError(f"{name}: expected at least {at_least} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _mat(t, name, dtype, rows, cols):
+    """A 2-D row-major operand with unit column stride and at least rows x cols elements;
+    returns (pointer, leading dimension in elements)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.device.type != _DEVICE_TYPE:
+        raise ValueError(f"{name}: expected a {_DEVICE_TYPE} tensor, got {t.device}")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name}: expected dtype {' or '.join(map(str, dts))}, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) < t.shape[1]):
+        raise ValueError(f"{name}: expected a 2-D row-major matrix with unit column stride")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name}: expected at least {rows} x {cols}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr()), int(t.stride(0))
+
+
+def _ws(ws, name="ws"):
+    _arg(ws, name, _U8)
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel()
+
+
+def _bt(dims):
+    return dims.B * dims.T
+
+
+def _x(x, dims, name="x"):
+    return _arg(x, name, _BF16, n=dims.B * dims.T * dims.d)
+
+
+def _check_layer(layer, dims, sparse=True, fields=None):
+    """The weights a layer struct points to: bf16 device tensors of the shapes dims implies."""
+    w = getattr(layer, "_tensors", None)
+    if w is None:
+        raise ValueError("layer: build it with make_layer (it keeps the weight tensors)")
+    d, F = dims.d, dims.ffn_hidden
+    dq, dkv = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    sizes = {"w_router": d, "g_attn": d, "w_qkv": (dq + 2 * dkv) * d, "w_o": d * dq, "g_ffn": d,
+             "w_gate": F * d, "w_up": F * d, "w_down": d * F}
+    need = fields if fields is not None else [n for n in sizes if sparse or n != "w_router"]
+    for n in sizes:
+        _arg(w.get(n), f"layer.{n}", _BF16, n=sizes[n], optional=n not in need)
+    for n in ("q_norm", "k_norm"):
+        _arg(w.get(n), f"layer.{n}", _BF16, n=dims.head_dim, optional=True)
+
+
+def _k(dims, K):
+    if K < 1 or dims.T // K < 1:
+        raise ValueError(f"K = {K}: floor(T/K) must be at least 1")
+    return dims.T // K
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -139,7 +220,8 @@ def make_layer(w: dict) -> Layer:
     w_down, optional q_norm / k_norm, and host values router_bias, varsigma, optional residual
     (0 or 1) and rope_theta. The returned struct holds raw device pointers; it keeps a
     reference to the tensors so that they outlive it (a caller passing a temporary dict would
-    otherwise hand the library freed memory that the allocator gives to the next tensor)."""
+    otherwise hand the library freed memory that the allocator gives to the next tensor).
+    The entry points check the tensors' dtype, device and sizes against their dims."""
     L = Layer(_ptr(w.get("w_router")), float(w.get("router_bias", 0.0)),
               float(w.get("varsigma", 1.0)), _ptr(w["g_attn"]), _ptr(w["w_qkv"]),
               _ptr(w["w_o"]), _ptr(w["g_ffn"]), _ptr(w["w_gate"]), _ptr(w["w_up"]),
@@ -159,35 +241,62 @@ def alloc_workspace(dims: Dims, K: int, entry: int, device="cuda"):
 
 
 def route_topk(x, w_router, router_bias, bias, tau, K, dims, logits, idx, gate, stream=None):
-    _check(lib.xmod_route_topk(_ptr(x), _ptr(w_router), router_bias, _ptr(bias), tau, K,
-                               ctypes.byref(dims), _ptr(logits), _ptr(idx), _ptr(gate), None, 0,
-                               _stream(stream)), "xmod_route_topk")
+    k = _k(dims, K)
+    args = (_x(x, dims), _arg(w_router, "w_router", _BF16, n=dims.d))
+    bias_p = _arg(bias, "bias", _F32, n=_bt(dims), optional=True)
+    outs = (_arg(logits, "logits", _F32, n=_bt(dims)), _arg(idx, "idx", _I32, at_least=dims.B * k),
+            _arg(gate, "gate", _F32, at_least=dims.B * k))
+    _check(lib.xmod_route_topk(args[0], args[1], router_bias, bias_p, tau, K, ctypes.byref(dims),
+                               *outs, None, 0, _stream(stream)), "xmod_route_topk")
 
 
 def topk_from_logits(logits, k, idx, gate=None, bias=None, delta=0.0, stream=None):
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [B, T]")
     B, T = logits.shape
-    _check(lib.xmod_topk_from_logits(_ptr(logits), B, T, k, _ptr(idx), _ptr(gate), _ptr(bias),
-                                     delta, _stream(stream)), "xmod_topk_from_logits")
+    lp = _arg(logits, "logits", _F32)
+    ip = _arg(idx, "idx", _I32, at_least=B * k)
+    gp = _arg(gate, "gate", _F32, at_least=B * k, optional=True)
+    bp = _arg(bias, "bias", _F32, n=B * T, optional=True)
+    _check(lib.xmod_topk_from_logits(lp, B, T, k, ip, gp, bp, delta, _stream(stream)),
+           "xmod_topk_from_logits")
 
 
 def pack(x, idx, x_packed, stream=None):
+    if x.dim() != 3 or idx.dim() != 2 or idx.shape[0] != x.shape[0]:
+        raise ValueError("pack: x [B, T, d] and idx [B, k] expected")
     B, T, d = x.shape
-    _check(lib.xmod_pack(_ptr(x), _ptr(idx), B, T, d, idx.shape[1], _ptr(x_packed),
-                         _stream(stream)), "xmod_pack")
+    k = idx.shape[1]
+    xp, ip = _arg(x, "x", _BF16), _arg(idx, "idx", _I32)
+    op = _arg(x_packed, "x_packed", _BF16, at_least=B * k * d)
+    _check(lib.xmod_pack(xp, ip, B, T, d, k, op, _stream(stream)), "xmod_pack")
 
 
 def scatter_gated(x, idx, gate, varsigma, a_packed, f_packed, stream=None):
+    if x.dim() != 3 or idx.dim() != 2 or idx.shape[0] != x.shape[0]:
+        raise ValueError("scatter_gated: x [B, T, d] and idx [B, k] expected")
     B, T, d = x.shape
-    _check(lib.xmod_scatter_gated(_ptr(x), _ptr(idx), _ptr(gate), varsigma, _ptr(a_packed),
-                                  _ptr(f_packed), B, T, d, idx.shape[1], _stream(stream)),
-           "xmod_scatter_gated")
+    k = idx.shape[1]
+    ptrs = (_arg(x, "x", _BF16), _arg(idx, "idx", _I32), _arg(gate, "gate", _F32, n=B * k))
+    ap = _arg(a_packed, "a_packed", _BF16, at_least=B * k * d)
+    fp = _arg(f_packed, "f_packed", _BF16, at_least=B * k * d)
+    _check(lib.xmod_scatter_gated(ptrs[0], ptrs[1], ptrs[2], varsigma, ap, fp, B, T, d, k,
+                                  _stream(stream)), "xmod_scatter_gated")
+
+
+def _routed_args(x, layer, dims, K, bias, ws, idx_out, gate_out, fields=None):
+    k = _k(dims, K)
+    _check_layer(layer, dims, True, fields)
+    return (_x(x, dims), _arg(bias, "bias", _F32, n=_bt(dims), optional=True),
+            _arg(idx_out, "idx_out", _I32, at_least=dims.B * k, optional=True),
+            _arg(gate_out, "gate_out", _F32, at_least=dims.B * k, optional=True), *_ws(ws))
 
 
 def sparse_layer_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_out=None,
                      gate_out=None, stream=None):
-    _check(lib.xmod_sparse_layer_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
-                                     _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
-                                     _ptr(ws), ws.numel(), _stream(stream)),
+    xp, bp, ip, gp, wp, wn = _routed_args(x, layer, dims, K, bias, ws, idx_out, gate_out)
+    _check(lib.xmod_sparse_layer_fwd(xp, ctypes.byref(layer), ctypes.byref(dims), K, bp, tau,
+                                     delta, ip, gp, wp, wn, _stream(stream)),
            "xmod_sparse_layer_fwd")
 
 
@@ -210,87 +319,142 @@ def alloc_grads(dims: Dims, device="cuda") -> dict:
 
 def sparse_layer_fwd_train(x, layer: Layer, dims: Dims, K, bias, tau, delta, saved, idx_out=None,
                            gate_out=None, stream=None):
-    _check(lib.xmod_sparse_layer_fwd_train(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
-                                           _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
-                                           _ptr(saved), saved.numel(), _stream(stream)),
+    xp, bp, ip, gp, wp, wn = _routed_args(x, layer, dims, K, bias, saved, idx_out, gate_out)
+    _check(lib.xmod_sparse_layer_fwd_train(xp, ctypes.byref(layer), ctypes.byref(dims), K, bp,
+                                           tau, delta, ip, gp, wp, wn, _stream(stream)),
            "xmod_sparse_layer_fwd_train")
 
 
 def sparse_layer_bwd(x, dy, dx, layer: Layer, dims: Dims, K, route_coef, saved, grads: Grads,
                      ws, loss_route=None, stream=None):
-    _check(lib.xmod_sparse_layer_bwd(_ptr(x), _ptr(dy), _ptr(dx), ctypes.byref(layer),
-                                     ctypes.byref(dims), K, route_coef, _ptr(saved), saved.numel(),
-                                     ctypes.byref(grads), _ptr(loss_route), _ptr(ws), ws.numel(),
-                                     _stream(stream)), "xmod_sparse_layer_bwd")
+    _k(dims, K)
+    _check_layer(layer, dims, True)
+    ptrs = (_x(x, dims), _x(dy, dims, "dy"), _x(dx, dims, "dx"))
+    sp, sn = _ws(saved, "saved")
+    wp, wn = _ws(ws)
+    d, F = dims.d, dims.ffn_hidden
+    dq, dkv = dims.n_q_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    sizes = {"w_router": d, "router_bias": 1, "varsigma": 1, "g_attn": d,
+             "w_qkv": (dq + 2 * dkv) * d, "w_o": d * dq, "g_ffn": d, "w_gate": F * d,
+             "w_up": F * d, "w_down": d * F}
+    gt = getattr(grads, "_tensors", None)
+    if gt is None:
+        raise ValueError("grads: build it with make_grads (it keeps the gradient tensors)")
+    for n in GRAD_FIELDS:
+        _arg(gt.get(n), f"grads.{n}", _F32, n=sizes[n])
+    lp = _arg(loss_route, "loss_route", _F32, at_least=1, optional=True)
+    _check(lib.xmod_sparse_layer_bwd(ptrs[0], ptrs[1], ptrs[2], ctypes.byref(layer),
+                                     ctypes.byref(dims), K, route_coef, sp, sn,
+                                     ctypes.byref(grads), lp, wp, wn, _stream(stream)),
+           "xmod_sparse_layer_bwd")
 
 
 def threshold_select(logits, counts, offsets, src, n_total, gate=None, bias=None, delta=0.0,
                      stream=None):
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [B, T]")
     B, T = logits.shape
-    _check(lib.xmod_threshold_select(_ptr(logits), B, T, _ptr(counts), _ptr(offsets), _ptr(src),
-                                     _ptr(gate), _ptr(n_total), _ptr(bias), delta,
+    ptrs = (_arg(logits, "logits", _F32), _arg(counts, "counts", _I32, at_least=B),
+            _arg(offsets, "offsets", _I32, at_least=B), _arg(src, "src", _I32, at_least=B * T))
+    gp = _arg(gate, "gate", _F32, at_least=B * T, optional=True)
+    np_ = _arg(n_total, "n_total", _I32, at_least=1)
+    bp = _arg(bias, "bias", _F32, n=B * T, optional=True)
+    _check(lib.xmod_threshold_select(ptrs[0], B, T, ptrs[1], ptrs[2], ptrs[3], gp, np_, bp, delta,
                                      _stream(stream)), "xmod_threshold_select")
 
 
 def sparse_layer_fwd_threshold(x, layer: Layer, dims: Dims, bias, tau, delta, ws, src_out=None,
                                counts_out=None, n_total_out=None, stream=None):
-    _check(lib.xmod_sparse_layer_fwd_threshold(_ptr(x), ctypes.byref(layer), ctypes.byref(dims),
-                                               _ptr(bias), tau, delta, _ptr(src_out),
-                                               _ptr(counts_out), _ptr(n_total_out), _ptr(ws),
-                                               ws.numel(), _stream(stream)),
+    _check_layer(layer, dims, True)
+    xp = _x(x, dims)
+    bp = _arg(bias, "bias", _F32, n=_bt(dims), optional=True)
+    sp = _arg(src_out, "src_out", _I32, at_least=_bt(dims), optional=True)
+    cp = _arg(counts_out, "counts_out", _I32, at_least=dims.B, optional=True)
+    tp = _arg(n_total_out, "n_total_out", _I32, at_least=1, optional=True)
+    wp, wn = _ws(ws)
+    _check(lib.xmod_sparse_layer_fwd_threshold(xp, ctypes.byref(layer), ctypes.byref(dims), bp,
+                                               tau, delta, sp, cp, tp, wp, wn, _stream(stream)),
            "xmod_sparse_layer_fwd_threshold")
 
 
 def mask_agreement(logits, idx, agree, stream=None):
+    if logits.dim() != 2 or idx.dim() != 2 or idx.shape[0] != logits.shape[0]:
+        raise ValueError("mask_agreement: logits [B, T] and idx [B, k] expected")
     B, T = logits.shape
-    _check(lib.xmod_mask_agreement(_ptr(logits), _ptr(idx), B, T, idx.shape[1], _ptr(agree),
+    ptrs = (_arg(logits, "logits", _F32), _arg(idx, "idx", _I32),
+            _arg(agree, "agree", (_I32, torch.uint32) if hasattr(torch, "uint32") else _I32,
+                 at_least=1))
+    _check(lib.xmod_mask_agreement(ptrs[0], ptrs[1], B, T, idx.shape[1], ptrs[2],
                                    _stream(stream)), "xmod_mask_agreement")
 
 
 def routed_ffn_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_out=None,
                    gate_out=None, stream=None):
-    _check(lib.xmod_routed_ffn_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
-                                   _ptr(bias), tau, delta, _ptr(idx_out), _ptr(gate_out),
-                                   _ptr(ws), ws.numel(), _stream(stream)), "xmod_routed_ffn_fwd")
+    xp, bp, ip, gp, wp, wn = _routed_args(
+        x, layer, dims, K, bias, ws, idx_out, gate_out,
+        fields=["w_router", "g_ffn", "w_gate", "w_up", "w_down"])
+    _check(lib.xmod_routed_ffn_fwd(xp, ctypes.byref(layer), ctypes.byref(dims), K, bp, tau, delta,
+                                   ip, gp, wp, wn, _stream(stream)), "xmod_routed_ffn_fwd")
 
 
 def attention_layer_fwd(x, layer: Layer, dims: Dims, ws, stream=None):
-    _check(lib.xmod_attention_layer_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims),
-                                        _ptr(ws), ws.numel(), _stream(stream)),
-           "xmod_attention_layer_fwd")
+    _check_layer(layer, dims, False, fields=["g_attn", "w_qkv", "w_o"])
+    xp = _x(x, dims)
+    wp, wn = _ws(ws)
+    _check(lib.xmod_attention_layer_fwd(xp, ctypes.byref(layer), ctypes.byref(dims), wp, wn,
+                                        _stream(stream)), "xmod_attention_layer_fwd")
 
 
 def sparse_layer_fwd_fullkv(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_out=None,
                             gate_out=None, stream=None):
-    _check(lib.xmod_sparse_layer_fwd_fullkv(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), K,
-                                            _ptr(bias), tau, delta, _ptr(idx_out),
-                                            _ptr(gate_out), _ptr(ws), ws.numel(),
-                                            _stream(stream)), "xmod_sparse_layer_fwd_fullkv")
+    xp, bp, ip, gp, wp, wn = _routed_args(x, layer, dims, K, bias, ws, idx_out, gate_out)
+    _check(lib.xmod_sparse_layer_fwd_fullkv(xp, ctypes.byref(layer), ctypes.byref(dims), K, bp,
+                                            tau, delta, ip, gp, wp, wn, _stream(stream)),
+           "xmod_sparse_layer_fwd_fullkv")
 
 
 def dense_layer_fwd(x, layer: Layer, dims: Dims, ws, stream=None):
-    _check(lib.xmod_dense_layer_fwd(_ptr(x), ctypes.byref(layer), ctypes.byref(dims), _ptr(ws),
-                                    ws.numel(), _stream(stream)), "xmod_dense_layer_fwd")
+    _check_layer(layer, dims, False)
+    xp = _x(x, dims)
+    wp, wn = _ws(ws)
+    _check(lib.xmod_dense_layer_fwd(xp, ctypes.byref(layer), ctypes.byref(dims), wp, wn,
+                                    _stream(stream)), "xmod_dense_layer_fwd")
 
 
 def block_fwd(x, layers: list, dims: Dims, N0, N1, A, K, bias, tau, delta, ws, stream=None):
+    ak = int(round(A * K))
+    _k(dims, K)
+    for i, L in enumerate(layers):
+        sparse = i >= N0 and (i - N0) % (ak + 1) < ak
+        _check_layer(L, dims, sparse)
+    xp = _x(x, dims)
+    bp = _arg(bias, "bias", _F32, n=_bt(dims))
+    wp, wn = _ws(ws)
     arr = (Layer * len(layers))(*layers)
-    _check(lib.xmod_block_fwd(_ptr(x), arr, len(layers), ctypes.byref(dims), N0, N1, A, K,
-                              _ptr(bias), tau, delta, _ptr(ws), ws.numel(), _stream(stream)),
-           "xmod_block_fwd")
+    _check(lib.xmod_block_fwd(xp, arr, len(layers), ctypes.byref(dims), N0, N1, A, K, bp, tau,
+                              delta, wp, wn, _stream(stream)), "xmod_block_fwd")
 
 
 def rmsnorm_rows(x, idx, gain, eps, k, out, stream=None):
+    if x.dim() != 3:
+        raise ValueError("rmsnorm_rows: x [B, T, d] expected")
     B, T, d = x.shape
-    _check(lib.xmod_rmsnorm_rows(_ptr(x), _ptr(idx), _ptr(gain), eps, B, T, d, k, _ptr(out),
-                                 _stream(stream)), "xmod_rmsnorm_rows")
+    xp = _arg(x, "x", _BF16)
+    ip = _arg(idx, "idx", _I32, n=B * k, optional=True)
+    gp = _arg(gain, "gain", _BF16, n=d)
+    op = _arg(out, "out", _BF16, at_least=B * k * d)
+    _check(lib.xmod_rmsnorm_rows(xp, ip, gp, eps, B, T, d, k, op, _stream(stream)),
+           "xmod_rmsnorm_rows")
 
 
 def gemm_bf16_nt(A, Bm, C, stream=None):
     M, K = A.shape
     N = Bm.shape[0]
-    _check(lib.xmod_gemm_bf16_nt(_ptr(A), A.stride(0), _ptr(Bm), Bm.stride(0), _ptr(C),
-                                 C.stride(0), M, N, K, _stream(stream)), "xmod_gemm_bf16_nt")
+    ap, lda = _mat(A, "A", _BF16, M, K)
+    bp, ldb = _mat(Bm, "B", _BF16, N, K)
+    cp, ldc = _mat(C, "C", _BF16, M, N)
+    _check(lib.xmod_gemm_bf16_nt(ap, lda, bp, ldb, cp, ldc, M, N, K, _stream(stream)),
+           "xmod_gemm_bf16_nt")
 
 
 def gemm_bf16(layout, A, Bm, C, stream=None):
@@ -301,25 +465,41 @@ def gemm_bf16(layout, A, Bm, C, stream=None):
     else:
         M, K = A.shape
     N = Bm.shape[0] if layout == GEMM_NT else Bm.shape[1]
+    ap, lda = _mat(A, "A", _BF16, *A.shape)
+    bp, ldb = _mat(Bm, "B", _BF16, *Bm.shape)
+    cp, ldc = _mat(C, "C", (_BF16, _F32), M, N)
     out_f32 = 1 if C.dtype == torch.float32 else 0
-    _check(lib.xmod_gemm_bf16(layout, _ptr(A), A.stride(0), _ptr(Bm), Bm.stride(0), _ptr(C),
-                              C.stride(0), out_f32, M, N, K, _stream(stream)), "xmod_gemm_bf16")
+    _check(lib.xmod_gemm_bf16(layout, ap, lda, bp, ldb, cp, ldc, out_f32, M, N, K,
+                              _stream(stream)), "xmod_gemm_bf16")
+
+
+def _attn_mats(qkv, o, B, k, Hq, Hkv, hd):
+    qp, ldq = _mat(qkv, "qkv", _BF16, B * k, (Hq + 2 * Hkv) * hd)
+    op, ldo = _mat(o, "o", _BF16, B * k, Hq * hd)
+    return qp, ldq, op, ldo
 
 
 def attention_fwd_lse(qkv, o, lse, B, k, Hq, Hkv, hd, stream=None):
-    _check(lib.xmod_attention_fwd_lse(_ptr(qkv), qkv.stride(0), _ptr(o), o.stride(0), _ptr(lse),
-                                      B, k, Hq, Hkv, hd, _stream(stream)), "xmod_attention_fwd_lse")
+    qp, ldq, op, ldo = _attn_mats(qkv, o, B, k, Hq, Hkv, hd)
+    lp = _arg(lse, "lse", _F32, at_least=B * k * Hq)
+    _check(lib.xmod_attention_fwd_lse(qp, ldq, op, ldo, lp, B, k, Hq, Hkv, hd, _stream(stream)),
+           "xmod_attention_fwd_lse")
 
 
 def attention_bwd(qkv, o, lse, dO, D, dqkv, B, k, Hq, Hkv, hd, stream=None):
-    _check(lib.xmod_attention_bwd(_ptr(qkv), qkv.stride(0), _ptr(o), o.stride(0), _ptr(lse),
-                                  _ptr(dO), dO.stride(0), _ptr(D), _ptr(dqkv), dqkv.stride(0), B,
-                                  k, Hq, Hkv, hd, _stream(stream)), "xmod_attention_bwd")
+    qp, ldq, op, ldo = _attn_mats(qkv, o, B, k, Hq, Hkv, hd)
+    lp = _arg(lse, "lse", _F32, at_least=B * k * Hq)
+    dop, ldd = _mat(dO, "dO", _BF16, B * k, Hq * hd)
+    Dp = _arg(D, "D", _F32, at_least=B * k * Hq)
+    gp, ldg = _mat(dqkv, "dqkv", _BF16, B * k, (Hq + 2 * Hkv) * hd)
+    _check(lib.xmod_attention_bwd(qp, ldq, op, ldo, lp, dop, ldd, Dp, gp, ldg, B, k, Hq, Hkv, hd,
+                                  _stream(stream)), "xmod_attention_bwd")
 
 
 def attention_fwd(qkv, o, B, k, Hq, Hkv, hd, stream=None):
-    _check(lib.xmod_attention_fwd(_ptr(qkv), qkv.stride(0), _ptr(o), o.stride(0), B, k, Hq, Hkv,
-                                  hd, _stream(stream)), "xmod_attention_fwd")
+    qp, ldq, op, ldo = _attn_mats(qkv, o, B, k, Hq, Hkv, hd)
+    _check(lib.xmod_attention_fwd(qp, ldq, op, ldo, B, k, Hq, Hkv, hd, _stream(stream)),
+           "xmod_attention_fwd")
 
 
 PHASES = ["router", "topk", "gather_rmsnorm", "qkv_gemm", "attention", "o_gemm",
@@ -337,7 +517,8 @@ PROBE_THREADS = 1024 * 256  # values the ceiling probes write (one per thread)
 def probe_mfma(out, iters, stream=None):
     """Back-to-back bf16 MFMAs on every SIMD (4 * iters per wave, 4096 waves); out: fp32
     tensor of PROBE_THREADS, each set to 64 * iters. Returns the flops enqueued."""
-    _check(lib.xmod_probe_mfma(_ptr(out), int(iters), _stream(stream)), "xmod_probe_mfma")
+    op = _arg(out, "out", _F32, at_least=PROBE_THREADS)
+    _check(lib.xmod_probe_mfma(op, int(iters), _stream(stream)), "xmod_probe_mfma")
     return 4096 * 4 * int(iters) * 32768
 
 
@@ -346,9 +527,11 @@ def probe_read(src, out, stream=None):
     PROBE_THREADS whose 32-bit wrap-around sum equals that of src's 32-bit words. Returns the
     bytes read."""
     nbytes = src.numel() * src.element_size()
+    sp = _arg(src, "src", src.dtype)
+    op = _arg(out, "out", _I32, at_least=PROBE_THREADS)
     lib.xmod_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                     ctypes.c_void_p]
-    _check(lib.xmod_probe_read(_ptr(src), nbytes, _ptr(out), _stream(stream)), "xmod_probe_read")
+    _check(lib.xmod_probe_read(sp, nbytes, op, _stream(stream)), "xmod_probe_read")
     return nbytes
 
 
