@@ -1,25 +1,31 @@
 """Throughput of one X-MoD Sparse(K) layer forward on one MI355X.
 
-Workload: the single Sparse(K=8) layer at B=8 x T=4096, d=2048, 16 heads x 128, SwiGLU hidden
-5632, bf16; 512 of 4096 tokens per sequence are routed (4096 routed rows per step). Weights
-N(0, 0.02), activations N(0, 1), carried bias N(0, 0.1), varsigma ~ U(0.5, 1.5), all seeded and
-synthetic. A step is one xmod_sparse_layer_fwd call (router, top-k, gather + RMSNorm, QKV GEMM,
-attention over the routed subset, O GEMM, residual + RMSNorm, gate/up GEMM with SwiGLU, down GEMM
-with the gated scatter back into x). Inputs are resident in HBM before timing starts; each step
-updates x and the carried bias in place, so consecutive steps act like a stack of layers that
-share weights (same shapes, same work per step).
+Headline workload: the long-context Sparse(K=4) layer with grouped-query attention, B=1 x
+T=32768, d=4096, 32 query / 8 key-value heads x 128, SwiGLU hidden 14336, bf16; 8192 of the
+32768 tokens are routed (8192 routed rows per step). Weights N(0, 0.02), activations N(0, 1)
+with 1 % of the rows scaled x8 (a skewed router distribution), all seeded and synthetic. A step
+is one xmod_sparse_layer_fwd call (router, top-k, gather + RMSNorm, QKV GEMM, attention over the
+routed subset, O GEMM, residual + RMSNorm, gate/up GEMM with SwiGLU, down GEMM with the gated
+scatter back into x).
 
-Before the W warm-up steps, untimed steps run for at least 0.2 s so that the clocks settle.
-Prints one JSON line: routed tokens/s over the K timed steps; the roofline of the dominant
-kernel (the gate/up GEMM), timed by HIP events the library records around that kernel in every
-timed step (two events per step); a per-kernel breakdown from K further steps with events
-around every kernel; informational lines for the eval-time threshold rule and one training
-step (forward + backward); the two stack workloads through the block entry point; the copy
-and read bandwidth, MFMA rate and vendor-library GEMM rates this GPU sustains (context for the
-fractions); and the CPU oracle timed on a bounded sample on this host.
+Protocol of the timed steps: before every step, outside its events, x and the carried bias are
+restored from pristine device copies and a 512 MiB scratch buffer is written (the 256 MB
+last-level cache holds no part of the layer's inputs), so each step starts from the same state
+with its inputs resident in HBM. Each step is bracketed by HIP events on the launch stream;
+ms_per_step is the median. Untimed steps run for at least 0.2 s first (the clocks settle), then
+the W warm-up steps.
+
+Prints one JSON line: routed tokens/s; the roofline of the dominant kernel (the gate/up GEMM),
+timed by HIP events the library records around that kernel in every timed step; a per-kernel
+breakdown from further steps with events around every kernel (cold, as the timed steps, and
+warm, back to back); the same for the other single-layer workloads (the small K=2 layer and the
+K=8 layer at B8 x T4096); the two stack workloads through the block entry point; informational
+lines for the eval-time threshold rule and one training step on the K=8 layer; the copy and
+read bandwidth, MFMA rate and vendor-library GEMM rates this GPU sustains; and the CPU oracle
+timed on a bounded sample of the headline workload on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-threshold]
-                      [--no-train] [--no-blocks] [--no-ceilings]
+                      [--no-train] [--no-blocks] [--no-ceilings] [--no-configs] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -88,11 +94,12 @@ def algorithmic_work_bwd(w):
     }
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None if
-    there is none or the kernel's sources changed since the counters were taken."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` at `workload` from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel's sources changed since the counters were
+    taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -102,6 +109,142 @@ def measured_traffic(kernel):
     if h.hexdigest()[:16] != rec["source_sha256_16"]:
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+FLUSH_BYTES = 512 << 20   # written before each cold step: twice the 256 MB last-level cache
+
+
+class LayerRun:
+    """One single-layer workload on the device: seeded inputs (workload.py), pristine copies of
+    x and the carried bias, the layer's weights and workspace."""
+
+    def __init__(self, xmod, w):
+        import torch
+        self.xmod, self.w = xmod, w
+        self.xb = wl.make_x(w)
+        self.lay = wl.make_layer(w, 0)
+        self.bias_np = wl.make_bias(w)
+        up = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+        self.dl = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in self.lay.items()}
+        self.L = xmod.make_layer(self.dl)
+        self.dims = xmod.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                   w.ffn_hidden, w.rms_eps)
+        self.x0 = up(self.xb)
+        self.x = self.x0.clone()
+        self.b0 = torch.from_numpy(self.bias_np).cuda()
+        self.bias = self.b0.clone()
+        self.ws = xmod.alloc_workspace(self.dims, w.K, xmod.WS_SPARSE_LAYER)
+        self.stream = torch.cuda.current_stream()
+        self.flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def step(self):
+        w = self.w
+        self.xmod.sparse_layer_fwd(self.x, self.L, self.dims, w.K, self.bias, w.tau, w.delta,
+                                   self.ws, stream=self.stream)
+
+    def restore(self, cold=True, i=0):
+        self.x.copy_(self.x0)
+        self.bias.copy_(self.b0)
+        if cold:
+            self.flush.fill_(i & 0x7F)
+
+    def settle(self, warmup):
+        """Untimed steps for at least 0.2 s (clocks settle), then the warm-up steps."""
+        import torch
+        t_end = time.perf_counter() + 0.2
+        for _ in range(400):
+            self.step()
+            torch.cuda.synchronize()
+            if time.perf_counter() > t_end:
+                break
+        for _ in range(warmup):
+            self.restore()
+            self.step()
+        self.restore(cold=False)
+        torch.cuda.synchronize()
+
+    def timed(self, steps, slots=None, cold=True):
+        """Per-step event times (ms) of `steps` steps, each from the pristine state (and, cold,
+        after the cache flush), with the library's events on the kernels of `slots` (None: no
+        kernel events; "all": every kernel). Returns (step times, kernel ms sums, calls)."""
+        import torch
+        xm = self.xmod
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        if slots is not None:
+            xm.phase_timing(True, slots=None if slots == "all" else slots)
+        for i in range(steps):
+            self.restore(cold, i)
+            ev[i][0].record(self.stream)
+            self.step()
+            ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        ph, n = (xm.phase_times() if slots is not None else ({}, 0))
+        if slots is not None:
+            xm.phase_timing(False)
+        return [a.elapsed_time(b) for a, b in ev], ph, n
+
+    def back_to_back(self, steps, slots="all"):
+        """`steps` steps back to back on the evolving state (warm caches), kernel events on."""
+        import torch
+        self.restore(cold=False)
+        self.xmod.phase_timing(True, slots=None if slots == "all" else slots)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        ph, n = self.xmod.phase_times()
+        self.xmod.phase_timing(False)
+        return ph, n
+
+
+def phase_table(w, phase_ms, steps):
+    work = algorithmic_work(w)
+    out = {}
+    for name in work:
+        avg = phase_ms[name] / steps
+        e = {"ms": round(avg, 5)}
+        if work[name]["flops"] > 0 and name.endswith(("gemm", "attention")):
+            e["tflops"] = round(work[name]["flops"] / (avg * 1e-3) / 1e12, 1)
+            e["frac_mfma_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        else:
+            e["gbs"] = round(work[name]["bytes"] / (avg * 1e-3) / 1e9, 1)
+            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
+        out[name] = e
+    return out
+
+
+def layer_line(run, steps, warmup):
+    """Timed steps of one single-layer workload (cold, from the pristine state, the dominant
+    kernel bracketed by the library's events), then the per-kernel breakdown cold and warm."""
+    import statistics
+    w = run.w
+    run.settle(warmup)
+    work = algorithmic_work(w)
+    dom = max(work, key=lambda n: work[n]["flops"])
+    times, dom_ms, n = run.timed(steps, slots=[dom])
+    assert n == steps
+    med = statistics.median(times)
+    M = w.B * w.k
+    dom_s = dom_ms[dom] / steps * 1e-3
+    achieved = work[dom]["flops"] / dom_s / 1e12
+    layer_fl = sum(v["flops"] for v in work.values())
+    _, ph_cold, _ = run.timed(steps, slots="all")
+    ph_warm, _ = run.back_to_back(steps)
+    return {
+        "ms_per_step": round(med, 5), "ms_mean": round(sum(times) / steps, 5),
+        "ms_min": round(min(times), 5), "routed_tokens_per_s": round(M / (med * 1e-3), 1),
+        "layer_tflops": round(layer_fl / (med * 1e-3) / 1e12, 1),
+        "layer_frac_mfma_peak": round(layer_fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom, w.name),
+                     "flops_per_launch": work[dom]["flops"],
+                     "ms_per_launch": round(dom_s * 1e3, 5)},
+        "phases_cold": phase_table(w, ph_cold, steps),
+        "phases_warm": phase_table(w, ph_warm, steps),
+    }
 
 
 def threshold_layer(xmod, w, xb, dl, dims, steps, warmup, time_oracle=True):
@@ -374,32 +517,39 @@ def measured_ceilings(w, reps=10):
     return out
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The oracle (float64 NumPy) on a bounded sample of the same workload on this host."""
+def cpu_baseline(w, xb, lay, bias, budget_s=12.0):
+    """The oracle (float64 NumPy, oracle/) on a bounded sample of the same workload on this
+    host: the router and top-k over every token and, per sequence, RMSNorm, keys and values of
+    the routed rows up to the last sampled one, then queries, attention, O, RMSNorm and SwiGLU
+    for evenly spaced sampled rows. A first pass on 64 rows per sequence sizes the sample to
+    about budget_s seconds; routed tokens/s = sampled rows / time of the second pass."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    xb = wl.make_x(w)
-    lay = wl.make_layer(w, 0)
-    bias = wl.make_bias(w)
+
+    def sample(n):
+        n = max(1, min(w.k, n))
+        rows = np.unique(np.linspace(0, w.k - 1, n).round().astype(np.int64))
+        return {b: rows for b in range(w.B)}, len(rows)
+
+    smp, n = sample(64)
     t0 = time.perf_counter()
-    oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
-                        sample={0: np.arange(w.k)})
+    oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=smp)
     t1 = time.perf_counter() - t0
-    n_seq = int(max(1, min(w.B, budget_s // max(t1, 1e-3))))
-    if n_seq > 1:
-        t0 = time.perf_counter()
-        oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta,
-                            sample={b: np.arange(w.k) for b in range(n_seq)})
-        t1 = time.perf_counter() - t0
-    routed = n_seq * w.k
-    return {"value": routed / t1, "unit": "routed tokens/s", "cores": int(threads),
+    smp, n = sample(int(64 * budget_s / max(t1, 1e-3)))
+    t0 = time.perf_counter()
+    oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=smp)
+    t1 = time.perf_counter() - t0
+    routed = n * w.B
+    return {"value": round(routed / t1, 1), "unit": "routed tokens/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(t1, 3),
-            "sample": f"{n_seq} of {w.B} sequences (router and top-k over all {w.B}; attention and "
-                      f"FFN over the {w.k} routed tokens of each sampled sequence), float64"}
+            "sample": f"{n} of the {w.k} routed rows of each of the {w.B} sequence(s), evenly "
+                      f"spaced ({routed} routed tokens; router and top-k over all {w.B * w.T} "
+                      f"tokens, keys and values of the routed rows up to the last sampled one), "
+                      f"float64"}
 
 
 def main():
@@ -416,6 +566,11 @@ def main():
                     help="skip the informational stack workloads (MoD pairs, A3K16 block)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured bandwidth, MFMA and library GEMM ceilings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other single-layer workloads (K=2 small layer, K=8 layer)")
+    ap.add_argument("--workload", default=wl.BENCH_WORKLOAD, choices=sorted(
+        n for n, v in wl.WORKLOADS.items() if v.N1 == 0),
+        help="the single-layer workload of the headline (default: the long-context GQA layer)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -428,126 +583,73 @@ def main():
     import torch
     from sparse_depth_token_amd import xmod
 
-    w = wl.WORKLOADS[wl.BENCH_WORKLOAD]
-    dev = "cuda"
-
-    def up(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    xb = wl.make_x(w)
-    lay = wl.make_layer(w, 0)
-    dl = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in lay.items()}
-    L = xmod.make_layer(dl)
-    dims = xmod.make_dims(w.B, w.T, w.d, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ffn_hidden,
-                          w.rms_eps)
-    x = up(xb)
-    bias = torch.from_numpy(wl.make_bias(w)).to(dev)
-    ws = xmod.alloc_workspace(dims, w.K, xmod.WS_SPARSE_LAYER)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        xmod.sparse_layer_fwd(x, L, dims, w.K, bias, w.tau, w.delta, ws, stream=stream)
-
     if args.copy_probe:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    # device warm-up: untimed steps for at least 0.2 s (clocks settle), then the W warm-up steps
-    t_end = time.perf_counter() + 0.2
-    for _ in range(400):
-        step()
-        torch.cuda.synchronize()
-        if time.perf_counter() > t_end:
-            break
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    work = algorithmic_work(w)
-    # the dominant kernel: the largest algorithmic work (the gate/up GEMM with SwiGLU)
-    dom = max(work, key=lambda n: work[n]["flops"])
-
-    # timed region: K steps; the library brackets the dominant kernel with events on the same
-    # stream (two events per step)
-    xmod.phase_timing(True, slots=[dom])
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    dom_ms, n_calls = xmod.phase_times()
-    xmod.phase_timing(False)
-    assert n_calls == args.steps
-    assert torch.isfinite(x.float()).all().item(), "non-finite hidden state"
-
-    ms_per_step = total_ms / args.steps
+    w = wl.WORKLOADS[args.workload]
+    print(f"[bench] {w.name}: drawing inputs", file=sys.stderr, flush=True)
+    run = LayerRun(xmod, w)
+    print(f"[bench] {w.name}: timing", file=sys.stderr, flush=True)
+    head = layer_line(run, args.steps, args.warmup)
+    assert torch.isfinite(run.x.float()).all().item(), "non-finite hidden state"
     M = w.B * w.k
-    value = M / (ms_per_step * 1e-3)
-
-    # per-kernel breakdown: K more steps with events around every kernel (not the timed region)
-    xmod.phase_timing(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    phase_ms, _ = xmod.phase_times()
-    xmod.phase_timing(False)
-    phases = {}
-    for name in xmod.FWD_PHASES:
-        ms = phase_ms[name]
-        avg = ms / args.steps
-        e = {"ms": round(avg, 5)}
-        if work[name]["flops"] > 0 and name.endswith(("gemm", "attention")):
-            e["tflops"] = round(work[name]["flops"] / (avg * 1e-3) / 1e12, 1)
-            e["frac_mfma_peak"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
-        else:
-            e["gbs"] = round(work[name]["bytes"] / (avg * 1e-3) / 1e9, 1)
-            e["frac_hbm_peak"] = round(e["gbs"] / PEAK_HBM_GBS, 4)
-        phases[name] = e
-    dom_avg_s = dom_ms[dom] / args.steps * 1e-3
-    if dom.endswith(("gemm", "attention")):
-        achieved = work[dom]["flops"] / dom_avg_s / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(dom)}
-    else:
-        achieved = work[dom]["bytes"] / dom_avg_s / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(dom)}
-    layer_flops = sum(v["flops"] for k2, v in work.items())
-
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "routed tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+        "metric": METRIC, "value": head["routed_tokens_per_s"], "unit": "routed tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "d": w.d, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_hidden": w.ffn_hidden,
                    "K": w.K, "routed_tokens_per_step": M, "parallelism": "none (1 GPU)"},
-        "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 1),
-        "layer_frac_mfma_peak": round(layer_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "roofline": roof,
-        "phases": phases,
+        "timing": "median of per-step events; each step from pristine x and bias after a "
+                  "512 MiB cache flush (outside the events)",
+        "ms_mean": head["ms_mean"], "ms_min": head["ms_min"],
+        "layer_tflops": head["layer_tflops"], "layer_frac_mfma_peak": head["layer_frac_mfma_peak"],
+        "roofline": head["roofline"],
+        "phases_cold": head["phases_cold"], "phases_warm": head["phases_warm"],
     }
-    if not args.no_threshold:
-        out["threshold_layer"] = threshold_layer(xmod, w, xb, dl, dims, args.steps, args.warmup,
-                                                 time_oracle=not args.no_cpu_baseline)
-    if not args.no_train:
-        out["train_step"] = train_step(xmod, w, xb, dl, dims, args.steps, args.warmup,
-                                       oracle_budget_s=0.0 if args.no_cpu_baseline else 6.0)
+    xb, lay, bias_np = run.xb, run.lay, run.bias_np
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        cfgs = {}
+        for name in ("sparse_k2_b2x512_d256", "sparse_k8_b8x4096_d2048"):
+            if name == w.name:
+                continue
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            r = LayerRun(xmod, wl.WORKLOADS[name])
+            cfgs[name] = layer_line(r, args.steps, args.warmup)
+            del r
+            torch.cuda.empty_cache()
+        out["configs"] = cfgs
+    k8 = wl.WORKLOADS["sparse_k8_b8x4096_d2048"]
+    if not (args.no_threshold and args.no_train):
+        r = LayerRun(xmod, k8)
+        if not args.no_threshold:
+            print("[bench] threshold layer", file=sys.stderr, flush=True)
+            out["threshold_layer"] = threshold_layer(xmod, k8, r.xb, r.dl, r.dims, args.steps,
+                                                     args.warmup,
+                                                     time_oracle=not args.no_cpu_baseline)
+        if not args.no_train:
+            print("[bench] training step", file=sys.stderr, flush=True)
+            out["train_step"] = train_step(xmod, k8, r.xb, r.dl, r.dims, args.steps, args.warmup,
+                                           oracle_budget_s=0.0 if args.no_cpu_baseline else 6.0)
+        del r
+        torch.cuda.empty_cache()
     if not args.no_blocks:
+        print("[bench] stacks", file=sys.stderr, flush=True)
         out["blocks"] = blocks(xmod)
     if not args.no_ceilings:
+        print("[bench] ceilings", file=sys.stderr, flush=True)
         out["measured_ceilings"] = measured_ceilings(w)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, xb, lay, bias_np)
     print(json.dumps(out), flush=True)
 
 

@@ -91,7 +91,8 @@ WORKLOADS = {
                                              8, 128, 14336, 4, skew_frac=0.01),
 }
 
-BENCH_WORKLOAD = "sparse_k8_b8x4096_d2048"
+# The workload of the benchmark's headline: the largest single-layer workload that fits one GPU.
+BENCH_WORKLOAD = "sparse_k4_gqa_b1x32768_d4096"
 
 
 def rng_for(seed: int, layer: int, tensor_id: int) -> np.random.Generator:
