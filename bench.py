@@ -9,8 +9,8 @@ routed subset, O GEMM, residual + RMSNorm, gate/up GEMM with SwiGLU, down GEMM w
 scatter back into x).
 
 Protocol of the timed steps: before every step, outside its events, x and the carried bias are
-restored from pristine device copies and a 512 MiB scratch buffer is written (the 256 MB
-last-level cache holds no part of the layer's inputs), so each step starts from the same state
+restored from pristine device copies and a 512 MiB scratch buffer is read (the 256 MB
+last-level cache then holds no part of the layer's inputs), so each step starts from the same state
 with its inputs resident in HBM. Each step is bracketed by HIP events on the launch stream;
 ms_per_step is the median. Untimed steps run for at least 0.2 s first (the clocks settle), then
 the W warm-up steps.
@@ -111,7 +111,7 @@ def measured_traffic(kernel, workload):
     return int(rec["traffic_bytes_per_launch"])
 
 
-FLUSH_BYTES = 512 << 20   # written before each cold step: twice the 256 MB last-level cache
+FLUSH_BYTES = 512 << 20   # read before each cold step: twice the 256 MB last-level cache
 
 
 class LayerRun:
@@ -136,18 +136,21 @@ class LayerRun:
         self.bias = self.b0.clone()
         self.ws = xmod.alloc_workspace(self.dims, w.K, xmod.WS_SPARSE_LAYER)
         self.stream = torch.cuda.current_stream()
-        self.flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        # the flush reads a buffer twice the size of the last-level cache (reads leave no dirty
+        # lines behind, whose write-back would slow the next kernel's reads)
+        self.flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.flush_sums = torch.empty(xmod.PROBE_THREADS, dtype=torch.int32, device="cuda")
 
     def step(self):
         w = self.w
         self.xmod.sparse_layer_fwd(self.x, self.L, self.dims, w.K, self.bias, w.tau, w.delta,
                                    self.ws, stream=self.stream)
 
-    def restore(self, cold=True, i=0):
+    def restore(self, cold=True):
         self.x.copy_(self.x0)
         self.bias.copy_(self.b0)
         if cold:
-            self.flush.fill_(i & 0x7F)
+            self.xmod.probe_read(self.flush, self.flush_sums, stream=self.stream)
 
     def settle(self, warmup):
         """Untimed steps for at least 0.2 s (clocks settle), then the warm-up steps."""
@@ -175,7 +178,7 @@ class LayerRun:
         if slots is not None:
             xm.phase_timing(True, slots=None if slots == "all" else slots)
         for i in range(steps):
-            self.restore(cold, i)
+            self.restore(cold)
             ev[i][0].record(self.stream)
             self.step()
             ev[i][1].record(self.stream)
@@ -521,8 +524,9 @@ def cpu_baseline(w, xb, lay, bias, budget_s=12.0):
     """The oracle (float64 NumPy, oracle/) on a bounded sample of the same workload on this
     host: the router and top-k over every token and, per sequence, RMSNorm, keys and values of
     the routed rows up to the last sampled one, then queries, attention, O, RMSNorm and SwiGLU
-    for evenly spaced sampled rows. A first pass on 64 rows per sequence sizes the sample to
-    about budget_s seconds; routed tokens/s = sampled rows / time of the second pass."""
+    for evenly spaced sampled rows. Passes on more rows per sequence until one takes at least
+    half of budget_s (or covers every routed row); routed tokens/s = sampled rows / time of
+    that pass."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -535,14 +539,15 @@ def cpu_baseline(w, xb, lay, bias, budget_s=12.0):
         rows = np.unique(np.linspace(0, w.k - 1, n).round().astype(np.int64))
         return {b: rows for b in range(w.B)}, len(rows)
 
-    smp, n = sample(64)
-    t0 = time.perf_counter()
-    oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=smp)
-    t1 = time.perf_counter() - t0
-    smp, n = sample(int(64 * budget_s / max(t1, 1e-3)))
-    t0 = time.perf_counter()
-    oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=smp)
-    t1 = time.perf_counter() - t0
+    rows = 64
+    while True:
+        smp, n = sample(rows)
+        t0 = time.perf_counter()
+        oracle.sparse_layer(xb, lay, w, w.K, bias=bias, tau=w.tau, delta=w.delta, sample=smp)
+        t1 = time.perf_counter() - t0
+        if t1 >= 0.5 * budget_s or n >= w.k:
+            break
+        rows = min(w.k, int(rows * max(2.0, 0.8 * budget_s / max(t1, 1e-3))))
     routed = n * w.B
     return {"value": round(routed / t1, 1), "unit": "routed tokens/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(t1, 3),
@@ -607,7 +612,7 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn_hidden": w.ffn_hidden,
                    "K": w.K, "routed_tokens_per_step": M, "parallelism": "none (1 GPU)"},
         "timing": "median of per-step events; each step from pristine x and bias after a "
-                  "512 MiB cache flush (outside the events)",
+                  "512 MiB cache flush by a streaming read (outside the events)",
         "ms_mean": head["ms_mean"], "ms_min": head["ms_min"],
         "layer_tflops": head["layer_tflops"], "layer_frac_mfma_peak": head["layer_frac_mfma_peak"],
         "roofline": head["roofline"],
