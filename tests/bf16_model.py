@@ -32,11 +32,11 @@ def _bf16(v):
     return oracle.round_to_bf16(v)
 
 
-def _attention_bf16(Q, Kt, Vt, q_rows, Hq, Hkv, hd, round_p, rnd):
+def _attention_bf16(Q, Kt, Vt, q_rows, Hq, Hkv, hd, round_p, rnd, acc):
     n, m = Q.shape[0], Kt.shape[0]
     visible = np.arange(m)[None, :] <= np.asarray(q_rows)[:, None]
-    out = np.empty((n, Hq * hd))
-    scale = 1.0 / np.sqrt(hd)
+    out = np.empty((n, Hq * hd), dtype=acc)
+    scale = acc(1.0 / np.sqrt(hd))
     for h in range(Hq):
         g = (h * Hkv) // Hq
         S = (Q[:, h * hd:(h + 1) * hd] @ Kt[:, g * hd:(g + 1) * hd].T) * scale
@@ -44,22 +44,25 @@ def _attention_bf16(Q, Kt, Vt, q_rows, Hq, Hkv, hd, round_p, rnd):
         P = np.exp(S - S.max(axis=1, keepdims=True))
         l = P.sum(axis=1, keepdims=True)
         if round_p:
-            P = rnd(P)
+            P = rnd(P).astype(acc)
         out[:, h * hd:(h + 1) * hd] = (P @ Vt[:, g * hd:(g + 1) * hd]) / l
     return out
 
 
 def sparse_layer_rows(xb, lay, w, K, bias=None, tau=1.0, sample=None, round_p=False,
-                      rounding=True, forced_idx=None):
+                      rounding=True, forced_idx=None, accumulate=np.float64):
     """Routed output rows of one sparse layer under the bf16-operand model.
 
     xb: bf16 bits [B, T, d]; lay: layer weights as produced by workload.make_layer; sample:
     {b: packed rows} (None: every routed row of every sequence). The selection is the oracle's
-    (top-k of the fp32 logits) unless forced_idx [B, k] gives one. rounding=False leaves every value in float64 (the model is then
+    (top-k of the fp32 logits) unless forced_idx [B, k] gives one. accumulate=np.float32 takes
+    every product and sum after the router in fp32 (the precision a matrix core accumulates in)
+    instead of float64; the residual is still formed in float64. rounding=False leaves every value in float64 (the model is then
     the oracle's layer, computed in a different order). Returns {b: (packed rows, positions,
     y rows float64)}.
     """
-    rnd = _bf16 if rounding else (lambda v: np.asarray(v, dtype=np.float64))
+    acc = accumulate
+    rnd = (lambda v: _bf16(v).astype(acc)) if rounding else (lambda v: np.asarray(v, dtype=acc))
     x = oracle.bf16_to_f64(xb)
     B, T, d = x.shape
     k = T // K
@@ -69,9 +72,9 @@ def sparse_layer_rows(xb, lay, w, K, bias=None, tau=1.0, sample=None, round_p=Fa
     idx = oracle.topk_select(ell, k) if forced_idx is None else np.asarray(forced_idx, np.int64)
     Hq, Hkv, hd = w.n_q_heads, w.n_kv_heads, w.head_dim
     dq, dkv = Hq * hd, Hkv * hd
-    Wqkv = oracle.bf16_to_f64(lay["w_qkv"])
-    Wo = oracle.bf16_to_f64(lay["w_o"])
-    Wg, Wu, Wd = (oracle.bf16_to_f64(lay[n]) for n in ("w_gate", "w_up", "w_down"))
+    Wqkv = oracle.bf16_to_f64(lay["w_qkv"]).astype(acc)
+    Wo = oracle.bf16_to_f64(lay["w_o"]).astype(acc)
+    Wg, Wu, Wd = (oracle.bf16_to_f64(lay[n]).astype(acc) for n in ("w_gate", "w_up", "w_down"))
     vs = float(lay.get("varsigma", 1.0))
     out = {}
     for b in (range(B) if sample is None else sorted(sample)):
@@ -82,13 +85,15 @@ def sparse_layer_rows(xb, lay, w, K, bias=None, tau=1.0, sample=None, round_p=Fa
         Q = rnd(u[rows] @ Wqkv[:dq].T)
         Kt = rnd(u @ Wqkv[dq:dq + dkv].T)
         Vt = rnd(u @ Wqkv[dq + dkv:].T)
-        O = rnd(_attention_bf16(Q, Kt, Vt, rows, Hq, Hkv, hd, round_p, rnd))
+        O = rnd(_attention_bf16(Q, Kt, Vt, rows, Hq, Hkv, hd, round_p, rnd, acc))
         a = O @ Wo.T
         v = rnd(oracle.rmsnorm(X[rows] + a, lay["g_ffn"], w.rms_eps))
-        g = rnd(oracle.silu(v @ Wg.T) * (v @ Wu.T))
+        zg, zu = v @ Wg.T, v @ Wu.T
+        g = rnd(zg / (1 + np.exp(-zg)) * zu)
         f = g @ Wd.T
         r = oracle.sigmoid(ell[b, idx[b, rows]].astype(np.float64))[:, None]
-        out[b] = (rows, idx[b, rows], X[rows] + (vs * r) * (a + f))
+        out[b] = (rows, idx[b, rows],
+                  X[rows] + (vs * r) * (a.astype(np.float64) + f.astype(np.float64)))
     return out
 
 

@@ -6,8 +6,13 @@
   At the bench layer (d 2048, F 5632) that distance stays inside the stated 2e-2 bar. At the
   long-context GQA layer (d 4096, F 14336, 8192 routed rows) it exceeds 2e-2 on the rows the
   GPU test samples: no implementation with bf16 matrix-core operands can meet 2e-2 there, so
-  the GPU test compares that layer with this model at 2e-2 and with the oracle at the model's
-  own distance plus 2e-2. The relative-L2 bar (5e-3) holds for the model at both shapes.
+  the GPU test holds that layer to the model's own distance from the oracle plus 2e-2. The
+  relative-L2 bar (5e-3) holds for the model at both shapes.
+* Which values cross a bf16 rounding boundary depends on how the sums before it are taken: the
+  same model accumulating in fp32 instead of float64 lands up to about 2e-2 from itself on the
+  long-context rows (relative L2 about 1e-3). That is the spread between two bf16-operand
+  computations that differ only in summation precision, and it is why the GPU is compared with
+  the model in relative L2 only, not element by element at 2e-2.
 """
 import numpy as np
 import pytest
@@ -58,10 +63,18 @@ def test_long_context_model_exceeds_stated_bar():
     xb, lay = wl.make_x(w), wl.make_layer(w, 0)
     sample = {0: LONG_ROWS}
     ref = oracle.sparse_layer(xb, lay, w, w.K, sample=sample)
-    for round_p in (False, True):
-        mod = bf16_model.sparse_layer_rows(xb, lay, w, w.K, sample=sample, round_p=round_p)
+    mods = {}
+    for round_p, acc in ((False, np.float64), (True, np.float64), (True, np.float32)):
+        mod = bf16_model.sparse_layer_rows(xb, lay, w, w.K, sample=sample, round_p=round_p,
+                                           accumulate=acc)
+        mods[(round_p, acc)] = mod
         worst, rel = bf16_model.gap(mod, ref["rows"])
-        print(f"long-context layer, {len(LONG_ROWS)} sampled rows, P rounded: {round_p}: "
-              f"bf16-operand model vs oracle max|diff| {worst:.4g}, relL2 {rel:.3g}")
+        print(f"long-context layer, {len(LONG_ROWS)} sampled rows, P rounded: {round_p}, "
+              f"{np.dtype(acc).name} sums: bf16-operand model vs oracle max|diff| {worst:.4g}, "
+              f"relL2 {rel:.3g}")
         assert 2e-2 < worst < 8e-2
         assert rel < 5e-3
+    a, b = mods[(True, np.float64)], mods[(True, np.float32)]
+    spread, rel = bf16_model.gap(b, a)
+    print(f"fp32 vs float64 sums in the model: max|diff| {spread:.4g}, relL2 {rel:.3g}")
+    assert 1e-3 < spread < 4e-2 and rel < 2e-3
