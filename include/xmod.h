@@ -162,6 +162,23 @@ xmod_status xmod_sparse_layer_fwd(void *x, const xmod_layer *layer, const xmod_d
                                   int32_t *idx_out, float *gate_out, void *ws, size_t ws_bytes,
                                   void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): xmod_sparse_layer_fwd without a caller workspace.
+ * The workspace is a static device array of XMOD_NOALLOC_SCRATCH_BYTES owned by the library,
+ * one per GPU, held until the process ends; this call allocates nothing. Arguments and
+ * results are those of xmod_sparse_layer_fwd (bit for bit: the same kernels run) minus
+ * ws / ws_bytes. Returns XMOD_ERR_WORKSPACE, before any launch, when the layer needs more than
+ * the array (xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_LAYER) > XMOD_NOALLOC_SCRATCH_BYTES;
+ * e.g. 4 x 4096 tokens at d 1536, K 8 fit, 8 x 4096 at d 2048 do not). The kernels run on the
+ * device of `stream` (the current device for the null stream). Every call on one GPU uses
+ * that GPU's one array and leaves its contents behind: calls that may overlap on one GPU (on
+ * different streams, or from host threads without ordering between them) race. */
+#define XMOD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+xmod_status xmod_sparse_layer_fwd_noalloc(void *x, const xmod_layer *layer,
+                                          const xmod_dims *dims, int32_t K, float *bias,
+                                          float tau, float delta, int32_t *idx_out,
+                                          float *gate_out, void *stream);
+
 /* Eval-time causal threshold routing of given fp32 logits [B,T] ([XMOD] "training-time top-k,
  * eval-time causal threshold"): a token enters when its routing probability sigmoid(ell) is at
  * least 1/2, i.e. ell >= 0 (-0 included, NaN never). Each sequence selects its own number of

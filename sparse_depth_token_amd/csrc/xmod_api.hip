@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "xmod.h"
@@ -415,6 +416,66 @@ xmod_status xmod_sparse_layer_fwd(void *x, const xmod_layer *layer, const xmod_d
   if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
   return sparse_layer(x, layer, dims, K, bias, tau, delta, idx_out, gate_out, ws,
                       (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free sparse layer: its workspace is a static device array ---------------
+namespace {
+
+// One copy per GPU, zero-initialised at load; every byte the layer reads is written by an
+// earlier kernel of the same call, so nothing needs clearing between calls.
+__device__ __align__(256) unsigned char scratch[XMOD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of stream s, looked up once per device with that
+// device current (the array's host-side name is not a device address).
+xmod_status scratch_for_stream(hipStream_t s, void **out) {
+  int dev = -1;
+  if (s) {
+    XMOD_HIP(hipStreamGetDevice(s, &dev));
+  } else {
+    XMOD_HIP(hipGetDevice(&dev));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return XMOD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    XMOD_HIP(hipGetDevice(&cur));
+    if (cur != dev) XMOD_HIP(hipSetDevice(dev));
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) XMOD_HIP(hipSetDevice(cur));
+    XMOD_HIP(e);
+    if (!p) return XMOD_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return XMOD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+xmod_status xmod_sparse_layer_fwd_noalloc(void *x, const xmod_layer *layer,
+                                          const xmod_dims *dims, int32_t K, float *bias,
+                                          float tau, float delta, int32_t *idx_out,
+                                          float *gate_out, void *stream) {
+  const xmod_status st = check_dims(dims);
+  if (st != XMOD_OK) return st;
+  if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
+  if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_LAYER);
+  if (need > XMOD_NOALLOC_SCRATCH_BYTES) return XMOD_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void *ws = nullptr;
+  const xmod_status sc = scratch_for_stream(s, &ws);
+  if (sc != XMOD_OK) return sc;
+  return sparse_layer(x, layer, dims, K, bias, tau, delta, idx_out, gate_out, ws, s);
 }
 
 xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,

@@ -20,11 +20,13 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 WS_ROUTE_TOPK, WS_SPARSE_LAYER, WS_DENSE_LAYER, WS_BLOCK, WS_SPARSE_THRESHOLD = 0, 1, 2, 3, 4
 WS_ROUTED_FFN, WS_ATTN_LAYER, WS_SPARSE_FULLKV = 5, 6, 7
 WS_TRAIN_SAVED, WS_BACKWARD = 8, 9
+NOALLOC_SCRATCH_BYTES = 64 << 20   # XMOD_NOALLOC_SCRATCH_BYTES
 GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 
 # Every symbol include/xmod.h declares, in declaration order.
 EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", "xmod_pack",
-            "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_threshold_select",
+            "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_sparse_layer_fwd_noalloc",
+            "xmod_threshold_select",
             "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_routed_ffn_fwd",
             "xmod_attention_layer_fwd", "xmod_sparse_layer_fwd_fullkv", "xmod_dense_layer_fwd",
             "xmod_block_fwd", "xmod_sparse_layer_fwd_train", "xmod_sparse_layer_bwd",
@@ -75,6 +77,8 @@ _sig = {
                                      _P(Grads), _vp, _vp, _sz, _vp]),
     "xmod_sparse_layer_fwd": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp, _vp,
                                      _vp, _sz, _vp]),
+    "xmod_sparse_layer_fwd_noalloc": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32,
+                                             _vp, _vp, _vp]),
     "xmod_threshold_select": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp]),
     "xmod_sparse_layer_fwd_threshold": (_i32, [_vp, _P(Layer), _P(Dims), _vp, _f32, _f32, _vp,
                                                _vp, _vp, _vp, _sz, _vp]),
@@ -298,6 +302,21 @@ def sparse_layer_fwd(x, layer: Layer, dims: Dims, K, bias, tau, delta, ws, idx_o
     _check(lib.xmod_sparse_layer_fwd(xp, ctypes.byref(layer), ctypes.byref(dims), K, bp, tau,
                                      delta, ip, gp, wp, wn, _stream(stream)),
            "xmod_sparse_layer_fwd")
+
+
+def sparse_layer_fwd_noalloc(x, layer: Layer, dims: Dims, K, bias, tau, delta, idx_out=None,
+                             gate_out=None, stream=None):
+    """xmod_sparse_layer_fwd with the library's static per-GPU workspace (no allocation; calls
+    that overlap on one GPU race)."""
+    k = _k(dims, K)
+    _check_layer(layer, dims, True)
+    xp = _x(x, dims)
+    bp = _arg(bias, "bias", _F32, n=_bt(dims), optional=True)
+    ip = _arg(idx_out, "idx_out", _I32, at_least=dims.B * k, optional=True)
+    gp = _arg(gate_out, "gate_out", _F32, at_least=dims.B * k, optional=True)
+    _check(lib.xmod_sparse_layer_fwd_noalloc(xp, ctypes.byref(layer), ctypes.byref(dims), K, bp,
+                                             tau, delta, ip, gp, _stream(stream)),
+           "xmod_sparse_layer_fwd_noalloc")
 
 
 def make_grads(g: dict) -> Grads:
