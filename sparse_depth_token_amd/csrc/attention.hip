@@ -352,13 +352,18 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   if (lse && active && gq == 0 && q_pos < k)
     lse[(row0 + q_pos) * Hq + h] = m_ref + __builtin_amdgcn_logf(l_tot);  // v_log_f32: log2
   if (active) {
+    // The epilogue's lane-dependent addresses are derived from an opaque copy of the lane id,
+    // so the compiler forms them here instead of keeping them live across the key loop.
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int r32e = lane_e & 31, gqe = lane_e >> 5;
     uint16_t *ow = lds + wid * 32 * HD;
 #pragma unroll
     for (int t = 0; t < NT_HD; ++t)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c = 4 * t + q4;  // 16-byte chunk of hd 32t + 8q4 .. +7
-        *(uint2 *)(ow + r32 * HD + ((c ^ (r32 & (C::CPR - 1))) * 8) + 4 * gq) =
+        *(uint2 *)(ow + r32e * HD + ((c ^ (r32e & (C::CPR - 1))) * 8) + 4 * gqe) =
             make_uint2(pack_bf16x2(oacc[t][4 * q4] * inv, oacc[t][4 * q4 + 1] * inv),
                        pack_bf16x2(oacc[t][4 * q4 + 2] * inv, oacc[t][4 * q4 + 3] * inv));
       }
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
     const int q0 = q_row0;
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / C::CPR, c = lane % C::CPR;
+      const int r = RPI * i + lane_e / C::CPR, c = lane_e % C::CPR;
       const uint4 v = *(const uint4 *)(ow + r * HD + ((c ^ (r & (C::CPR - 1))) * 8));
       if (q0 + r < k) *(uint4 *)(o + (row0 + q0 + r) * ldo + h * HD + c * 8) = v;
     }
