@@ -495,7 +495,7 @@ def measured_ceilings(w, reps=10):
     del dst
     # the library's own probes: a streaming read of the same 1 GiB, back-to-back MFMAs
     sums = torch.empty(xmod.PROBE_THREADS, dtype=torch.int32, device="cuda")
-    t_read = timed(lambda: xmod.probe_read(src, sums))
+    t_reads = {dep: timed(lambda: xmod.probe_read(src, sums, dep)) for dep in (4, 8, 16)}
     del src
     acc = torch.empty(xmod.PROBE_THREADS, dtype=torch.float32, device="cuda")
     iters = 4096
@@ -503,7 +503,9 @@ def measured_ceilings(w, reps=10):
     mfma_flops = 4096 * 4 * iters * 32768
     M = w.B * w.k
     out = {"hbm_copy_gbs": round(2 * n / t_copy / 1e9, 1),
-           "hbm_read_gbs": round(n / t_read / 1e9, 1),
+           "hbm_read_gbs": round(n / min(t_reads.values()) / 1e9, 1),
+           "hbm_read_gbs_by_loads_in_flight": {str(dep): round(n / t / 1e9, 1)
+                                               for dep, t in t_reads.items()},
            "mfma_bf16_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
     gemms = {}
     for name, (m, nn, kk) in {"gateup_shape": (M, 2 * w.ffn_hidden, w.d),
@@ -514,9 +516,11 @@ def measured_ceilings(w, reps=10):
         gemms[name] = round(2.0 * m * nn * kk / t / 1e12, 1)
         del a, bw
     out["library_gemm_tflops"] = gemms
-    out["note"] = ("torch copy (read + write), the library's streaming-read and back-to-back "
-                   "MFMA probes, and torch.matmul (vendor library) on this GPU; the roofline "
-                   "fractions use the vendor peaks (8 TB/s, 2.5 PFLOP/s)")
+    out["note"] = ("torch copy (read + write), the library's streaming-read probe (4, 8 or 16 "
+                   "16-byte loads in flight per thread, 1024 threads per CU; the best is "
+                   "hbm_read_gbs) and back-to-back MFMA probe, and torch.matmul (vendor library) "
+                   "on this GPU; the roofline fractions use the vendor peaks (8 TB/s, "
+                   "2.5 PFLOP/s)")
     return out
 
 

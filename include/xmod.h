@@ -392,11 +392,13 @@ xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls);
  *   operands back to back (32768 flops each, 4 waves per workgroup); out[t] = 64 * iters
  *   (4 accumulators of 16 per product). INVALID_ARG: out NULL or iters outside [1, 2^18].
  * xmod_probe_read: reads `bytes` (a multiple of 16, 16-byte aligned) of src with 16-byte loads in
- *   a grid-stride pass; out[t] = the 32-bit wrap-around sum of the words thread t read, so the
- *   sum over t equals that of every 32-bit word of src. INVALID_ARG: NULL pointer, bytes 0 or
- *   not a multiple of 16. */
+ *   a grid-stride pass, loads_in_flight (4, 8 or 16) independent loads outstanding per thread
+ *   (16 * loads_in_flight KB per CU); out[t] = the 32-bit wrap-around sum of the words thread t
+ *   read, so the sum over t equals that of every 32-bit word of src. INVALID_ARG: NULL pointer,
+ *   bytes 0 or not a multiple of 16, loads_in_flight not 4, 8 or 16. */
 xmod_status xmod_probe_mfma(float *out, int32_t iters, void *stream);
-xmod_status xmod_probe_read(const void *src, size_t bytes, uint32_t *out, void *stream);
+xmod_status xmod_probe_read(const void *src, size_t bytes, int32_t loads_in_flight, uint32_t *out,
+                            void *stream);
 
 const char *xmod_status_string(xmod_status st);
 int32_t xmod_last_hip_error(void);

@@ -2,8 +2,9 @@
 // layer's kernels are bound by, measured in the same run as the layer, beside the vendor peaks.
 //  * MFMA: every wave issues independent v_mfma_f32_32x32x16_bf16 back to back (four
 //    accumulators, no memory traffic in the loop).
-//  * HBM read: a grid-stride pass of 16-byte loads over a buffer, every 32-bit word added into
-//    a per-thread sum (kept, so that nothing is skipped; the sums are checkable on the host).
+//  * HBM read: a grid-stride pass of 16-byte loads over a buffer, 4, 8 or 16 of them in flight
+//    per thread, every 32-bit word added into a per-thread sum (kept, so that nothing is
+//    skipped; the sums are checkable on the host).
 #include "common.h"
 
 namespace xmod {
@@ -34,16 +35,19 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float *__restrict__ out
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// D independent 16-byte loads in flight per thread (1024 threads per CU: 16 D KB per CU)
+template <int D>
 __global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *__restrict__ src, int64_t n16,
                                                          uint32_t *__restrict__ out) {
   uint32_t s = 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // four 16-byte loads in flight per thread
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    s += v0.x + v0.y + v0.z + v0.w + v1.x + v1.y + v1.z + v1.w;
-    s += v2.x + v2.y + v2.z + v2.w + v3.x + v3.y + v3.z + v3.w;
+  for (; i + (D - 1) * stride < n16; i += D * stride) {
+    uint4 v[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) v[j] = src[i + j * stride];
+#pragma unroll
+    for (int j = 0; j < D; ++j) s += v[j].x + v[j].y + v[j].z + v[j].w;
   }
   for (; i < n16; i += stride) {
     const uint4 v = src[i];
@@ -57,9 +61,16 @@ hipError_t launch_probe_mfma(float *out, int iters, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_probe_read(const void *src, size_t bytes, uint32_t *out, hipStream_t s) {
-  hipLaunchKernelGGL(probe_read_kernel, dim3(PROBE_WGS), dim3(256), 0, s, (const uint4 *)src,
-                     (int64_t)(bytes / 16), out);
+hipError_t launch_probe_read(const void *src, size_t bytes, int depth, uint32_t *out,
+                             hipStream_t s) {
+  const uint4 *p = (const uint4 *)src;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (depth == 16)
+    hipLaunchKernelGGL(probe_read_kernel<16>, dim3(PROBE_WGS), dim3(256), 0, s, p, n16, out);
+  else if (depth == 8)
+    hipLaunchKernelGGL(probe_read_kernel<8>, dim3(PROBE_WGS), dim3(256), 0, s, p, n16, out);
+  else
+    hipLaunchKernelGGL(probe_read_kernel<4>, dim3(PROBE_WGS), dim3(256), 0, s, p, n16, out);
   return hipGetLastError();
 }
 

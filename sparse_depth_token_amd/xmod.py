@@ -100,6 +100,7 @@ _sig = {
     "xmod_gemm_bf16": (_i32, [_i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                               _vp]),
     "xmod_attention_fwd": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "xmod_probe_read": (_i32, [_vp, _sz, _i32, _vp, _vp]),
     "xmod_phase_timing_enable": (None, [_i32]),
     "xmod_phase_timing_slots": (None, [ctypes.c_uint32]),
     "xmod_phase_times": (_i32, [_P(_f32), _i32, _P(_i32)]),
@@ -541,16 +542,15 @@ def probe_mfma(out, iters, stream=None):
     return 4096 * 4 * int(iters) * 32768
 
 
-def probe_read(src, out, stream=None):
-    """Streaming read of every byte of the contiguous tensor src; out: int32 tensor of
-    PROBE_THREADS whose 32-bit wrap-around sum equals that of src's 32-bit words. Returns the
-    bytes read."""
+def probe_read(src, out, loads_in_flight=4, stream=None):
+    """Streaming read of every byte of the contiguous tensor src, loads_in_flight (4, 8 or 16)
+    16-byte loads outstanding per thread; out: int32 tensor of PROBE_THREADS whose 32-bit
+    wrap-around sum equals that of src's 32-bit words. Returns the bytes read."""
     nbytes = src.numel() * src.element_size()
     sp = _arg(src, "src", src.dtype)
     op = _arg(out, "out", _I32, at_least=PROBE_THREADS)
-    lib.xmod_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                    ctypes.c_void_p]
-    _check(lib.xmod_probe_read(sp, nbytes, op, _stream(stream)), "xmod_probe_read")
+    _check(lib.xmod_probe_read(sp, nbytes, int(loads_in_flight), op, _stream(stream)),
+           "xmod_probe_read")
     return nbytes
 
 

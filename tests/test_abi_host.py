@@ -228,11 +228,11 @@ def test_layout_gemm_and_attention_backward_reject_before_launch(x):
 
 def test_probes_reject_before_launch(x):
     L = x.lib
-    L.xmod_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     assert L.xmod_probe_mfma(None, 10, None) == x.ERR_INVALID_ARG
     assert L.xmod_probe_mfma(FAKE, 0, None) == x.ERR_INVALID_ARG
     assert L.xmod_probe_mfma(FAKE, (1 << 18) + 1, None) == x.ERR_INVALID_ARG
-    assert L.xmod_probe_read(None, 64, FAKE, None) == x.ERR_INVALID_ARG
-    assert L.xmod_probe_read(FAKE, 0, FAKE, None) == x.ERR_INVALID_ARG
-    assert L.xmod_probe_read(FAKE, 24, FAKE, None) == x.ERR_INVALID_ARG
-    assert L.xmod_probe_read(FAKE, 64, None, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read(None, 64, 4, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read(FAKE, 0, 4, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read(FAKE, 24, 4, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read(FAKE, 64, 4, None, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read(FAKE, 64, 5, FAKE, None) == x.ERR_INVALID_ARG
