@@ -224,10 +224,15 @@ gemm_kernel(GemmArgs g) {
   auto issue_tile = [&](int kt, int stage) { issue_part(kt, stage, 0, C::NA + C::NB); };
 
   // --- fragment read offsets within a stage ---
-  // Fragment rows are wm0 + 32i + r32 (A) and wn0 + 32j + r32 (B), with wm0, wn0 multiples of
-  // 64; then swz(row) = swz(r32) ^ (BK == 64 ? 4i & 7 : 0), so a k-step needs two chunk
-  // offsets (even / odd tile) plus a constant 32-row stride folded into the immediate offset.
+  // Fragment rows are wm0 + 32i + r32 (A) and wn0 + 32j + r32 (B). For BK = 64,
+  // swz(32 q + r32) = swz(r32) ^ (4 q & 7): the chunk XOR flips with the parity of the
+  // fragment's 32-row block q = wm0 / 32 + i (wn0 / 32 + j), so a k-step needs two chunk offsets
+  // (even / odd block) plus a constant 32-row stride folded into the immediate offset. A wave
+  // tile 32 rows wide starts on an odd block in every other wave; its block parity offset
+  // (a_par, b_par: 0 or 32 elements) is folded into the base.
   const int wm0 = (wid / C::NWN) * WM, wn0 = (wid % C::NWN) * WN;
+  const int a_par = (BK == 64 && WM % 64 != 0) ? (((wm0 >> 5) & 1) << 5) : 0;
+  const int b_par = (BK == 64 && WN % 64 != 0) ? (((wn0 >> 5) & 1) << 5) : 0;
   const int a_base = (wm0 + r32) * BK;
   const int b_base = C::A_ELEMS + (wn0 + r32) * BK;
   const int sw_lane = swz<BK>(r32);
@@ -284,17 +289,19 @@ gemm_kernel(GemmArgs g) {
       if (C::B_KM)
         fb[buf][j] = tr_frag(lds_addr(st) + bkm[j], ks, BN);
       else
-        fb[buf][j] = *(const bf16x8 *)(st + b_base + ((j & 1) ? c_odd : c_even) + 32 * BK * j);
+        fb[buf][j] = *(const bf16x8 *)(st + b_base + (((j & 1) ? c_odd : c_even) ^ b_par) +
+                                       32 * BK * j);
     } else {
       const int i = f == 0 ? 0 : f - C::TN;
       if (C::A_KM)
         fa[buf][i] = tr_frag(lds_addr(st) + akm[i], ks, BM);
       else
-        fa[buf][i] = *(const bf16x8 *)(st + a_base + ((i & 1) ? c_odd : c_even) + 32 * BK * i);
+        fa[buf][i] = *(const bf16x8 *)(st + a_base + (((i & 1) ? c_odd : c_even) ^ a_par) +
+                                       32 * BK * i);
     }
   };
   constexpr int NMF = C::TM * C::TN, NFR = C::TM + C::TN;
-  constexpr int HALF = NMF / 2;
+  constexpr int HALF = NMF > 1 ? NMF / 2 : 1;
   constexpr int FPS = (NFR + HALF - 1) / HALF;  // fragment reads per early slot
 
   // NS-stage ring: while tile kt is multiplied, tiles kt+1 .. kt+NS-1 are in flight. vmcnt
@@ -335,10 +342,14 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int f = t * FPS; f < (t + 1) * FPS; ++f)
         if (f < NFR) load_frag(ld_st, ld_ks, ld_buf, f);
-      if (t >= HALF && dma_hi > dma_lo) {
-        const int per = (dma_hi - dma_lo + (NMF - HALF) - 1) / (NMF - HALF);
-        const int lo = dma_lo + (t - HALF) * per;
-        issue_part(dma_kt, dma_stage, lo, min(lo + per, dma_hi));
+      if constexpr (NMF > HALF) {
+        if (t >= HALF && dma_hi > dma_lo) {
+          const int per = (dma_hi - dma_lo + (NMF - HALF) - 1) / (NMF - HALF);
+          const int lo = dma_lo + (t - HALF) * per;
+          issue_part(dma_kt, dma_stage, lo, min(lo + per, dma_hi));
+        }
+      } else if (dma_hi > dma_lo) {  // one MFMA per k-step: its copies go out in that slot
+        issue_part(dma_kt, dma_stage, dma_lo, dma_hi);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -572,8 +583,12 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
 //    and the second wave per SIMD beat 256x128 by ~5 %.
 //  * otherwise 256x128 (four compute waves of 64x128 plus four loader waves, BK = 64,
 //    three-stage ring) when the grid gives at least 5/8 of the 256 CUs a tile, else 128x128
-//    (four compute waves of 64x64 plus four loader waves). Loader waves took 8 % off the
-//    down projection and 1-3 % off the others; a 64x128 wave tile (two activation by four
+//    (four compute waves of 64x64 plus four loader waves), or, when 128x128 tiles would give
+//    at most half of the CUs one, 64x64 (four compute waves of 32x32 plus four loader waves):
+//    at 1024 routed rows and d = 1024 the O and down products go from 64 to 256 tiles
+//    (11.7 -> 9.2 us and 24.8 -> 16.2 us; at 192 tiles of 128x128 the larger tiles win).
+//    Loader waves took 8 % off the down projection and 1-3 % off the others; a 64x128 wave
+//    tile (two activation by four
 //    weight fragments per k-step) sustains more MFMA work per LDS read than 128x64 with one
 //    wave per SIMD (1.72 against 1.48 PFLOP/s in a register-fed probe).
 constexpr int GEMM_CUS = 256;
@@ -589,6 +604,11 @@ static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
   }
   const long t_big = tm * ((g.N + 128 / half - 1) / (128 / half));
   if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 64, 128, 64, 3, EPI, LAY, 4>(g, s);
+  if constexpr (LAY == LAY_NT && !swiglu) {
+    // a grid of at most half a wave of 128x128 tiles: 64x64 tiles (four times as many)
+    const long t_128 = ((g.M + 127) / 128) * ((g.N + 127) / 128);
+    if (t_128 <= GEMM_CUS / 2) return run_gemm<64, 64, 32, 32, 64, 3, EPI, LAY, 4>(g, s);
+  }
   return run_gemm<128, 128, 64, 64, 64, 3, EPI, LAY, 4>(g, s);
 }
 

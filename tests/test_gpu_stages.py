@@ -197,7 +197,11 @@ def test_rmsnorm_rows(x, B, T, d, k, use_idx):
 @pytest.mark.parametrize("M,N,K", [(512, 768, 256), (300, 200, 128), (4096, 2048, 2048),
                                    (1000, 1536, 1024), (8192, 6144, 512),
                                    # wide grids: several waves of 256x128 tiles, ragged rows
-                                   (4096, 6144, 128), (3900, 6144, 192)])
+                                   (4096, 6144, 128), (3900, 6144, 192),
+                                   # small grids of 64x64 tiles (32-row wave tiles): the
+                                   # A3K16 layer's O and down shapes, ragged rows and columns
+                                   (1024, 1024, 1024), (1024, 1024, 2816), (1000, 1000, 640),
+                                   (72, 136, 64)])
 def test_gemm(x, M, N, K):
     say(f"[gemm] M{M} N{N} K{K}")
     rng = np.random.default_rng(12)
