@@ -6,16 +6,17 @@
 // 0-based). Softmax uses the scale 1/sqrt(head_dim) and the usual online recurrence (running
 // max, rescaled running sum and output), so the k x k score matrix is never stored.
 //
-// Work split: 8 waves per workgroup, 32 query rows per wave, key/value tiles of 64 rows shared
-// by the workgroup. The register footprint allows one workgroup per CU (two waves per SIMD).
-// Two ways of giving a workgroup its 256 query rows, chosen at launch:
-//  * one q-tile of 256 packed rows, last tile first in dispatch order: every wave stays busy
+// Work split: NW = 8 (or 4) waves per workgroup, 32 query rows per wave, key/value tiles of 64
+// rows shared by the workgroup. The register footprint allows two waves per SIMD. Two ways of
+// giving a workgroup its 32 NW query rows, chosen at launch:
+//  * one q-tile of 32 NW packed rows, last tile first in dispatch order: every wave stays busy
 //    to the last key tiles, so each SIMD keeps two waves whose MFMA and softmax work overlap.
 //    Used when the grid holds more workgroups than there are CUs.
-//  * a pair of q-tiles of 128 rows (tile nqt-1-p for waves 0-3, tile p for waves 4-7): every
-//    workgroup has the same causal work, and the earlier tile's key/value tiles are a prefix
-//    of the later one's. Used when each CU gets at most one workgroup: the longest workgroup
-//    then holds half as many long rows.
+//  * a pair of q-tiles of 16 NW rows (tile nqt-1-p for the first half of the waves, tile p for
+//    the second): every workgroup has the same causal work, and the earlier tile's key/value
+//    tiles are a prefix of the later one's. Used when each CU gets at most one workgroup: the
+//    longest workgroup then holds half as many long rows. Grids of at most half a wave of
+//    256-row tiles take four-wave workgroups, so that twice as many CUs share the work.
 //
 //  * K and V tiles are copied global -> LDS by the DMA form of the load (no staging registers)
 //    into a two-stage ring: tile j+1 is in flight while tile j is used. Both stay row-major
@@ -40,9 +41,10 @@ __device__ __forceinline__ void attn_dma16(const void *gsrc, uint16_t *lds_block
                                    0, 0);
 }
 
-template <int HD>
+template <int HD, int NW_>
 struct AttnCfg {
-  static constexpr int BQ = 256, BQP = 128, BKV = 64, NW = 8, NT = 64 * NW;
+  // NW waves of 32 query rows: a q-tile of 32 NW rows, or a pair of q-tiles of 16 NW rows
+  static constexpr int NW = NW_, BQ = 32 * NW, BQP = 16 * NW, BKV = 64, NT = 64 * NW;
   static constexpr int CPR = HD / 8;              // 16-byte chunks per row
   static constexpr int RPB = 64 / CPR;            // rows per 1 KB DMA block
   static constexpr int TILE = BKV * HD;           // elements of one K (or V) tile
@@ -73,8 +75,8 @@ struct FullKV {
   int T = 0;
 };
 
-template <int HD, bool FULLKV>
-__global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
+template <int HD, bool FULLKV, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
                                                       uint16_t *__restrict__ o, int ldo,
                                                       int k_fixed, int Hq, int Hkv,
                                                       float scale_log2,
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
                                                       const int32_t *__restrict__ seq_len,
                                                       FullKV fkv, float *__restrict__ lse,
                                                       int paired) {
-  using C = AttnCfg<HD>;
+  using C = AttnCfg<HD, NW>;
   constexpr int BQ = C::BQ, BQP = C::BQP, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
   // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
   // it by more than 2^RESCALE_LOG2 (log2 units), so weights exp2(x - M) stay below 2^8 and most
@@ -110,9 +112,9 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
   bool active;
   if (paired) {
     const int qt_hi = nqt - 1 - it;
-    const bool later = wid < 4;
-    q_row0 = (later ? qt_hi : it) * BQP + (wid & 3) * 32;
-    active = later || it != qt_hi;  // the middle tile of an odd count: waves 0-3 only
+    const bool later = wid < NW / 2;
+    q_row0 = (later ? qt_hi : it) * BQP + (wid % (NW / 2)) * 32;
+    active = later || it != qt_hi;  // the middle tile of an odd count: the first half only
     q_end = min(qt_hi * BQP + BQP, k);
   } else {
     const int qt = nqt - 1 - it;
@@ -382,6 +384,14 @@ __global__ __launch_bounds__(512, 2) void attn_kernel(const uint16_t *__restrict
 
 constexpr int ATTN_CUS = 256;  // MI355X
 
+template <int HD, bool FULLKV, int NW>
+static void launch_nw(dim3 grid, hipStream_t s, const uint16_t *qkv, int ld_qkv, uint16_t *o,
+                      int ld_o, int k, int Hq, int Hkv, float scale_log2, const int32_t *seq_off,
+                      const int32_t *seq_len, const FullKV &fkv, float *lse, int paired) {
+  hipLaunchKernelGGL((attn_kernel<HD, FULLKV, NW>), grid, dim3(64 * NW), 0, s, qkv, ld_qkv, o,
+                     ld_o, k, Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse, paired);
+}
+
 template <bool FULLKV>
 static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
                         int Hq, int Hkv, int hd, const int32_t *seq_off, const int32_t *seq_len,
@@ -390,17 +400,29 @@ static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, 
   // head's and sequence's longest tiles are dispatched first. Per-sequence lengths (k is then
   // only their bound): a quarter of the units of a longest sequence per (head, sequence), each
   // workgroup looping over its share.
-  const int nqt = (k + AttnCfg<128>::BQ - 1) / AttnCfg<128>::BQ;
-  const int paired = (long)Hq * B * nqt <= ATTN_CUS;
-  const int units = paired ? ((k + AttnCfg<128>::BQP - 1) / AttnCfg<128>::BQP + 1) / 2 : nqt;
+  const long hb = (long)Hq * B;
+  const long t256 = hb * ((k + 255) / 256);
+  int nw = 8, paired = t256 <= ATTN_CUS;
+  // At most half a wave of 256-row tiles: four-wave workgroups (pairs of 64-row q-tiles), twice
+  // as many of them on the CUs. 1024 routed rows, 8 heads: 15.1 -> 12.3 us; 2048 rows, 12 heads
+  // 20.9 -> 18.8 us; identical results (each wave's rows see the same key tiles in the same
+  // order). At 256 workgroups of eight waves (4096 rows, 16 heads) it gains nothing.
+  if (t256 <= 128) nw = 4;
+  const int bq = 32 * nw;
+  const int units = paired ? ((k + bq / 2 - 1) / (bq / 2) + 1) / 2 : (k + bq - 1) / bq;
   const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)(seq_len ? (units + 3) / 4 : units));
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
-  if (hd == 128)
-    hipLaunchKernelGGL((attn_kernel<128, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
-                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse, paired);
-  else
-    hipLaunchKernelGGL((attn_kernel<64, FULLKV>), grid, dim3(512), 0, s, qkv, ld_qkv, o, ld_o, k,
-                       Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse, paired);
+#define XMOD_ATTN_NW(HD_, NW_)                                                                \
+  launch_nw<HD_, FULLKV, NW_>(grid, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv, scale_log2, seq_off, \
+                              seq_len, fkv, lse, paired)
+  if (hd == 128) {
+    if (nw == 8) XMOD_ATTN_NW(128, 8);
+    else XMOD_ATTN_NW(128, 4);
+  } else {
+    if (nw == 8) XMOD_ATTN_NW(64, 8);
+    else XMOD_ATTN_NW(64, 4);
+  }
+#undef XMOD_ATTN_NW
 }
 
 hipError_t launch_attention(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
