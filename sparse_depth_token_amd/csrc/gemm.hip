@@ -106,7 +106,7 @@ struct GemmCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY, int NL>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY, int NL, int SCHED>
 __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>::NT),
                              (GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>::WAVES_PER_EU)) void
 gemm_kernel(GemmArgs g) {
@@ -379,7 +379,47 @@ gemm_kernel(GemmArgs g) {
   // One loop body with rotating stage offsets (kept in scalar registers): a single exit keeps
   // the accumulators in one register assignment for the epilogue. Loader and compute waves
   // meet at the same barriers: one after the first tile, one per k-tile, one after the loop.
-  if (loader) {
+  if constexpr (SCHED == 1) {
+    // Alternating groups: waves 0-3 and 4-7 (one of each per SIMD) take turns between a load
+    // phase (both k-steps' fragments of a k-tile into registers, this wave's share of the DMA
+    // copies of the tile NS - 1 ahead) and a compute phase (that k-tile's MFMAs from
+    // registers), one barrier between phases, the second group one phase behind the first:
+    // while one wave of a SIMD computes, the other loads.
+    static_assert(NL == 0 && C::NW == 8 && KS == 2 && !C::A_KM && !C::B_KM, "alternating schedule");
+    const int grp = wid >> 2;
+    constexpr int WAIT_PH = (NDMA & 15) | (7 << 4) | (0 << 8) | ((NDMA >> 4) << 14);
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
+    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));  // every copy landed
+    __syncthreads();
+    int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
+    if (grp == 1) __builtin_amdgcn_s_barrier();
+#pragma unroll 1
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int f = 0; f < NFR; ++f) load_frag(lds + st_cur, ks, ks, f);
+      issue_tile(kt + NS - 1, st_dma);
+      // this phase's fragments have landed; the copies of the previous load phase too
+      __builtin_amdgcn_s_waitcnt(WAIT_PH);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < NMF; ++t) {
+          const int i = t / C::TN, j = t % C::TN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0,
+                                                             0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      st_dma = st_cur;
+      st_cur = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
+    }
+    if (grp == 0) __builtin_amdgcn_s_barrier();
+  } else if (loader) {
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
@@ -563,7 +603,8 @@ gemm_kernel(GemmArgs g) {
   }  // tile loop
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY = LAY_NT, int NL = 0>
+template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY = LAY_NT, int NL = 0,
+          int SCHED = 0>
 static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
   using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>;
   const int tiles_m = (g.M + BM - 1) / BM;
@@ -572,8 +613,8 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
   const int tiles = tiles_m * tiles_n;
   const int wgs_per_cu = C::WAVES_PER_EU * 4 / (C::NW + NL);  // resident workgroups per CU
   const int grid = g.map.n_dev ? min(tiles, 256 * wgs_per_cu) : tiles;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>), dim3(grid), dim3(C::NT),
-                     0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY, NL, SCHED>), dim3(grid),
+                     dim3(C::NT), 0, s, g);
   return hipGetLastError();
 }
 
@@ -581,6 +622,10 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
 //  * SwiGLU with at least two waves of 256x256 tiles: 256x256 (eight waves of 128x64, two per
 //    SIMD, BK = 32, four-stage ring, each wave copying its share): the halved epilogue per flop
 //    and the second wave per SIMD beat 256x128 by ~5 %.
+//  * other products with at least two waves of 256x256 tiles: the same tile with the two wave
+//    groups alternating between load and compute phases (8192 rows, d = 4096: QKV 346 -> 339 us,
+//    O 254 -> 243, down 872 -> 840; identical results). For SwiGLU the alternation gained
+//    < 1 %, and the 256x128 tile below stays ahead on smaller grids.
 //  * otherwise 256x128 (four compute waves of 64x128 plus four loader waves, BK = 64,
 //    three-stage ring) when the grid gives at least 5/8 of the 256 CUs a tile, else 128x128
 //    (four compute waves of 64x64 plus four loader waves), or, when 128x128 tiles would give
@@ -601,6 +646,11 @@ static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
   if constexpr (swiglu) {
     const long t_256 = tm * ((g.N + 256 / half - 1) / (256 / half));
     if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI, LAY>(g, s);
+  }
+  if constexpr (LAY == LAY_NT && !swiglu) {
+    // at least two waves of 256x256 tiles: 256x256, the two wave groups alternating
+    const long t_256 = tm * ((g.N + 255) / 256);
+    if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI, LAY, 0, 1>(g, s);
   }
   const long t_big = tm * ((g.N + 128 / half - 1) / (128 / half));
   if (t_big >= GEMM_CUS * 5 / 8) return run_gemm<256, 128, 64, 128, 64, 3, EPI, LAY, 4>(g, s);
