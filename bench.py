@@ -407,9 +407,10 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
     ([Sparse(8)] + [Dense]) x 4 at B4 x T4096, d 1536, and the X-MoD A3K16 block (one dense
     prefix layer, 48 Sparse(16) layers, one dense anchor) at B4 x T4096, d 1024. Weights are
     drawn on the device (N(0, 0.02), gains 1), activations N(0, 1); each timed call starts from
-    the same hidden state. Reports the block's time and flop rate, and one sparse and one dense
-    layer of the same shapes timed alone (routed tokens/s of the sparse layer; the ratio of the
-    two layers' times). Informational."""
+    the same hidden state. Reports the block's time and flop rate, the same block captured once
+    as a HIP graph and replayed (the host launch cost of its kernels removed), and one sparse
+    and one dense layer of the same shapes timed alone (routed tokens/s of the sparse layer; the
+    ratio of the two layers' times; their sum over the block's layers). Informational."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(seed)
     bf = torch.bfloat16
@@ -448,6 +449,15 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
 
         t_block = timed(lambda: xmod.block_fwd(x, Ls, dims, w.N0, w.N1, A, w.K, bias, w.tau,
                                                w.delta, ws))
+        # the same block captured once as a HIP graph and replayed: the launches of its
+        # kernels (about nine per layer) no longer go through the host one by one
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            xmod.block_fwd(x, Ls, dims, w.N0, w.N1, A, w.K, bias, w.tau, w.delta, ws)
+        t_graph = timed(graph.replay)
+        del graph
         t_sparse = timed(lambda: xmod.sparse_layer_fwd(x, Ls[w.N0], dims, w.K, bias, w.tau,
                                                        w.delta, ws))
         t_dense = timed(lambda: xmod.dense_layer_fwd(x, Ls[0], dims, ws))
@@ -456,6 +466,8 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
         f_block = n_sparse * layer_flops(w, True) + n_dense * layer_flops(w, False)
         out[name] = {"layers": n_layers, "sparse_layers": n_sparse, "block_ms": round(t_block, 4),
                      "block_tflops": round(f_block / (t_block * 1e-3) / 1e12, 1),
+                     "block_graph_replay_ms": round(t_graph, 4),
+                     "layers_alone_ms": round(n_sparse * t_sparse + n_dense * t_dense, 4),
                      "sparse_layer_ms": round(t_sparse, 5), "dense_layer_ms": round(t_dense, 5),
                      "sparse_routed_tokens_per_s": round(w.B * w.k / (t_sparse * 1e-3), 1),
                      "sparse_layer_tflops": round(layer_flops(w, True) / (t_sparse * 1e-3) / 1e12, 1),
@@ -463,7 +475,8 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
                      "sparse_over_dense_time": round(t_sparse / t_dense, 4)}
         del Ls, ws, x, x0
         torch.cuda.empty_cache()
-    out["timing"] = "events around each call, each call from the same hidden state"
+    out["timing"] = ("events around each call (or graph replay), each from the same hidden "
+                     "state")
     return out
 
 

@@ -238,3 +238,38 @@ def test_bias_rotation_free_running(x):
     # free-running block with the oracle's
     ref = oracle.block_forward(xb, host, w, kinds, w.K, tau=w.tau, delta=w.delta)
     check_values(bf16_vals(host_bits(xt)), ref, "rotation block output")
+
+
+@pytest.mark.parametrize("name", ["a3k16_block_b4x4096_d1024"])
+def test_block_graph_replay_equals_eager(x, name):
+    """xmod_block_fwd enqueues kernels only (the bias reset is a fill kernel, not a memset), so
+    it can be captured in a HIP graph. Every one of several replays, with eager work and
+    synchronisations between them, equals the eager block bit for bit."""
+    w = wl.WORKLOADS[name]
+    say(f"[graph replay] {name}")
+    kinds, _, dev, Ls = _gpu_layers(x, w)
+    dims = _dims(x, w)
+    ws = x.alloc_workspace(dims, w.K, x.WS_BLOCK)
+    xb = wl.make_x(w)
+    A = w.AK / w.K
+    x0 = dev_bf16(xb)
+    xt = x0.clone()
+    bt = torch.empty((w.B, w.T), dtype=torch.float32, device="cuda")
+    x.block_fwd(xt, Ls, dims, w.N0, w.N1, A, w.K, bt, w.tau, w.delta, ws)
+    torch.cuda.synchronize()
+    y_eager, b_eager = host_bits(xt), bt.cpu().numpy()
+    xt.copy_(x0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        x.block_fwd(xt, Ls, dims, w.N0, w.N1, A, w.K, bt, w.tau, w.delta, ws)
+    for rep in range(3):
+        xt.copy_(x0)
+        bt.fill_(float(rep + 7))                  # eager work between the replays
+        x.sparse_layer_fwd(x0.clone(), Ls[w.N0], dims, w.K, None, w.tau, w.delta, ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(xt), y_eager), f"replay {rep}: hidden state"
+        assert np.array_equal(bt.cpu().numpy(), b_eager), f"replay {rep}: carried bias"
+    del graph
