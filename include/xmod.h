@@ -134,9 +134,12 @@ xmod_status xmod_route_topk(const void *x, const void *w_router, float router_bi
                             float *logits, int32_t *idx, float *gate, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Top-k of given fp32 logits [B,T]: idx [B,k] int32 ascending; ties to the lower position,
- * -0 equals +0, NaN ranks lowest. gate [B,k] fp32 = sigmoid(logit) at idx, or NULL.
- * If bias is non-NULL, bias[b, idx] += delta (fp32). */
+/* Top-k of given fp32 logits [B,T] ([XMOD] "training-time top-k": the top-1/K tokens of each
+ * sequence; [MOD] "basic architecture": top-k of the router scores): idx [B,k] int32 ascending;
+ * ties to the lower position (the MoE/SSM chapter's routing checklist asks for the tie rule to
+ * be declared), -0 equals +0, NaN ranks lowest. gate [B,k] fp32 = sigmoid(logit) at idx
+ * ([XMOD] Eq. (8)), or NULL. If bias is non-NULL, bias[b, idx] += delta (fp32): the carried
+ * bias grows for every selected token ([XMOD] "three stabilisers"). */
 xmod_status xmod_topk_from_logits(const float *logits, int32_t B, int32_t T, int32_t k,
                                   int32_t *idx, float *gate, float *bias, float delta,
                                   void *stream);
@@ -246,7 +249,10 @@ xmod_status xmod_sparse_layer_fwd_fullkv(void *x, const xmod_layer *layer, const
                                          int32_t *idx_out, float *gate_out, void *ws,
                                          size_t ws_bytes, void *stream);
 
-/* Forward of one dense layer (every token, no gate): y = x + (a + f), in place on x. */
+/* Forward of one dense layer (every token, no gate): y = x + (a + f), in place on x, with
+ * a = Attn(RMSNorm(x)) causal over the whole sequence and f = SwiGLU(RMSNorm(x + a)): the
+ * [Dense] layer of the stacks of [XMOD] Eqs. (1) and (3) (the anchor of every block, the dense
+ * prefix), pre-norm as [MOD] "basic architecture". Workspace: XMOD_WS_DENSE_LAYER. */
 xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_dims *dims,
                                  void *ws, size_t ws_bytes, void *stream);
 
