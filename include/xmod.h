@@ -128,7 +128,8 @@ size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_poin
 /* Router and top-k of one sparse layer ([XMOD] Eq. (8), "training-time top-k"; [MOD]).
  *   x [B,T,d] bf16; w_router [d] bf16; bias [B,T] fp32 or NULL (zeros), read only.
  *   logits [B,T] fp32 out: ell. idx [B,k] int32 out, ascending. gate [B,k] fp32 out:
- *   sigmoid(ell) at idx. k = floor(T/K). No workspace is needed (ws may be NULL). */
+ *   sigmoid(ell) at idx. k = floor(T/K). ws: xmod_workspace_bytes(dims, K, XMOD_WS_ROUTE_TOPK)
+ *   bytes (0 for most shapes), or NULL; see xmod_topk_from_logits. */
 xmod_status xmod_route_topk(const void *x, const void *w_router, float router_bias,
                             const float *bias, float tau, int32_t K, const xmod_dims *dims,
                             float *logits, int32_t *idx, float *gate, void *ws, size_t ws_bytes,
@@ -139,10 +140,15 @@ xmod_status xmod_route_topk(const void *x, const void *w_router, float router_bi
  * ties to the lower position (the MoE/SSM chapter's routing checklist asks for the tie rule to
  * be declared), -0 equals +0, NaN ranks lowest. gate [B,k] fp32 = sigmoid(logit) at idx
  * ([XMOD] Eq. (8)), or NULL. If bias is non-NULL, bias[b, idx] += delta (fp32): the carried
- * bias grows for every selected token ([XMOD] "three stabilisers"). */
+ * bias grows for every selected token ([XMOD] "three stabilisers").
+ * ws: xmod_topk_workspace_bytes(B, T) bytes of device memory, or NULL. The size is nonzero for
+ * sequences longer than 8192 positions (at most 32 MiB: large batches run in groups); with it
+ * each sequence is split over several workgroups, without it each sequence runs on one
+ * workgroup. Both write identical results. A ws smaller than needed: XMOD_ERR_WORKSPACE. */
+size_t xmod_topk_workspace_bytes(int32_t B, int32_t T);
 xmod_status xmod_topk_from_logits(const float *logits, int32_t B, int32_t T, int32_t k,
-                                  int32_t *idx, float *gate, float *bias, float delta,
-                                  void *stream);
+                                  int32_t *idx, float *gate, float *bias, float delta, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* Gather the selected rows: x_packed[b*k + j] = x[b, idx[b,j]] (bit copy). x [B,T,d] bf16,
  * x_packed [B*k, d] bf16 out. ([MOD] "basic architecture": gather of the chosen tokens.) */

@@ -102,8 +102,12 @@ hipError_t launch_router(const uint16_t *x, const uint16_t *w, float beta, const
                          float tau, float *logits, int64_t rows, int d, hipStream_t s,
                          float *s_out = nullptr);
 
+// Top-k of each sequence's logits (ascending positions, ties to the lower position). With
+// scratch (topk_scratch_bytes(B, T) bytes; 0 means none is used) long sequences are split over
+// several workgroups; the result is the same either way.
 hipError_t launch_topk(const float *logits, int B, int T, int k, int32_t *idx, float *gate,
-                       float *bias, float delta, hipStream_t s);
+                       float *bias, float delta, hipStream_t s, void *scratch = nullptr);
+size_t topk_scratch_bytes(int B, int T);
 
 // Eval-time threshold routing: per sequence the tokens with logit >= 0, packed flat in
 // sequence order (counts[b], offsets[b], src[m] = b*T + t, gate[m] = sigmoid(logit)), the

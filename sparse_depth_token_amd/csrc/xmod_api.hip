@@ -93,6 +93,7 @@ bool layer_ok(const xmod_layer *L, bool sparse) {
 
 struct Plan {
   size_t logits = 0, idx = 0, gate = 0, u = 0, qkv = 0, o = 0, a = 0, g = 0, total = 0;
+  size_t topk = 0;                               // scratch of the chunked top-k (may be empty)
   size_t counts = 0, offsets = 0, n_total = 0;  // threshold routing
 };
 
@@ -107,6 +108,7 @@ Plan plan_layer(const xmod_dims *dm, int64_t M, bool sparse, bool threshold = fa
     p.logits = take((size_t)dm->B * dm->T * 4);
     p.idx = take((size_t)M * 4);
     p.gate = take((size_t)M * 4);
+    if (!threshold) p.topk = take(topk_scratch_bytes(dm->B, dm->T));
   }
   if (threshold) {
     p.counts = take((size_t)dm->B * 4);
@@ -197,7 +199,7 @@ xmod_status sparse_layer(void *x, const xmod_layer *L, const xmod_dims *dm, int3
   XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)L->w_router, L->router_bias, bias,
                          tau, logits, (int64_t)dm->B * dm->T, dm->d, s));
   phase_mark(s);
-  XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s));
+  XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s, at<void>(ws, p.topk)));
   phase_mark(s);
   return run_body((uint16_t *)x, topk_map(idx, dm, k), M, nullptr, nullptr, gate, L, dm, k, p,
                   ws, s);
@@ -261,7 +263,7 @@ namespace {
 
 struct PlanMech {
   size_t logits = 0, idx = 0, gate = 0, u = 0, u2 = 0, qkv = 0, kv = 0, o = 0, a = 0, g = 0;
-  size_t total = 0;
+  size_t topk = 0, total = 0;
 };
 
 // kind 0: routed FFN refinement (M = B*k routed rows); 1: full-sequence attention block;
@@ -277,6 +279,7 @@ PlanMech plan_mech(const xmod_dims *dm, int64_t M, int kind) {
     p.logits = take((size_t)BT * 4);
     p.idx = take((size_t)M * 4);
     p.gate = take((size_t)M * 4);
+    p.topk = take(topk_scratch_bytes(dm->B, dm->T));
   }
   if (kind == 0) {
     p.u = take((size_t)M * dm->d * 2);
@@ -300,11 +303,11 @@ PlanMech plan_mech(const xmod_dims *dm, int64_t M, int kind) {
 
 xmod_status route_topk_into(const void *x, const xmod_layer *L, const xmod_dims *dm, int k,
                             float *bias, float tau, float delta, float *logits, int32_t *idx,
-                            float *gate, hipStream_t s) {
+                            float *gate, void *topk_scratch, hipStream_t s) {
   XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)L->w_router, L->router_bias, bias,
                          tau, logits, (int64_t)dm->B * dm->T, dm->d, s));
   phase_mark(s);
-  XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s));
+  XMOD_HIP(launch_topk(logits, dm->B, dm->T, k, idx, gate, bias, delta, s, topk_scratch));
   phase_mark(s);
   return XMOD_OK;
 }
@@ -325,7 +328,7 @@ size_t xmod_train_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entr
 size_t xmod_workspace_bytes(const xmod_dims *dims, int32_t K, int32_t entry_point) {
   if (check_dims(dims) != XMOD_OK) return 0;
   switch (entry_point) {
-    case XMOD_WS_ROUTE_TOPK: return 0;
+    case XMOD_WS_ROUTE_TOPK: return topk_scratch_bytes(dims->B, dims->T);
     case XMOD_WS_SPARSE_LAYER:
       if (K < 1 || dims->T / K < 1) return 0;
       return plan_layer(dims, (int64_t)dims->B * (dims->T / K), true).total;
@@ -356,26 +359,36 @@ xmod_status xmod_route_topk(const void *x, const void *w_router, float router_bi
                             const float *bias, float tau, int32_t K, const xmod_dims *dims,
                             float *logits, int32_t *idx, float *gate, void *ws, size_t ws_bytes,
                             void *stream) {
-  (void)ws; (void)ws_bytes;
   const xmod_status st = check_dims(dims);
   if (st != XMOD_OK) return st;
   if (!x || !w_router || !logits || !idx || !gate || K < 1 || dims->T / K < 1)
     return XMOD_ERR_INVALID_ARG;
   if (!isfinite(router_bias) || !isfinite(tau)) return XMOD_ERR_INVALID_ARG;
+  const size_t need = topk_scratch_bytes(dims->B, dims->T);
+  if (ws && ws_bytes < need) return XMOD_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)w_router, router_bias, bias, tau,
                          logits, (int64_t)dims->B * dims->T, dims->d, s));
-  XMOD_HIP(launch_topk(logits, dims->B, dims->T, dims->T / K, idx, gate, nullptr, 0.f, s));
+  XMOD_HIP(launch_topk(logits, dims->B, dims->T, dims->T / K, idx, gate, nullptr, 0.f, s,
+                       need ? ws : nullptr));
   return XMOD_OK;
 }
 
+size_t xmod_topk_workspace_bytes(int32_t B, int32_t T) {
+  if (B < 1 || T < 1 || T > 65536) return 0;
+  return topk_scratch_bytes(B, T);
+}
+
 xmod_status xmod_topk_from_logits(const float *logits, int32_t B, int32_t T, int32_t k,
-                                  int32_t *idx, float *gate, float *bias, float delta,
-                                  void *stream) {
+                                  int32_t *idx, float *gate, float *bias, float delta, void *ws,
+                                  size_t ws_bytes, void *stream) {
   if (!logits || !idx || B < 1 || T < 1 || k < 1 || k > T) return XMOD_ERR_INVALID_ARG;
   if (T > 65536) return XMOD_ERR_UNSUPPORTED;
   if (!isfinite(delta)) return XMOD_ERR_INVALID_ARG;
-  XMOD_HIP(launch_topk(logits, B, T, k, idx, gate, bias, delta, (hipStream_t)stream));
+  const size_t need = topk_scratch_bytes(B, T);
+  if (ws && ws_bytes < need) return XMOD_ERR_WORKSPACE;
+  XMOD_HIP(launch_topk(logits, B, T, k, idx, gate, bias, delta, (hipStream_t)stream,
+                       need ? ws : nullptr));
   return XMOD_OK;
 }
 
@@ -754,7 +767,7 @@ xmod_status xmod_routed_ffn_fwd(void *x, const xmod_layer *layer, const xmod_dim
   uint16_t *u = at<uint16_t>(ws, p.u), *gbuf = at<uint16_t>(ws, p.g);
   phase_begin(s, 0);
   const xmod_status r = route_topk_into(x, layer, dims, k, bias, tau, delta, at<float>(ws, p.logits),
-                                        idx, gate, s);
+                                        idx, gate, at<void>(ws, p.topk), s);
   if (r != XMOD_OK) return r;
   const RowMap map = topk_map(idx, dims, k);
   XMOD_HIP(launch_gather_rows((const uint16_t *)x, map, (const uint16_t *)layer->g_ffn,
@@ -842,7 +855,7 @@ xmod_status xmod_sparse_layer_fwd_fullkv(void *x, const xmod_layer *layer, const
   float *a = at<float>(ws, p.a);
   phase_begin(s, 0);
   const xmod_status r = route_topk_into(x, layer, dims, k, bias, tau, delta,
-                                        at<float>(ws, p.logits), idx, gate, s);
+                                        at<float>(ws, p.logits), idx, gate, at<void>(ws, p.topk), s);
   if (r != XMOD_OK) return r;
   RowMap all;
   all.T = T; all.x_rows = BT;
@@ -905,7 +918,8 @@ namespace {
 int64_t pad_rows(int64_t M) { return (M + 63) / 64 * 64; }
 
 struct PlanTrain {
-  size_t s = 0, logits = 0, idx = 0, gate = 0, X = 0, u = 0, qkv = 0, o = 0, lse = 0, a = 0;
+  size_t s = 0, logits = 0, idx = 0, gate = 0, topk = 0, X = 0, u = 0, qkv = 0, o = 0, lse = 0;
+  size_t a = 0;
   size_t v = 0, g = 0, z = 0, f = 0, total = 0;
 };
 
@@ -920,6 +934,7 @@ PlanTrain plan_train(const xmod_dims *dm, int64_t M) {
   p.logits = take(BT * 4);
   p.idx = take(M * 4);
   p.gate = take(M * 4);
+  p.topk = take(topk_scratch_bytes(dm->B, dm->T));
   p.X = take(Mp * d * 2);
   p.u = take(Mp * d * 2);
   p.qkv = take(Mp * nqkv * 2);
@@ -1015,7 +1030,8 @@ xmod_status xmod_sparse_layer_fwd_train(void *x, const xmod_layer *layer, const 
   XMOD_HIP(launch_router((const uint16_t *)x, (const uint16_t *)layer->w_router,
                          layer->router_bias, bias, tau, logits, BT, d, s, sv));
   phase_mark(s);
-  XMOD_HIP(launch_topk(logits, dims->B, dims->T, k, idx, gate, bias, delta, s));
+  XMOD_HIP(launch_topk(logits, dims->B, dims->T, k, idx, gate, bias, delta, s,
+                       at<void>(saved, p.topk)));
   if (idx_out) XMOD_HIP(launch_copy32(idx_out, idx, M, s));
   if (gate_out) XMOD_HIP(launch_copy32(gate_out, gate, M, s));
   phase_mark(s);

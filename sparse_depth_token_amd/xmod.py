@@ -24,7 +24,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # XMOD_NOALLOC_SCRATCH_BYTES
 GEMM_NT, GEMM_NN, GEMM_TN = 0, 1, 2
 
 # Every symbol include/xmod.h declares, in declaration order.
-EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_from_logits", "xmod_pack",
+EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_workspace_bytes",
+            "xmod_topk_from_logits", "xmod_pack",
             "xmod_scatter_gated", "xmod_sparse_layer_fwd", "xmod_sparse_layer_fwd_noalloc",
             "xmod_threshold_select",
             "xmod_sparse_layer_fwd_threshold", "xmod_mask_agreement", "xmod_routed_ffn_fwd",
@@ -68,7 +69,8 @@ _P = ctypes.POINTER
 _sig = {
     "xmod_workspace_bytes": (_sz, [_P(Dims), _i32, _i32]),
     "xmod_route_topk": (_i32, [_vp, _vp, _f32, _vp, _f32, _i32, _P(Dims), _vp, _vp, _vp, _vp, _sz, _vp]),
-    "xmod_topk_from_logits": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _f32, _vp]),
+    "xmod_topk_workspace_bytes": (_sz, [_i32, _i32]),
+    "xmod_topk_from_logits": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _f32, _vp, _sz, _vp]),
     "xmod_pack": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "xmod_scatter_gated": (_i32, [_vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "xmod_sparse_layer_fwd_train": (_i32, [_vp, _P(Layer), _P(Dims), _i32, _vp, _f32, _f32, _vp,
@@ -245,17 +247,26 @@ def alloc_workspace(dims: Dims, K: int, entry: int, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def route_topk(x, w_router, router_bias, bias, tau, K, dims, logits, idx, gate, stream=None):
+def route_topk(x, w_router, router_bias, bias, tau, K, dims, logits, idx, gate, ws=None,
+               stream=None):
+    """ws: None (one workgroup per sequence) or alloc_workspace(dims, K, WS_ROUTE_TOPK)."""
     k = _k(dims, K)
     args = (_x(x, dims), _arg(w_router, "w_router", _BF16, n=dims.d))
     bias_p = _arg(bias, "bias", _F32, n=_bt(dims), optional=True)
     outs = (_arg(logits, "logits", _F32, n=_bt(dims)), _arg(idx, "idx", _I32, at_least=dims.B * k),
             _arg(gate, "gate", _F32, at_least=dims.B * k))
+    wp, wn = _ws(ws) if ws is not None else (None, 0)
     _check(lib.xmod_route_topk(args[0], args[1], router_bias, bias_p, tau, K, ctypes.byref(dims),
-                               *outs, None, 0, _stream(stream)), "xmod_route_topk")
+                               *outs, wp, wn, _stream(stream)), "xmod_route_topk")
 
 
-def topk_from_logits(logits, k, idx, gate=None, bias=None, delta=0.0, stream=None):
+def topk_workspace_bytes(B, T):
+    return int(lib.xmod_topk_workspace_bytes(B, T))
+
+
+def topk_from_logits(logits, k, idx, gate=None, bias=None, delta=0.0, ws=None, stream=None):
+    """ws: None (one workgroup per sequence) or a uint8 device tensor of at least
+    topk_workspace_bytes(B, T) bytes (long sequences split over several workgroups)."""
     if logits.dim() != 2:
         raise ValueError("logits: expected [B, T]")
     B, T = logits.shape
@@ -263,7 +274,8 @@ def topk_from_logits(logits, k, idx, gate=None, bias=None, delta=0.0, stream=Non
     ip = _arg(idx, "idx", _I32, at_least=B * k)
     gp = _arg(gate, "gate", _F32, at_least=B * k, optional=True)
     bp = _arg(bias, "bias", _F32, n=B * T, optional=True)
-    _check(lib.xmod_topk_from_logits(lp, B, T, k, ip, gp, bp, delta, _stream(stream)),
+    wp, wn = _ws(ws) if ws is not None else (None, 0)
+    _check(lib.xmod_topk_from_logits(lp, B, T, k, ip, gp, bp, delta, wp, wn, _stream(stream)),
            "xmod_topk_from_logits")
 
 

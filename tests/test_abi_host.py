@@ -115,9 +115,22 @@ def test_block_rejects_before_launch(x):
 
 def test_stage_entry_points_reject_before_launch(x):
     L = x.lib
-    assert L.xmod_topk_from_logits(FAKE, 2, 100, 0, FAKE, None, None, 0.0, None) == x.ERR_INVALID_ARG
-    assert L.xmod_topk_from_logits(FAKE, 2, 100, 101, FAKE, None, None, 0.0, None) == x.ERR_INVALID_ARG
-    assert L.xmod_topk_from_logits(FAKE, 1, 70000, 5, FAKE, None, None, 0.0, None) == x.ERR_UNSUPPORTED
+    f = L.xmod_topk_from_logits
+    assert f(FAKE, 2, 100, 0, FAKE, None, None, 0.0, None, 0, None) == x.ERR_INVALID_ARG
+    assert f(FAKE, 2, 100, 101, FAKE, None, None, 0.0, None, 0, None) == x.ERR_INVALID_ARG
+    assert f(FAKE, 1, 70000, 5, FAKE, None, None, 0.0, None, 0, None) == x.ERR_UNSUPPORTED
+    # the chunked select's workspace: per 4096-position chunk the counts of 2048 buckets and two
+    # bases, per sequence the threshold; none for sequences of at most 8192 positions; large
+    # batches run in groups of at most 4096 chunks
+    n = L.xmod_topk_workspace_bytes
+    assert n(1, 8192) == 0 and n(1, 70000) == 0 and n(0, 16384) == 0
+    assert n(1, 8193) == 3 * 8192 + 3 * 8 + 8
+    assert n(1, 32768) == 8 * 8192 + 8 * 8 + 8
+    assert n(256, 65536) == 256 * (16 * 8192 + 16 * 8 + 8) == n(1000, 65536)
+    assert f(FAKE, 1, 32768, 5, FAKE, None, None, 0.0, FAKE, n(1, 32768) - 1,
+             None) == x.ERR_WORKSPACE
+    dm = _dims(x, T=16384)
+    assert x.workspace_bytes(dm, 4, x.WS_ROUTE_TOPK) == n(dm.B, dm.T) > 0
     assert L.xmod_pack(FAKE, FAKE, 2, 10, 100, 5, FAKE, None) == x.ERR_UNSUPPORTED
     assert L.xmod_pack(FAKE, None, 2, 10, 128, 5, FAKE, None) == x.ERR_INVALID_ARG
     assert L.xmod_scatter_gated(FAKE, FAKE, FAKE, float("inf"), FAKE, FAKE, 2, 10, 128, 5,

@@ -48,30 +48,61 @@ def _logit_cases():
         lv = rng.integers(0, levels, (B, T)).astype(np.float32) - 1.0
         lv[rng.random(lv.shape) < 0.2] = -0.0
         cases.append((f"{levels}-level ties B{B} T{T} k{k}", lv, k))
+    # shapes of the chunked select (4096-position chunks): a ragged last chunk, k = 1 and k = T,
+    # many sequences (1370 x 3 chunks: two groups of at most 4096 chunks), and NaN / infinities
+    # across chunks
+    for B, T, k in [(2, 8193, 1), (1, 9000, 9000), (70, 12288, 100), (2, 65535, 30000),
+                    (1370, 8200, 2050)]:
+        cases.append((f"normal B{B} T{T} k{k}", rng.standard_normal((B, T)).astype(np.float32), k))
+    odd = rng.standard_normal((3, 12000)).astype(np.float32)
+    odd[0, ::3] = np.nan
+    odd[1, ::11] = np.inf
+    odd[1, 5::13] = -np.inf
+    odd[2, :] = np.nan
+    odd[2, 7000:7010] = -np.inf
+    cases.append(("NaN and infinities B3 T12000", odd, 4000))
     return cases
 
 
-@pytest.mark.parametrize("case", range(len(_logit_cases())))
-def test_topk_bit_exact(x, case):
+def _ref_topk(ell, k):
+    """The selection with +-inf ordered by value and NaN below everything (then position)."""
+    if np.all(np.isfinite(ell)):
+        return oracle.topk_select(ell, k)
+    B, T = ell.shape
+    nan = np.isnan(ell)
+    v = np.where(nan, 0.0, ell.astype(np.float64))
+    return np.stack([np.sort(np.lexsort((np.arange(T), -v[b], nan[b]))[:k]) for b in range(B)])
+
+
+# (case, chunked): every case on one workgroup per sequence, and the cases long enough for the
+# chunked select (more than 8192 positions) again with its workspace
+_TOPK_PARAMS = [(i, False) for i in range(len(_logit_cases()))] + \
+    [(i, True) for i, (_, ell, _) in enumerate(_logit_cases()) if ell.shape[1] > 8192]
+
+
+@pytest.mark.parametrize("case,chunked", _TOPK_PARAMS)
+def test_topk_bit_exact(x, case, chunked):
     name, ell, k = _logit_cases()[case]
-    say(f"[topk] {name}")
+    say(f"[topk] {name} chunked={chunked}")
     B, T = ell.shape
     lg = torch.from_numpy(ell).cuda()
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     gate = torch.empty((B, k), dtype=torch.float32, device="cuda")
     bias0 = (np.random.default_rng(case).standard_normal((B, T)) * 0.1).astype(np.float32)
     bias = torch.from_numpy(bias0).cuda()
-    x.topk_from_logits(lg, k, idx, gate, bias, 0.05)
+    ws = None
+    if chunked:
+        n = x.topk_workspace_bytes(B, T)
+        assert n > 0
+        ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")  # not zeroed: unused
+    x.topk_from_logits(lg, k, idx, gate, bias, 0.05, ws=ws)
     torch.cuda.synchronize()
-    if np.all(np.isfinite(ell)):
-        ref = oracle.topk_select(ell, k)
-    else:  # the oracle requires finite logits; order +-inf explicitly by value, then position
-        ref = np.stack([np.sort(np.lexsort((np.arange(T), -ell[b].astype(np.float64)))[:k])
-                        for b in range(B)])
+    ref = _ref_topk(ell, k)
     got = idx.cpu().numpy()
     assert np.array_equal(got, ref), f"{name}: first mismatch {np.argwhere(got != ref)[:3]}"
-    want_gate = oracle.sigmoid(ell[np.arange(B)[:, None], ref])
-    assert np.allclose(gate.cpu().numpy(), want_gate, rtol=2e-6, atol=1e-30)
+    with np.errstate(all="ignore"):
+        want_gate = oracle.sigmoid(ell[np.arange(B)[:, None], ref])
+    assert np.allclose(gate.cpu().numpy(), want_gate, rtol=2e-6, atol=1e-30, equal_nan=True)
     want_bias = bias0.copy()
     want_bias[np.arange(B)[:, None], ref] = (bias0[np.arange(B)[:, None], ref] + np.float32(0.05))
     assert np.array_equal(bias.cpu().numpy(), want_bias)
