@@ -520,20 +520,30 @@ def measured_ceilings(w, reps=10):
            "hbm_read_gbs_by_loads_in_flight": {str(dep): round(n / t / 1e9, 1)
                                                for dep, t in t_reads.items()},
            "mfma_bf16_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
-    gemms = {}
+    # the same products by the vendor library and by this library's GEMM (xmod_gemm_bf16_nt,
+    # plain bf16 store), one after the other on the same operands (N(0, 1), so the matrix
+    # cores draw the power of random data), after a warm-up of a second each
+    gemms, ours = {}, {}
     for name, (m, nn, kk) in {"gateup_shape": (M, 2 * w.ffn_hidden, w.d),
                               "square_8192": (8192, 8192, 8192)}.items():
         a = torch.randn(m, kk, device="cuda").to(torch.bfloat16)
         bw = torch.randn(nn, kk, device="cuda").to(torch.bfloat16)
-        t = timed(lambda: torch.matmul(a, bw.t()))
-        gemms[name] = round(2.0 * m * nn * kk / t / 1e12, 1)
-        del a, bw
+        c = torch.empty(m, nn, device="cuda", dtype=torch.bfloat16)
+        for label, fn in (("vendor", lambda: torch.matmul(a, bw.t(), out=c)),
+                          ("ours", lambda: xmod.gemm_bf16_nt(a, bw, c))):
+            t_one = timed(fn)
+            for _ in range(max(1, int(1.0 / t_one))):
+                fn()
+            t = min(timed(fn) for _ in range(3))
+            (gemms if label == "vendor" else ours)[name] = round(2.0 * m * nn * kk / t / 1e12, 1)
+        del a, bw, c
     out["library_gemm_tflops"] = gemms
+    out["this_library_gemm_tflops"] = ours
     out["note"] = ("torch copy (read + write), the library's streaming-read probe (4, 8 or 16 "
                    "16-byte loads in flight per thread, 1024 threads per CU; the best is "
                    "hbm_read_gbs) and back-to-back MFMA probe, and torch.matmul (vendor library) "
-                   "on this GPU; the roofline fractions use the vendor peaks (8 TB/s, "
-                   "2.5 PFLOP/s)")
+                   "beside this library's plain GEMM on the same operands, on this GPU; the "
+                   "roofline fractions use the vendor peaks (8 TB/s, 2.5 PFLOP/s)")
     return out
 
 
