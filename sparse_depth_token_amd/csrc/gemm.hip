@@ -112,6 +112,10 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>::NT)
 gemm_kernel(GemmArgs g) {
   using C = GemmCfg<BM, BN, WM, WN, BK, NS, EPI, LAY, NL>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
+  // residual epilogue: the destination row in x and the gate factor of each tile row
+  constexpr bool RES = EPI == EPI_RESIDUAL;
+  __shared__ int64_t s_xrow[RES ? BM : 1];
+  __shared__ float s_gate[RES ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r32 = lane & 31, gq = lane >> 5;
@@ -148,6 +152,18 @@ gemm_kernel(GemmArgs g) {
   const int tn = (wg % per_group) / gsz;
   const int m0 = tm * BM;
   const int n0 = tn * C::BN_OUT;  // first output column
+  // The residual epilogue's per-row operands (the row map's entry and the gate factor), loaded
+  // now into registers (thread t: tile row t) so that their latency passes under the k loop,
+  // and parked in LDS after it: the epilogue's loads of x then depend on no other global load.
+  int64_t ep_xrow = 0;
+  float ep_gate = 0.f;
+  if (RES && tid < BM && m0 + tid < M) {
+    ep_xrow = rowmap_x(g.map, m0 + tid);
+    if (g.gate) {
+      const float gm = g.gate[m0 + tid];
+      ep_gate = g.residual_form == 1 ? gm : __fmul_rn(g.varsigma, gm);
+    }
+  }
 
   // --- DMA descriptors (rows fixed across k-tiles) ---
   // 1 KB block b of a tile holds rows RPB*b .. RPB*b + RPB-1 and is filled by wave b % NW with
@@ -452,6 +468,10 @@ gemm_kernel(GemmArgs g) {
       st_cur = st_next;
     }
   }
+  if (RES && tid < BM) {
+    s_xrow[tid] = ep_xrow;
+    s_gate[tid] = ep_gate;
+  }
   __syncthreads();  // all DMA landed and all fragment reads done before LDS holds the C tile
 
   // --- epilogue, in NCH passes of RCH tile rows ---
@@ -524,7 +544,7 @@ gemm_kernel(GemmArgs g) {
     constexpr int CPO = C::BN_OUT / 8;                                // chunks per output row
     constexpr int CPRO = (EPI == EPI_SWIGLU_SAVE ? 3 : 1) * CPO;      // chunks per tile row
     constexpr int CHUNKS = C::RCH * CPRO;
-#pragma unroll 2
+#pragma unroll 4
     for (int id = tid; id < CHUNKS; id += C::NT) {
       const int r = id / CPRO, cc = id % CPRO;
       const int part = EPI == EPI_SWIGLU_SAVE ? cc / CPO : 0;  // g, zg, zu
@@ -533,7 +553,7 @@ gemm_kernel(GemmArgs g) {
       if (EPI == EPI_RESIDUAL) {
         const float *lf = (const float *)lds + r * C::CS + cc * 8;
         const f32x4 f0 = *(const f32x4 *)lf, f1 = *(const f32x4 *)(lf + 4);
-        const int64_t xrow = rowmap_x(g.map, m);
+        const int64_t xrow = s_xrow[r_lo + r];
         uint16_t *xp = g.x + xrow * g.ldc + n;
         f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};  // no a: a = 0
         if (g.a) {
@@ -543,7 +563,7 @@ gemm_kernel(GemmArgs g) {
         }
         const u32x4 xv = *(const u32x4 *)xp;
         const bool mod = g.gate && g.residual_form == 1;
-        const float gg = g.gate ? (mod ? g.gate[m] : __fmul_rn(g.varsigma, g.gate[m])) : 0.f;
+        const float gg = s_gate[r_lo + r];
         u32x4 yv;
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
