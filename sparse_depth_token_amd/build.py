@@ -28,9 +28,16 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host AddressSanitizer on the library's host code only (argument checks, workspace planning,
+# launch set-up); the device code is built as in the product. Each sanitizer flag sits right
+# after -Xarch_host so that it reaches the host compilation alone.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Xarch_host", "-shared-libasan"]
+
+
+def _compile(src: str, verbose: bool, build_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in l]
@@ -41,14 +48,18 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libxmod.so; always rebuilds. Returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR,
+          host_asan: bool = False) -> str:
+    """Compile every source and link the library (libxmod.so in the package unless `out` says
+    otherwise); always rebuilds. host_asan: host code under AddressSanitizer (load the result
+    with the sanitizer's runtime preloaded). Returns the library path."""
+    os.makedirs(build_dir, exist_ok=True)
+    extra = ASAN_FLAGS if host_asan else []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
-                       capture_output=True, text=True)
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-o", tmp,
+                        *objs], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     # every internal symbol must be defined (a kernel whose host stub was dropped shows up here)
@@ -56,10 +67,10 @@ def build(verbose: bool = False) -> str:
     missing = [l.split()[-1] for l in nm.stdout.splitlines() if "xmod" in l]
     if missing:
         raise RuntimeError("undefined library symbols after link: " + ", ".join(missing[:5]))
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

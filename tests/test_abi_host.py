@@ -20,6 +20,15 @@ def x():
         from sparse_depth_token_amd import build
         build.build()
     from sparse_depth_token_amd import xmod
+    # XMOD_TEST_LIB: run these checks against another build of the library (the host
+    # AddressSanitizer build of tests/test_host_asan.py), through the same signatures
+    other = os.environ.get("XMOD_TEST_LIB")
+    if other:
+        L = ctypes.CDLL(other)
+        for name, (res, args) in xmod._sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        xmod.lib = L
     return xmod
 
 
