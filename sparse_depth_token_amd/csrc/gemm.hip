@@ -37,11 +37,21 @@
 
 namespace xmod {
 
-// 16-byte global -> LDS copy (DMA form): lane l of the wave writes bytes [16l, 16l+16) of the
-// 1 KB LDS block at `lds_block` (wave-uniform).
-__device__ __forceinline__ void dma16(const void *gsrc, uint16_t *lds_block) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds_block, 16,
-                                   0, 0);
+// 16-byte global -> LDS copy (DMA form, through a buffer resource): lane l of the wave writes
+// bytes [16l, 16l+16) of the 1 KB LDS block at `lds_block` (wave-uniform), read from byte
+// voff + soff of the resource. voff is the lane's part of the offset, fixed across k-tiles;
+// soff is the k-tile's part, uniform, so a copy costs no vector arithmetic.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      uint16_t *lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds_block, 16, voff, soff, 0, 0);
+}
+// A raw buffer resource over an operand: every byte offset the kernel forms is below 2^32 (the
+// operands hold fewer than 2^31 elements), and the kernel clamps its rows itself, so the
+// record count is the largest one (no range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)0xFFFFFFFFu,
+                                           0x00020000);
 }
 
 // Physical 16-byte chunk index of logical chunk c in LDS row r (rows of BK bf16), for the
@@ -205,8 +215,8 @@ gemm_kernel(GemmArgs g) {
       b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
     }
   }
-  const char *a_bytes = (const char *)g.A;
-  const char *b_bytes[2] = {(const char *)g.B, (const char *)(C::SWIGLU_FWD ? g.B2 : g.B)};
+  const __amdgpu_buffer_rsrc_t rs_a = operand_rsrc(g.A), rs_b = operand_rsrc(g.B);
+  const __amdgpu_buffer_rsrc_t rs_b2 = operand_rsrc(g.B2 ? g.B2 : g.B);
   auto b_half = [&](int i) {  // which weight matrix DMA block i of B reads (SwiGLU: gate / up)
     return C::SWIGLU_FWD ? (((C::RPB * (C::NDW * i + wv)) >> 5) & 1) : 0;  // wave-uniform
   };
@@ -217,24 +227,23 @@ gemm_kernel(GemmArgs g) {
     const int ktc = min(kt, nk_last);
     const uint32_t kb = (uint32_t)ktc * (BK * 2);
     const uint32_t kb_a = C::A_KM ? (uint32_t)ktc * BK * (uint32_t)g.lda * 2u : kb;
-    const char *b_km = (const char *)g.B;
+    bool km_second = false;
     uint32_t kb_b = kb;
     if (C::B_KM) {
       int kr = ktc * BK;
       if (g.K1 > 0 && kr >= g.K1) {
-        b_km = (const char *)g.B2;
+        km_second = true;
         kr -= g.K1;
       }
       kb_b = (uint32_t)kr * (uint32_t)g.ldb * 2u;
     }
 #pragma unroll
     for (int i = 0; i < C::NA; ++i)
-      if (i >= lo && i < hi)
-        dma16(a_bytes + (a_off[i] + kb_a), lds + stage + 512 * (C::NDW * i + wv));
+      if (i >= lo && i < hi) dma16(rs_a, a_off[i], kb_a, lds + stage + 512 * (C::NDW * i + wv));
 #pragma unroll
     for (int i = 0; i < C::NB; ++i)
       if (C::NA + i >= lo && C::NA + i < hi)
-        dma16((C::B_KM ? b_km : b_bytes[b_half(i)]) + (b_off[i] + kb_b),
+        dma16((C::B_KM ? km_second : b_half(i) != 0) ? rs_b2 : rs_b, b_off[i], kb_b,
               lds + stage + C::A_ELEMS + 512 * (C::NDW * i + wv));
   };
   auto issue_tile = [&](int kt, int stage) { issue_part(kt, stage, 0, C::NA + C::NB); };
