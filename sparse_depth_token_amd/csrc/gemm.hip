@@ -33,6 +33,9 @@
 //    tiles are visited in groups of 8 row-blocks for L2 reuse.
 //  * The epilogue goes through LDS (bf16 or fp32 tile, in row chunks when the fp32 tile does
 //    not fit) so global stores and the residual's reads of x and a are 16-byte row chunks.
+//    The exception is the forward SwiGLU product on large grids: a CU-sized grid walks the
+//    tiles, the copy ring runs on from one tile into the next (the next tile's first k-tiles
+//    are copied under this one's last k-steps) and the epilogue stores from registers.
 #include "common.h"
 
 namespace xmod {
@@ -143,25 +146,35 @@ gemm_kernel(GemmArgs g) {
 
   // Tiles are visited in a grid-stride loop: one tile per workgroup when the grid covers them
   // all, several when the row count is device-side and the grid is only CU-sized.
+  // SCHED 2 (persistent walk over a CU-sized grid): the copy ring runs on across tiles. The
+  // last NS - 1 k-steps of a tile copy the first NS - 1 k-tiles of the workgroup's next tile,
+  // and the last k-step reads that tile's first fragments; the epilogue stores from registers
+  // and leaves LDS alone, so the next tile's k loop starts without waiting for a copy.
+  constexpr bool PF = SCHED == 2;
+  static_assert(!PF || (EPI == EPI_SWIGLU && NL == 0), "persistent walk: forward SwiGLU tiles");
+  bf16x8 fa[2][C::TM], fb[2][C::TN];
+  int st_cur = 0, st_dma = (NS - 1) * C::STAGE;  // ring stages: next to multiply, next to fill
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-  if (tile != (int)blockIdx.x) __syncthreads();  // the previous tile's epilogue is done with LDS
+  if (!PF && tile != (int)blockIdx.x) __syncthreads();  // the previous epilogue is done with LDS
 
   // --- tile id: XCD-contiguous remap, then grouped row-block order ---
-  int wg = tile;
-  {
-    const int nwg = n_tiles, q = nwg / 8, rem = nwg % 8;
-    const int xcd = wg % 8, loc = wg / 8;
-    wg = xcd * q + (xcd < rem ? xcd : rem) + loc;
-  }
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * tiles_n;
-  const int group = wg / per_group;
-  const int first_m = group * GROUP;
-  const int gsz = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (wg % per_group) % gsz;
-  const int tn = (wg % per_group) / gsz;
-  const int m0 = tm * BM;
-  const int n0 = tn * C::BN_OUT;  // first output column
+  auto tile_origin = [&](int t, int &m0_, int &n0_) {
+    int wg = t;
+    {
+      const int nwg = n_tiles, q = nwg / 8, rem = nwg % 8;
+      const int xcd = wg % 8, loc = wg / 8;
+      wg = xcd * q + (xcd < rem ? xcd : rem) + loc;
+    }
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int group = wg / per_group;
+    const int first_m = group * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    m0_ = (first_m + (wg % per_group) % gsz) * BM;
+    n0_ = ((wg % per_group) / gsz) * C::BN_OUT;  // first output column
+  };
+  int m0, n0;
+  tile_origin(tile, m0, n0);
   // The residual epilogue's per-row operands (the row map's entry and the gate factor), loaded
   // now into registers (thread t: tile row t) so that their latency passes under the k loop,
   // and parked in LDS after it: the epilogue's loads of x then depend on no other global load.
@@ -186,34 +199,43 @@ gemm_kernel(GemmArgs g) {
   // A k-major operand's block b holds k-rows (512/R) b .. of the tile's R columns; lane l lands
   // at k-row (512/R) b + l / (R/8), physical chunk l % (R/8), so it fetches logical chunk
   // (l % (R/8)) ^ swz_km(k-row) (columns past the matrix are clamped: only stores are masked).
-  uint32_t a_off[C::NA], b_off[C::NB];
+  auto dma_offsets = [&](int tm0, int tn0, uint32_t (&ao)[C::NA], uint32_t (&bo)[C::NB]) {
 #pragma unroll
-  for (int i = 0; i < C::NA; ++i) {
-    if (C::A_KM) {
-      constexpr int CPT = BM / 8, RPT = 64 / CPT;
-      const int krow = RPT * (C::NDW * i + wv) + lane / CPT;
-      const int gm = min(m0 + (((lane % CPT) ^ swz_km(krow)) << 3), M - 8);
-      a_off[i] = ((uint32_t)krow * (uint32_t)g.lda + (uint32_t)gm) * 2u;
-    } else {
-      const int row = C::RPB * (C::NDW * i + wv) + lane / C::CPR;
-      const int gm = min(m0 + row, M - 1);
-      a_off[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+    for (int i = 0; i < C::NA; ++i) {
+      if (C::A_KM) {
+        constexpr int CPT = BM / 8, RPT = 64 / CPT;
+        const int krow = RPT * (C::NDW * i + wv) + lane / CPT;
+        const int gm = min(tm0 + (((lane % CPT) ^ swz_km(krow)) << 3), M - 8);
+        ao[i] = ((uint32_t)krow * (uint32_t)g.lda + (uint32_t)gm) * 2u;
+      } else {
+        const int row = C::RPB * (C::NDW * i + wv) + lane / C::CPR;
+        const int gm = min(tm0 + row, M - 1);
+        ao[i] = ((uint32_t)gm * (uint32_t)g.lda + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+      }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < C::NB; ++i) {
-    if (C::B_KM) {
-      constexpr int CPT = BN / 8, RPT = 64 / CPT;
-      const int krow = RPT * (C::NDW * i + wv) + lane / CPT;
-      const int gn = min(n0 + (((lane % CPT) ^ swz_km(krow)) << 3), g.N - 8);
-      b_off[i] = ((uint32_t)krow * (uint32_t)g.ldb + (uint32_t)gn) * 2u;
-    } else {
-      const int row = C::RPB * (C::NDW * i + wv) + lane / C::CPR;
-      // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
-      int gn = C::SWIGLU_FWD ? n0 + (row >> 6) * 32 + (row & 31) : n0 + row;
-      gn = min(gn, g.N - 1);
-      b_off[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+    for (int i = 0; i < C::NB; ++i) {
+      if (C::B_KM) {
+        constexpr int CPT = BN / 8, RPT = 64 / CPT;
+        const int krow = RPT * (C::NDW * i + wv) + lane / CPT;
+        const int gn = min(tn0 + (((lane % CPT) ^ swz_km(krow)) << 3), g.N - 8);
+        bo[i] = ((uint32_t)krow * (uint32_t)g.ldb + (uint32_t)gn) * 2u;
+      } else {
+        const int row = C::RPB * (C::NDW * i + wv) + lane / C::CPR;
+        // SwiGLU: 32-row blocks of the B tile alternate gate and up weights.
+        int gn = C::SWIGLU_FWD ? tn0 + (row >> 6) * 32 + (row & 31) : tn0 + row;
+        gn = min(gn, g.N - 1);
+        bo[i] = ((uint32_t)gn * (uint32_t)g.ldb + (((lane % C::CPR) ^ swz<BK>(row)) << 3)) * 2u;
+      }
     }
+  };
+  uint32_t a_off[C::NA], b_off[C::NB], a_nx[C::NA], b_nx[C::NB];
+  dma_offsets(m0, n0, a_off, b_off);
+  const bool has_next = PF && tile + (int)gridDim.x < n_tiles;
+  if (has_next) {
+    int m1, n1;
+    tile_origin(tile + gridDim.x, m1, n1);
+    dma_offsets(m1, n1, a_nx, b_nx);
   }
   const __amdgpu_buffer_rsrc_t rs_a = operand_rsrc(g.A), rs_b = operand_rsrc(g.B);
   const __amdgpu_buffer_rsrc_t rs_b2 = operand_rsrc(g.B2 ? g.B2 : g.B);
@@ -224,7 +246,8 @@ gemm_kernel(GemmArgs g) {
   // the last one, into the stage at element offset `stage`. A k-tile of a k-major operand
   // starts BK rows further down; a k-major B switches to B2 at k-row K1 (tile-aligned).
   auto issue_part = [&](int kt, int stage, int lo, int hi) {
-    const int ktc = min(kt, nk_last);
+    const bool nx = PF && kt > nk_last && has_next;  // the next tile's k-tile kt - nk
+    const int ktc = nx ? kt - nk : min(kt, nk_last);
     const uint32_t kb = (uint32_t)ktc * (BK * 2);
     const uint32_t kb_a = C::A_KM ? (uint32_t)ktc * BK * (uint32_t)g.lda * 2u : kb;
     bool km_second = false;
@@ -239,11 +262,13 @@ gemm_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int i = 0; i < C::NA; ++i)
-      if (i >= lo && i < hi) dma16(rs_a, a_off[i], kb_a, lds + stage + 512 * (C::NDW * i + wv));
+      if (i >= lo && i < hi)
+        dma16(rs_a, nx ? a_nx[i] : a_off[i], kb_a, lds + stage + 512 * (C::NDW * i + wv));
 #pragma unroll
     for (int i = 0; i < C::NB; ++i)
       if (C::NA + i >= lo && C::NA + i < hi)
-        dma16((C::B_KM ? km_second : b_half(i) != 0) ? rs_b2 : rs_b, b_off[i], kb_b,
+        dma16((C::B_KM ? km_second : b_half(i) != 0) ? rs_b2 : rs_b, nx ? b_nx[i] : b_off[i],
+              kb_b,
               lds + stage + C::A_ELEMS + 512 * (C::NDW * i + wv));
   };
   auto issue_tile = [&](int kt, int stage) { issue_part(kt, stage, 0, C::NA + C::NB); };
@@ -292,7 +317,6 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  bf16x8 fa[2][C::TM], fb[2][C::TN];
   // Fragment f of k-step ks of stage st into buffer buf, in first-use order of the MFMA loop
   // below (row-major over (i, j)): A0, B0 .. B(TN-1), A1 .. A(TM-1).
   // Two transposing reads (k 0..3 and 4..7 of the lane's 8) of a k-major fragment. The
@@ -417,7 +441,8 @@ gemm_kernel(GemmArgs g) {
     for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
     __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));  // every copy landed
     __syncthreads();
-    int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
+    st_cur = 0;
+    st_dma = (NS - 1) * C::STAGE;
     if (grp == 1) __builtin_amdgcn_s_barrier();
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
@@ -449,7 +474,8 @@ gemm_kernel(GemmArgs g) {
     for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
     __syncthreads();
-    int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
+    st_cur = 0;
+    st_dma = (NS - 1) * C::STAGE;
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
       // stage st_dma was released by the previous barrier; tile kt + 1 lands before this one
@@ -460,15 +486,18 @@ gemm_kernel(GemmArgs g) {
       st_cur = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
     }
   } else {
-    if (NL == 0) {
+    if (!PF || tile == (int)blockIdx.x) {
+      if (NL == 0) {
 #pragma unroll
-      for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
-      __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+        for (int t = 0; t < NS - 1; ++t) issue_tile(t, t * C::STAGE);
+        __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < NFR; ++f) load_frag(lds, 0, 0, f);
+      st_cur = 0;
+      st_dma = (NS - 1) * C::STAGE;
     }
-    __syncthreads();
-#pragma unroll
-    for (int f = 0; f < NFR; ++f) load_frag(lds, 0, 0, f);
-    int st_cur = 0, st_dma = (NS - 1) * C::STAGE;
 #pragma unroll 1
     for (int kt = 0; kt < nk; ++kt) {
       const int st_next = st_cur == (NS - 1) * C::STAGE ? 0 : st_cur + C::STAGE;
@@ -476,6 +505,32 @@ gemm_kernel(GemmArgs g) {
       st_dma = st_cur;
       st_cur = st_next;
     }
+  }
+  if constexpr (PF) {
+    // SwiGLU straight from the accumulators: each lane holds 4 consecutive output columns of
+    // one row (8-byte stores; the L2 merges a row's pieces). LDS keeps the next tile's copies.
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const int m = m0 + wm0 + 32 * i + r32;
+#pragma unroll
+      for (int p = 0; p < C::TN / 2; ++p)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int n = n0 + (wn0 / 64 + p) * 32 + 8 * q4 + 4 * gq;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float zg = acc[i][2 * p][4 * q4 + e];
+            const float zu = acc[i][2 * p + 1][4 * q4 + e];
+            v[e] = zg / (1.0f + __expf(-zg)) * zu;
+          }
+          u32x2 w2;
+          w2[0] = pack_bf16x2(v[0], v[1]);
+          w2[1] = pack_bf16x2(v[2], v[3]);
+          if (m < M && n < n_out) *(u32x2 *)(g.C + (size_t)m * g.ldc + n) = w2;
+        }
+    }
+    continue;
   }
   if (RES && tid < BM) {
     s_xrow[tid] = ep_xrow;
@@ -630,6 +685,9 @@ gemm_kernel(GemmArgs g) {
     }
   }
   }  // tile loop
+  // PF: the last tile's surplus copies (clamped to its last k-tile) and its unused fragment
+  // reads complete before the workgroup gives up its LDS
+  if (PF) __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (0 << 8) | (0 << 14));
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int NS, int EPI, int LAY = LAY_NT, int NL = 0,
@@ -641,7 +699,7 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
   // device-side row count: a CU-sized grid walks the tiles (g.M is only the bound)
   const int tiles = tiles_m * tiles_n;
   const int wgs_per_cu = C::WAVES_PER_EU * 4 / (C::NW + NL);  // resident workgroups per CU
-  const int grid = g.map.n_dev ? min(tiles, 256 * wgs_per_cu) : tiles;
+  const int grid = g.map.n_dev || SCHED == 2 ? min(tiles, 256 * wgs_per_cu) : tiles;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, BK, NS, EPI, LAY, NL, SCHED>), dim3(grid),
                      dim3(C::NT), 0, s, g);
   return hipGetLastError();
@@ -650,7 +708,9 @@ static hipError_t run_gemm(const GemmArgs &g, hipStream_t s) {
 // Tile choice (measured on the projections of the X-MoD layer at 4096 routed rows):
 //  * SwiGLU with at least two waves of 256x256 tiles: 256x256 (eight waves of 128x64, two per
 //    SIMD, BK = 32, four-stage ring, each wave copying its share): the halved epilogue per flop
-//    and the second wave per SIMD beat 256x128 by ~5 %.
+//    and the second wave per SIMD beat 256x128 by ~5 %. One workgroup per CU walks its tiles
+//    with the ring running across tile boundaries (SCHED 2): no tile waits for its first
+//    k-tile (8192 x 14336 x 4096: 1541 -> 1511 us; 4096 x 5632 x 2048: 179 -> 171 us).
 //  * other products with at least two waves of 256x256 tiles: the same tile with the two wave
 //    groups alternating between load and compute phases (8192 rows, d = 4096: QKV 346 -> 339 us,
 //    O 254 -> 243, down 872 -> 840; identical results). For SwiGLU the alternation gained
@@ -674,7 +734,11 @@ static hipError_t dispatch(const GemmArgs &g, hipStream_t s) {
   const long tm = (g.M + 255) / 256;
   if constexpr (swiglu) {
     const long t_256 = tm * ((g.N + 256 / half - 1) / (256 / half));
-    if (t_256 >= 2 * GEMM_CUS) return run_gemm<256, 256, 128, 64, 32, 4, EPI, LAY>(g, s);
+    if (t_256 >= 2 * GEMM_CUS) {
+      if (EPI == EPI_SWIGLU && g.K / 32 >= 4)
+        return run_gemm<256, 256, 128, 64, 32, 4, EPI_SWIGLU, LAY, 0, 2>(g, s);
+      return run_gemm<256, 256, 128, 64, 32, 4, EPI, LAY>(g, s);
+    }
   }
   if constexpr (LAY == LAY_NT && !swiglu) {
     // at least two waves of 256x256 tiles: 256x256, the two wave groups alternating

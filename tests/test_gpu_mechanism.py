@@ -32,6 +32,7 @@ def _run(x, w, xb, lay, bias, entry, ws_id, K):
     xt = dev_bf16(xb)
     bt = torch.from_numpy(bias.copy()).cuda() if bias is not None else None
     ws = x.alloc_workspace(dims, K, ws_id)
+    ws.fill_(255)  # NaN bits: an intermediate the kernels leave unwritten poisons the output
     L = x.make_layer(layer_to_device(lay))
     if entry is None:
         x.attention_layer_fwd(xt, L, dims, ws)
@@ -75,6 +76,11 @@ ROUTED = {
                                    varsigma_range=(0.5, 1.5)),
     "B2 T2048 K8 d1024 F2816": wl.Workload("rffn_b", 131, 2, 2048, 1024, 8, 8, 128, 2816, 8,
                                            bias_std=0.1, gain_std=0.1),
+    # 2000 routed rows x F 8256: 8 x 65 gate/up tiles of 256 x 256 (ragged rows; the last column
+    # tile half full),
+    # enough for the persistent walk (two or three tiles per workgroup on 256 CUs)
+    "B1 T8000 K4 d256 F8256 (persistent SwiGLU tiles)": wl.Workload(
+        "rffn_c", 140, 1, 8000, 256, 4, 4, 64, 8256, 4, bias_std=0.1, gain_std=0.1),
 }
 
 
