@@ -32,6 +32,7 @@
 //    so lanes that address 4 consecutive keys at 4 consecutive hd offsets hand every lane 4
 //    keys of one hd column.
 #include "common.h"
+#include "wave.h"
 
 namespace xmod {
 
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[t][e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+      mt = max_with_xor32(mt) * scale_log2;
       if (__builtin_amdgcn_ballot_w64(mt > m_ref + RESCALE_LOG2)) {
         const float m_new = fmaxf(m_ref, mt);
         const float corr = __builtin_amdgcn_exp2f(m_ref - m_new);  // exp2(-inf) = 0
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
   // wave owns 32 rows x HD, 16-byte chunks XOR-swizzled by row) so that global stores are
   // whole row segments. Written straight from the MFMA layout, every store instruction would
   // touch 32 rows with 16 bytes each, which the memory system handles far below its rate.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = sum_with_xor32(l_run);
   const float inv = 1.0f / l_tot;
   // log2 of the softmax normaliser in the weights' units: P = exp2(score * scale_log2 - lse)
   if (lse && active && gq == 0 && q_pos < k)

@@ -30,4 +30,19 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// Lane l and lane l ^ 32 (the two halves of the wave) exchange x by v_permlane32_swap, a
+// register-to-register swap of the upper half of one operand with the lower half of the other:
+// swapping x with itself leaves {x, partner} in the two results in lane-dependent order, so a
+// commutative combination of the pair needs no lane select.
+__device__ __forceinline__ float max_with_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace xmod
