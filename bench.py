@@ -600,9 +600,9 @@ def main():
                     help="skip the measured bandwidth, MFMA and library GEMM ceilings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other single-layer workloads (K=2 small layer, K=8 layer)")
-    ap.add_argument("--workload", default=wl.BENCH_WORKLOAD, choices=sorted(
-        n for n, v in wl.WORKLOADS.items() if v.N1 == 0),
-        help="the single-layer workload of the headline (default: the long-context GQA layer)")
+    ap.add_argument("--workload", default=wl.BENCH_WORKLOAD, choices=sorted(wl.WORKLOADS),
+        help="the single-layer workload of the headline (default: the long-context GQA layer); "
+             "a stack workload gives one sparse layer of the stack's shape")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 256 MiB device copy first (a known-size reference for "
                          "FETCH_SIZE / WRITE_SIZE counters)")
