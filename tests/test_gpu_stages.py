@@ -232,13 +232,16 @@ def test_rmsnorm_rows(x, B, T, d, k, use_idx):
                                    # small grids of 64x64 tiles (32-row wave tiles): the
                                    # A3K16 layer's O and down shapes, ragged rows and columns
                                    (1024, 1024, 1024), (1024, 1024, 2816), (1000, 1000, 640),
-                                   (72, 136, 64)])
+                                   (72, 136, 64),
+                                   # 28 x 20 tiles of 256x256 (more than two waves on the
+                                   # 256 CUs), ragged rows and columns
+                                   (7000, 5000, 192)])
 def test_gemm(x, M, N, K):
     say(f"[gemm] M{M} N{N} K{K}")
     rng = np.random.default_rng(12)
     A = wl.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
     Bw = wl.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
-    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")  # unwritten: NaN
     x.gemm_bf16_nt(dev_bf16(A), dev_bf16(Bw), C)
     torch.cuda.synchronize()
     Af, Bf = bf16_vals(A), bf16_vals(Bw)
@@ -255,7 +258,9 @@ def test_gemm(x, M, N, K):
     # weight gradients dY^T X (sums over K token rows); M and N multiples of 8, not of the tile
     ("TN", 256, 768, 512, True, 0), ("TN", 2048, 5632, 4096, True, 0),
     ("TN", 1544, 1032, 192, True, 32), ("TN", 11264, 2048, 256, True, 0),
-    ("NT", 640, 384, 256, True, 0)])
+    ("NT", 640, 384, 256, True, 0),
+    # 256x256 tiles over more than two waves: fp32 and bf16 stores, ragged tiles, a strided A
+    ("NT", 7000, 5000, 192, True, 0), ("NT", 6500, 5200, 256, False, 24)])
 def test_gemm_layouts(x, layout, M, N, K, f32, pad):
     say(f"[gemm {layout}] M{M} N{N} K{K} f32={f32} pad={pad}")
     rng = np.random.default_rng(14)
@@ -266,7 +271,8 @@ def test_gemm_layouts(x, layout, M, N, K, f32, pad):
     Bw = wl.f32_to_bf16_bits((rng.standard_normal(b_shape) * 0.05).astype(np.float32))
     # optional row padding of A: a strided view (leading dimension > its columns)
     Ad = dev_bf16(np.pad(A, ((0, 0), (0, pad)))) [:, :a_shape[1]] if pad else dev_bf16(A)
-    C = torch.empty((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.float32 if f32 else torch.bfloat16,
+                   device="cuda")  # an element the kernel leaves unwritten stays NaN
     x.gemm_bf16(lay, Ad, dev_bf16(Bw), C)
     torch.cuda.synchronize()
     Af, Bf = bf16_vals(A), bf16_vals(Bw)
