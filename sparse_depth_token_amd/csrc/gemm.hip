@@ -19,8 +19,9 @@
 //    registers), plus (optionally) four loader waves that only copy k-tiles into LDS.
 //  * The weight fragment is the MFMA's first operand and the activation fragment its second,
 //    so each lane ends with 4 consecutive output columns of one row.
-//  * k-tiles are copied global -> LDS by the DMA form of the load (global_load_lds_dwordx4:
-//    16 bytes per lane, no staging registers) into an NS-stage LDS ring: tiles kt+1 .. kt+NS-1
+//  * k-tiles are copied global -> LDS by the DMA form of the load (buffer_load_dwordx4 ... lds
+//    through one buffer resource per operand: 16 bytes per lane, no staging registers, the
+//    k-tile's offset a scalar operand) into an NS-stage LDS ring: tiles kt+1 .. kt+NS-1
 //    are in flight while tile kt is multiplied. Before each barrier a wave waits only for its
 //    own loads of the next tile. When the compute waves copy their own tiles, the copies are
 //    spread over the k-steps (the CU's vector-memory path moves 64 bytes per clock).
