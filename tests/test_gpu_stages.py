@@ -114,7 +114,8 @@ def test_topk_bit_exact(x, case, chunked):
 
 @pytest.mark.parametrize("name,B,T,d,skew", [("d256", 2, 512, 256, 0.0), ("d2048", 8, 4096, 2048, 0.0),
                                              ("d1536 ragged", 3, 999, 1536, 0.0),
-                                             ("d4096 skewed", 1, 8192, 4096, 0.01)])
+                                             ("d4096 skewed", 1, 8192, 4096, 0.01),
+                                             ("d8192 widest, ragged", 2, 1000, 8192, 0.0)])
 def test_router_logits(x, name, B, T, d, skew):
     say(f"[router] {name}")
     w = wl.scaled(wl.WORKLOADS["sparse_k2_b2x512_d256"], B=B, T=T, d=d, skew_frac=skew, seed=7)
@@ -152,7 +153,8 @@ def _rand_idx(rng, B, T, k):
     return np.stack([np.sort(rng.permutation(T)[:k]) for _ in range(B)]).astype(np.int32)
 
 
-@pytest.mark.parametrize("B,T,d,k", [(2, 512, 256, 256), (3, 777, 1536, 100), (1, 4096, 4096, 1024)])
+@pytest.mark.parametrize("B,T,d,k", [(2, 512, 256, 256), (3, 777, 1536, 100), (1, 4096, 4096, 1024),
+                                     (2, 300, 8192, 77)])
 def test_pack_bit_exact(x, B, T, d, k):
     say(f"[pack] B{B} T{T} d{d} k{k}")
     rng = np.random.default_rng(9)
@@ -172,7 +174,7 @@ def _f32_gated(X, g, a, f):
     return (X.astype(np.float32) + p).astype(np.float32)
 
 
-@pytest.mark.parametrize("B,T,d,k", [(2, 512, 256, 256), (3, 777, 1536, 100)])
+@pytest.mark.parametrize("B,T,d,k", [(2, 512, 256, 256), (3, 777, 1536, 100), (2, 300, 8192, 77)])
 def test_scatter_bit_exact_and_untouched_rows(x, B, T, d, k):
     say(f"[scatter] B{B} T{T} d{d} k{k}")
     rng = np.random.default_rng(10)
@@ -203,7 +205,8 @@ def test_scatter_bit_exact_and_untouched_rows(x, B, T, d, k):
 
 
 @pytest.mark.parametrize("B,T,d,k,use_idx", [(2, 512, 256, 256, True), (3, 777, 1536, 100, True),
-                                             (2, 64, 4096, 64, False)])
+                                             (2, 64, 4096, 64, False), (2, 300, 6144, 50, True),
+                                             (1, 64, 8192, 64, False)])
 def test_rmsnorm_rows(x, B, T, d, k, use_idx):
     say(f"[rmsnorm] B{B} T{T} d{d} k{k} idx={use_idx}")
     rng = np.random.default_rng(11)
