@@ -214,6 +214,20 @@ def test_threshold_layer_bench_shape_sampled(x):
     check_threshold(w, xb, lay, bias, got, sample=sample)
 
 
+def test_threshold_layer_routes_nothing(x):
+    """Every logit below 0 in every sequence: the device-side row count is 0, every kernel of
+    the body finds no work, and x and the carried bias come back bit-identical."""
+    w = wl.Workload("thr_none", 83, 3, 700, 512, 8, 2, 64, 1536, 1, bias_std=0.1)
+    say("[threshold layer] no token routed in any sequence")
+    xb = wl.make_x(w)
+    lay = wl.make_layer(w, 0)
+    bias = wl.make_bias(w) + 50.0                        # ell = s - b far below 0 everywhere
+    y_bits, sel, bias_g = run_threshold_gpu(x, w, xb, lay, bias)
+    assert all(len(s) == 0 for s in sel)
+    assert np.array_equal(y_bits, xb)
+    assert np.array_equal(bias_g, bias)
+
+
 def test_threshold_layer_deterministic(x):
     w, _ = SMALL["B4 T700 d512 GQA 8/2 hd64, router bias 0.2"]
     xb = wl.make_x(w)
