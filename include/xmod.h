@@ -48,7 +48,8 @@
  *     XMOD_ERR_INVALID_ARG: NULL required pointer, non-positive size, K < 1, floor(T/K) < 1,
  *       Hq % Hkv != 0, A*K not an integer, wrong number of layers.
  *     XMOD_ERR_UNSUPPORTED: head_dim not 64 or 128, d or ffn_hidden not a multiple of 64,
- *       T > 65536 (top-k holds one sequence in one workgroup), d > 8192.
+ *       T > 65536 (the selection kernels hold one sequence's keys or decisions in one
+ *       workgroup's registers or LDS at some stage), d > 8192.
  *     XMOD_ERR_WORKSPACE: workspace NULL or smaller than xmod_workspace_bytes().
  *     XMOD_ERR_HIP: a kernel launch failed; xmod_last_hip_error() returns the hipError_t
  *       (kept per calling thread). Faults inside kernels surface at the caller's next sync.
