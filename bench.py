@@ -61,10 +61,14 @@ def algorithmic_work(w):
         "gather_rmsnorm": {"bytes": 4.0 * M * d, "flops": 3.0 * M * d},
         "qkv_gemm": {"flops": 2.0 * M * d * nqkv, "bytes": 2.0 * (M * d + nqkv * d + M * nqkv)},
         "attention": {"flops": att_flops, "bytes": 2.0 * (M * nqkv + M * dq)},
-        "o_gemm": {"flops": 2.0 * M * dq * d, "bytes": 2.0 * (M * dq + d * dq + M * d)},
-        "residual_rmsnorm": {"bytes": 6.0 * M * d, "flops": 4.0 * M * d},
+        # a is written in fp32
+        "o_gemm": {"flops": 2.0 * M * dq * d, "bytes": 2.0 * (M * dq + d * dq) + 4.0 * M * d},
+        # X (bf16) and a (fp32) read, v (bf16) written
+        "residual_rmsnorm": {"bytes": 8.0 * M * d, "flops": 4.0 * M * d},
         "gateup_swiglu_gemm": {"flops": 4.0 * M * d * F, "bytes": 2.0 * (M * d + 2 * F * d + M * F)},
-        "down_scatter_gemm": {"flops": 2.0 * M * F * d, "bytes": 2.0 * (M * F + d * F + 3 * M * d)},
+        # g, W_down, X (bf16) and a (fp32) read, the selected rows of x (bf16) written
+        "down_scatter_gemm": {"flops": 2.0 * M * F * d,
+                              "bytes": 2.0 * (M * F + d * F) + 8.0 * M * d},
     }
 
 
