@@ -49,7 +49,11 @@
  *       Hq % Hkv != 0, A*K not an integer, wrong number of layers.
  *     XMOD_ERR_UNSUPPORTED: head_dim not 64 or 128, d or ffn_hidden not a multiple of 64,
  *       T > 65536 (the selection kernels hold one sequence's keys or decisions in one
- *       workgroup's registers or LDS at some stage), d > 8192.
+ *       workgroup's registers or LDS at some stage), d > 8192, or a matrix of 2^31 elements or
+ *       more for the projections (they address operands by 32-bit byte offsets): with M the
+ *       routed rows (B*floor(T/K) for the top-k layer entry points, B*T for the dense, block,
+ *       threshold and mechanism-control entry points), (M + 64) * max(d, dq + 2 dkv,
+ *       2 ffn_hidden) and each weight matrix must stay below 2^31 elements.
  *     XMOD_ERR_WORKSPACE: workspace NULL or smaller than xmod_workspace_bytes().
  *     XMOD_ERR_HIP: a kernel launch failed; xmod_last_hip_error() returns the hipError_t
  *       (kept per calling thread). Faults inside kernels surface at the caller's next sync.
@@ -331,7 +335,7 @@ xmod_status xmod_rmsnorm_rows(const void *x, const int32_t *idx, const void *gai
                               int32_t B, int32_t T, int32_t d, int32_t k, void *out, void *stream);
 
 /* C[M,N] = bf16(A[M,K] B[N,K]^T), fp32 accumulate; all row-major, leading dims in elements.
- * K must be a multiple of 64. */
+ * K must be a multiple of 64; M*lda, N*ldb and M*ldc below 2^31 (XMOD_ERR_UNSUPPORTED). */
 xmod_status xmod_gemm_bf16_nt(const void *A, int32_t lda, const void *Bm, int32_t ldb, void *C,
                               int32_t ldc, int32_t M, int32_t N, int32_t K, void *stream);
 

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -77,6 +78,21 @@ xmod_status check_dims(const xmod_dims *dm) {
   if (dm->head_dim != 64 && dm->head_dim != 128) return XMOD_ERR_UNSUPPORTED;
   if (dm->d % 64 != 0 || dm->ffn_hidden % 64 != 0 || dm->d > 8192) return XMOD_ERR_UNSUPPORTED;
   if (dm->T > 65536) return XMOD_ERR_UNSUPPORTED;
+  return XMOD_OK;
+}
+
+// The GEMMs address their operands with 32-bit byte offsets (one buffer resource per
+// operand), so every matrix a layer multiplies must hold fewer than 2^31 elements: the
+// activations of M rows ([M, d], [M, dq + 2 dkv], [M, dq], and [M, 2F] for the training
+// forward's saved pre-activations, M padded to 64 for the weight gradients) and the weights.
+xmod_status check_rows(const xmod_dims *dm, int64_t M) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t dq = (int64_t)dm->n_q_heads * dm->head_dim;
+  const int64_t nqkv = dq + 2LL * dm->n_kv_heads * dm->head_dim;
+  const int64_t width = std::max({(int64_t)dm->d, nqkv, (int64_t)2 * dm->ffn_hidden});
+  if ((M + 64) * width >= lim) return XMOD_ERR_UNSUPPORTED;
+  if (nqkv * dm->d >= lim || dq * dm->d >= lim || (int64_t)dm->ffn_hidden * dm->d >= lim)
+    return XMOD_ERR_UNSUPPORTED;
   return XMOD_OK;
 }
 
@@ -425,6 +441,7 @@ xmod_status xmod_sparse_layer_fwd(void *x, const xmod_layer *layer, const xmod_d
   const xmod_status st = check_dims(dims);
   if (st != XMOD_OK) return st;
   if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * (dims->T / K)) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
   const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_LAYER);
   if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
@@ -482,6 +499,7 @@ xmod_status xmod_sparse_layer_fwd_noalloc(void *x, const xmod_layer *layer,
   const xmod_status st = check_dims(dims);
   if (st != XMOD_OK) return st;
   if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * (dims->T / K)) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
   const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_LAYER);
   if (need > XMOD_NOALLOC_SCRATCH_BYTES) return XMOD_ERR_WORKSPACE;
@@ -497,6 +515,7 @@ xmod_status xmod_dense_layer_fwd(void *x, const xmod_layer *layer, const xmod_di
   const xmod_status st = check_dims(dims);
   if (st != XMOD_OK) return st;
   if (!x || !layer_ok(layer, false)) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * dims->T) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   const size_t need = xmod_workspace_bytes(dims, 1, XMOD_WS_DENSE_LAYER);
   if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
   return dense_layer(x, layer, dims, ws, (hipStream_t)stream);
@@ -515,6 +534,7 @@ xmod_status xmod_block_fwd(void *x, const xmod_layer *layers, int32_t n_layers,
   if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
   const int64_t expect = (int64_t)N0 + (int64_t)N1 * (ak + 1);
   if (expect != n_layers) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * dims->T) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   for (int64_t i = 0; i < n_layers; ++i) {
     const bool sparse = i >= N0 && ((i - N0) % (ak + 1)) < ak;
     if (!layer_ok(&layers[i], sparse)) return XMOD_ERR_INVALID_ARG;
@@ -561,6 +581,9 @@ xmod_status xmod_gemm_bf16_nt(const void *A, int32_t lda, const void *Bm, int32_
   if (!A || !Bm || !Cm || M < 1 || N < 1 || K < 1 || lda < K || ldb < K || ldc < N)
     return XMOD_ERR_INVALID_ARG;
   if (K % 64 != 0 || N % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || ldc % 8 != 0)
+    return XMOD_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;  // operands addressed by 32-bit byte offsets
+  if ((int64_t)M * lda >= lim || (int64_t)N * ldb >= lim || (int64_t)M * ldc >= lim)
     return XMOD_ERR_UNSUPPORTED;
   GemmArgs g{};
   g.A = (const uint16_t *)A; g.lda = lda; g.B = (const uint16_t *)Bm; g.ldb = ldb;
@@ -728,6 +751,7 @@ xmod_status xmod_sparse_layer_fwd_threshold(void *x, const xmod_layer *layer,
   if (st != XMOD_OK) return st;
   if (!x || !layer_ok(layer, true)) return XMOD_ERR_INVALID_ARG;
   if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * dims->T) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if ((int64_t)dims->B * dims->T > INT32_MAX) return XMOD_ERR_UNSUPPORTED;
   const size_t need = xmod_workspace_bytes(dims, 1, XMOD_WS_SPARSE_THRESHOLD);
   if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
@@ -750,6 +774,7 @@ xmod_status xmod_routed_ffn_fwd(void *x, const xmod_layer *layer, const xmod_dim
                                 void *stream) {
   const xmod_status st = check_dims(dims);
   if (st != XMOD_OK) return st;
+  if (check_rows(dims, (int64_t)dims->B * dims->T) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if (!x || !layer || !layer->w_router || !layer->g_ffn || !layer->w_gate || !layer->w_up ||
       !layer->w_down || K < 1 || dims->T / K < 1)
     return XMOD_ERR_INVALID_ARG;
@@ -794,6 +819,7 @@ xmod_status xmod_attention_layer_fwd(void *x, const xmod_layer *layer, const xmo
                                      void *ws, size_t ws_bytes, void *stream) {
   const xmod_status st = check_dims(dims);
   if (st != XMOD_OK) return st;
+  if (check_rows(dims, (int64_t)dims->B * dims->T) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if (!x || !layer || !layer->g_attn || !layer->w_qkv || !layer->w_o) return XMOD_ERR_INVALID_ARG;
   if (!(layer->rope_theta >= 0.f) || !isfinite(layer->rope_theta)) return XMOD_ERR_INVALID_ARG;
   const size_t need = xmod_workspace_bytes(dims, 1, XMOD_WS_ATTN_LAYER);
@@ -840,6 +866,7 @@ xmod_status xmod_sparse_layer_fwd_fullkv(void *x, const xmod_layer *layer, const
   if (st != XMOD_OK) return st;
   if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
   if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * dims->T) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   const size_t need = xmod_workspace_bytes(dims, K, XMOD_WS_SPARSE_FULLKV);
   if (!ws || ws_bytes < need) return XMOD_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -1009,6 +1036,7 @@ xmod_status xmod_sparse_layer_fwd_train(void *x, const xmod_layer *layer, const 
   if (st != XMOD_OK) return st;
   if (!x || !layer_ok(layer, true) || K < 1 || dims->T / K < 1) return XMOD_ERR_INVALID_ARG;
   if (!isfinite(tau) || !isfinite(delta)) return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * (dims->T / K)) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if (!core_form(layer)) return XMOD_ERR_UNSUPPORTED;
   const int k = dims->T / K;
   const int64_t M = (int64_t)dims->B * k, Mp = pad_rows(M), BT = (int64_t)dims->B * dims->T;
@@ -1082,6 +1110,7 @@ xmod_status xmod_sparse_layer_bwd(const void *x, const void *dy, void *dx,
   if (st != XMOD_OK) return st;
   if (!x || !dy || !dx || !saved || !gr || !layer_ok(layer, true) || K < 1 || dims->T / K < 1)
     return XMOD_ERR_INVALID_ARG;
+  if (check_rows(dims, (int64_t)dims->B * (dims->T / K)) != XMOD_OK) return XMOD_ERR_UNSUPPORTED;
   if (!gr->w_router || !gr->router_bias || !gr->varsigma || !gr->g_attn || !gr->w_qkv ||
       !gr->w_o || !gr->g_ffn || !gr->w_gate || !gr->w_up || !gr->w_down)
     return XMOD_ERR_INVALID_ARG;

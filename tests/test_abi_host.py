@@ -258,3 +258,33 @@ def test_probes_reject_before_launch(x):
     assert L.xmod_probe_read(FAKE, 24, 4, FAKE, None) == x.ERR_INVALID_ARG
     assert L.xmod_probe_read(FAKE, 64, 4, None, None) == x.ERR_INVALID_ARG
     assert L.xmod_probe_read(FAKE, 64, 5, FAKE, None) == x.ERR_INVALID_ARG
+
+
+def test_operand_size_limits_reject_before_launch(x):
+    """The projections address their operands by 32-bit byte offsets: a layer whose activation
+    or weight matrices would hold 2^31 elements or more is refused before any launch (it would
+    otherwise read wrapped addresses)."""
+    L = _layer(x)
+    ws = (FAKE, 1 << 40)
+    # top-k layer: 8 x 16384 routed rows of 2F = 28672 columns (3.8e9 elements)
+    big = _dims(x, B=8, T=65536, d=4096, n_q_heads=32, n_kv_heads=8, ffn_hidden=14336)
+    assert x.lib.xmod_sparse_layer_fwd(FAKE, ctypes.byref(L), ctypes.byref(big), 4, None, 1.0,
+                                       0.05, None, None, *ws, None) == x.ERR_UNSUPPORTED
+    assert x.lib.xmod_sparse_layer_fwd_noalloc(FAKE, ctypes.byref(L), ctypes.byref(big), 4, None,
+                                               1.0, 0.05, None, None, None) == x.ERR_UNSUPPORTED
+    # dense layer and block: every one of the B*T rows is projected
+    dense = _dims(x, B=2, T=65536, d=4096, n_q_heads=32, n_kv_heads=8, ffn_hidden=14336)
+    assert x.lib.xmod_dense_layer_fwd(FAKE, ctypes.byref(L), ctypes.byref(dense), *ws,
+                                      None) == x.ERR_UNSUPPORTED
+    layers = (x.Layer * 2)(*[_layer(x) for _ in range(2)])
+    assert x.lib.xmod_block_fwd(FAKE, layers, 2, ctypes.byref(dense), 0, 1, 0.5, 2, FAKE, 1.0,
+                                0.05, *ws, None) == x.ERR_UNSUPPORTED
+    # a weight matrix of 2^31 elements (F x d = 262144 x 8192) on a tiny input
+    wide = _dims(x, B=1, T=64, d=8192, n_q_heads=64, n_kv_heads=64, ffn_hidden=262144)
+    assert x.lib.xmod_sparse_layer_fwd(FAKE, ctypes.byref(L), ctypes.byref(wide), 1, None, 1.0,
+                                       0.05, None, None, *ws, None) == x.ERR_UNSUPPORTED
+    # stage GEMM: A of 65536 x 32768 elements
+    assert x.lib.xmod_gemm_bf16_nt(FAKE, 32768, FAKE, 32768, FAKE, 64, 65536, 64, 32768,
+                                   None) == x.ERR_UNSUPPORTED
+    assert x.lib.xmod_gemm_bf16(x.GEMM_NT, FAKE, 32768, FAKE, 32768, FAKE, 64, 0, 65536, 64,
+                                32768, None) == x.ERR_UNSUPPORTED
