@@ -660,6 +660,9 @@ def main():
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             r = LayerRun(xmod, wl.WORKLOADS[name])
             cfgs[name] = layer_line(r, args.steps, args.warmup)
+            if not args.no_cpu_baseline:  # the oracle on this workload, a few seconds' sample
+                cfgs[name]["cpu_baseline"] = cpu_baseline(r.w, r.xb, r.lay, r.bias_np,
+                                                          budget_s=4.0)
             del r
             torch.cuda.empty_cache()
         out["configs"] = cfgs
