@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 namespace xmod {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -13,17 +14,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest even (inputs are finite).
+// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest even.
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
+// gfx950 converts in hardware (v_cvt_pk_bf16_f32: round to nearest even, two values at once).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// The same rounding in integer arithmetic (identical bits for finite inputs), for code whose
+// register allocation the conversion instruction's pairing upsets.
+__device__ __forceinline__ uint32_t pack_bf16x2_int(float lo, float hi) {
+  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+  a += 0x7FFFu + ((a >> 16) & 1u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (a >> 16) | (b & 0xFFFF0000u);
 }
 // Unpack 8 bf16 held in a uint4 into floats.
 __device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
@@ -35,6 +45,10 @@ __device__ __forceinline__ void unpack8(const uint4 &v, float *f) {
 __device__ __forceinline__ uint4 pack8(const float *f) {
   return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+__device__ __forceinline__ uint4 pack8_int(const float *f) {
+  return make_uint4(pack_bf16x2_int(f[0], f[1]), pack_bf16x2_int(f[2], f[3]),
+                    pack_bf16x2_int(f[4], f[5]), pack_bf16x2_int(f[6], f[7]));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -41,6 +41,13 @@
 
 namespace xmod {
 
+// The logistic function of the SwiGLU epilogues by the hardware's exp2 and reciprocal (about one
+// ulp each; the products are rounded to bf16 next), where 1 / (1 + e^-z) with a correctly
+// rounded division costs about ten vector instructions per element.
+__device__ __forceinline__ float swiglu_sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
 // 16-byte global -> LDS copy (DMA form, through a buffer resource): lane l of the wave writes
 // bytes [16l, 16l+16) of the 1 KB LDS block at `lds_block` (wave-uniform), read from byte
 // voff + soff of the resource. voff is the lane's part of the offset, fixed across k-tiles;
@@ -523,7 +530,7 @@ gemm_kernel(GemmArgs g) {
           for (int e = 0; e < 4; ++e) {
             const float zg = acc[i][2 * p][4 * q4 + e];
             const float zu = acc[i][2 * p + 1][4 * q4 + e];
-            v[e] = zg / (1.0f + __expf(-zg)) * zu;
+            v[e] = zg * swiglu_sigmoid(zg) * zu;
           }
           u32x2 w2;
           w2[0] = pack_bf16x2(v[0], v[1]);
@@ -561,19 +568,24 @@ gemm_kernel(GemmArgs g) {
             for (int e = 0; e < 4; ++e) {
               const float zg = acc[i][2 * p][4 * q4 + e];
               const float zu = acc[i][2 * p + 1][4 * q4 + e];
-              v[e] = zg / (1.0f + __expf(-zg)) * zu;
+              v[e] = zg * swiglu_sigmoid(zg) * zu;
             }
+            // (the training form's three conversions per element round in integer arithmetic:
+            // the conversion instruction made its register allocation spill; same bits)
+            const auto pk = [](float a, float b) {
+              return EPI == EPI_SWIGLU_SAVE ? pack_bf16x2_int(a, b) : pack_bf16x2(a, b);
+            };
             u32x2 w2;
-            w2[0] = pack_bf16x2(v[0], v[1]);
-            w2[1] = pack_bf16x2(v[2], v[3]);
+            w2[0] = pk(v[0], v[1]);
+            w2[1] = pk(v[2], v[3]);
             uint16_t *t = lds + row * C::CS + colblk + 8 * q4 + 4 * gq;
             *(u32x2 *)t = w2;
             if (EPI == EPI_SWIGLU_SAVE) {  // zg and zu beside g in the tile
-              w2[0] = pack_bf16x2(acc[i][2 * p][4 * q4], acc[i][2 * p][4 * q4 + 1]);
-              w2[1] = pack_bf16x2(acc[i][2 * p][4 * q4 + 2], acc[i][2 * p][4 * q4 + 3]);
+              w2[0] = pk(acc[i][2 * p][4 * q4], acc[i][2 * p][4 * q4 + 1]);
+              w2[1] = pk(acc[i][2 * p][4 * q4 + 2], acc[i][2 * p][4 * q4 + 3]);
               *(u32x2 *)(t + C::BN_OUT) = w2;
-              w2[0] = pack_bf16x2(acc[i][2 * p + 1][4 * q4], acc[i][2 * p + 1][4 * q4 + 1]);
-              w2[1] = pack_bf16x2(acc[i][2 * p + 1][4 * q4 + 2], acc[i][2 * p + 1][4 * q4 + 3]);
+              w2[0] = pk(acc[i][2 * p + 1][4 * q4], acc[i][2 * p + 1][4 * q4 + 1]);
+              w2[1] = pk(acc[i][2 * p + 1][4 * q4 + 2], acc[i][2 * p + 1][4 * q4 + 3]);
               *(u32x2 *)(t + 2 * C::BN_OUT) = w2;
             }
           }
@@ -668,7 +680,7 @@ gemm_kernel(GemmArgs g) {
         for (int e = 0; e < 4; ++e) { dg[e] = d0[e]; dg[4 + e] = d1[e]; }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float sg = 1.0f / (1.0f + __expf(-zg[e]));
+          const float sg = swiglu_sigmoid(zg[e]);
           ou[e] = dg[e] * (zg[e] * sg);
           og[e] = dg[e] * zu[e] * (sg * (1.0f + zg[e] * (1.0f - sg)));
         }

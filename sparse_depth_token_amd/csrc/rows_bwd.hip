@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(
             wacc[i][e] = fmaf(ds[r], Xf[e], wacc[i][e]);
             o[e] = G[e] + ds[r] * wr[i][e];
           }
-          *(uint4 *)(dx + tt[r] * d + (size_t)c * 8) = pack8(o);
+          *(uint4 *)(dx + tt[r] * d + (size_t)c * 8) = pack8_int(o);  // (fewer spills)
         }
       }
     }
