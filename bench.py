@@ -414,7 +414,8 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
     the same hidden state. Reports the block's time and flop rate, the same block captured once
     as a HIP graph and replayed (the host launch cost of its kernels removed), and one sparse
     and one dense layer of the same shapes timed alone (routed tokens/s of the sparse layer; the
-    ratio of the two layers' times; their sum over the block's layers). Informational."""
+    ratio of the two layers' times; their sum over the block's layers), and for the A3K16 block
+    which tokens its sparse layers route (`routing_diagnostics`). Informational."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(seed)
     bf = torch.bfloat16
@@ -467,6 +468,7 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
         t_dense = timed(lambda: xmod.dense_layer_fwd(x, Ls[0], dims, ws))
         n_sparse = w.N1 * w.AK
         n_dense = n_layers - n_sparse
+        routing = routing_diagnostics(xmod, w, Ls, dims, x, x0, bias, ws) if w.AK > 1 else None
         f_block = n_sparse * layer_flops(w, True) + n_dense * layer_flops(w, False)
         out[name] = {"layers": n_layers, "sparse_layers": n_sparse, "block_ms": round(t_block, 4),
                      "block_tflops": round(f_block / (t_block * 1e-3) / 1e12, 1),
@@ -477,11 +479,51 @@ def blocks(xmod, steps=5, warmup=2, seed=7):
                      "sparse_layer_tflops": round(layer_flops(w, True) / (t_sparse * 1e-3) / 1e12, 1),
                      "dense_layer_tflops": round(layer_flops(w, False) / (t_dense * 1e-3) / 1e12, 1),
                      "sparse_over_dense_time": round(t_sparse / t_dense, 4)}
+        if routing:
+            out[name]["routing"] = routing
         del Ls, ws, x, x0
         torch.cuda.empty_cache()
     out["timing"] = ("events around each call (or graph replay), each from the same hidden "
                      "state")
     return out
+
+
+def routing_diagnostics(xmod, w, Ls, dims, x, x0, bias, ws):
+    """Which tokens the stack's sparse layers route (random-initialised weights, synthetic
+    input): the stack walked layer by layer through the single-layer entry points (the same
+    results as the block entry point) with each sparse layer's selection kept. coverage: the
+    share of tokens routed by at least one sparse layer; adjacent_jaccard: the mean, over
+    sequences and adjacent sparse layers, of |S_l & S_l+1| / |S_l | S_l+1|. Beside them the
+    values for independent random choices of a 1/K share per layer, 1 - (1 - 1/K)^n and
+    p / (2 - p), the references the X-MoD review's routing-diagnostics table prints."""
+    import torch
+    x.copy_(x0)
+    idx = torch.empty((w.B, w.k), dtype=torch.int32, device="cuda")
+    masks = []
+    n_in_block = w.AK + 1
+    for i, L in enumerate(Ls):
+        sparse = i >= w.N0 and (i - w.N0) % n_in_block < w.AK
+        if i >= w.N0 and (i - w.N0) % n_in_block == 0:
+            bias.zero_()                                  # the block start's reset
+        if sparse:
+            xmod.sparse_layer_fwd(x, L, dims, w.K, bias, w.tau, w.delta, ws, idx)
+            m = torch.zeros((w.B, w.T), dtype=torch.bool, device="cuda")
+            m.scatter_(1, idx.long(), True)
+            masks.append(m)
+        else:
+            xmod.dense_layer_fwd(x, L, dims, ws)
+    sel = torch.stack(masks)                              # [layers, B, T]
+    coverage = sel.any(0).float().mean().item()
+    inter = (sel[1:] & sel[:-1]).sum(-1).float()
+    union = (sel[1:] | sel[:-1]).sum(-1).float()
+    jac = (inter / union).mean().item()
+    p = 1.0 / w.K
+    n = sel.shape[0]
+    return {"sparse_layers": n, "coverage": round(coverage, 5),
+            "adjacent_jaccard": round(jac, 5),
+            "independent_coverage": round(1.0 - (1.0 - p) ** n, 5),
+            "independent_jaccard": round(p / (2.0 - p), 5),
+            "bias_step": w.delta}
 
 
 def measured_ceilings(w, reps=10):
