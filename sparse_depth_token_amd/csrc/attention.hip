@@ -7,7 +7,8 @@
 // max, rescaled running sum and output), so the k x k score matrix is never stored.
 //
 // Work split: NW = 8 (or 4) waves per workgroup, 32 query rows per wave, key/value tiles of 64
-// rows shared by the workgroup. The register footprint allows two waves per SIMD. Two ways of
+// rows (128 for sequences of 2048 packed rows or more) shared by the workgroup. The register
+// footprint allows two waves per SIMD. Two ways of
 // giving a workgroup its 32 NW query rows, chosen at launch:
 //  * one q-tile of 32 NW packed rows, last tile first in dispatch order: every wave stays busy
 //    to the last key tiles, so each SIMD keeps two waves whose MFMA and softmax work overlap.
@@ -42,10 +43,11 @@ __device__ __forceinline__ void attn_dma16(const void *gsrc, uint16_t *lds_block
                                    0, 0);
 }
 
-template <int HD, int NW_>
+template <int HD, int NW_, int BKV_>
 struct AttnCfg {
-  // NW waves of 32 query rows: a q-tile of 32 NW rows, or a pair of q-tiles of 16 NW rows
-  static constexpr int NW = NW_, BQ = 32 * NW, BQP = 16 * NW, BKV = 64, NT = 64 * NW;
+  // NW waves of 32 query rows: a q-tile of 32 NW rows, or a pair of q-tiles of 16 NW rows;
+  // key/value tiles of BKV rows
+  static constexpr int NW = NW_, BQ = 32 * NW, BQP = 16 * NW, BKV = BKV_, NT = 64 * NW;
   static constexpr int CPR = HD / 8;              // 16-byte chunks per row
   static constexpr int RPB = 64 / CPR;            // rows per 1 KB DMA block
   static constexpr int TILE = BKV * HD;           // elements of one K (or V) tile
@@ -76,7 +78,7 @@ struct FullKV {
   int T = 0;
 };
 
-template <int HD, bool FULLKV, int NW>
+template <int HD, bool FULLKV, int NW, int BKV_ = 64>
 __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__restrict__ qkv, int ldq,
                                                       uint16_t *__restrict__ o, int ldo,
                                                       int k_fixed, int Hq, int Hkv,
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
                                                       const int32_t *__restrict__ seq_len,
                                                       FullKV fkv, float *__restrict__ lse,
                                                       int paired) {
-  using C = AttnCfg<HD, NW>;
+  using C = AttnCfg<HD, NW, BKV_>;
+  constexpr int NB = BKV_ / 32;  // 32-key blocks per tile
   constexpr int BQ = C::BQ, BQP = C::BQP, BKV = C::BKV, KS = HD / 16, NT_HD = HD / 32;
   // Lazy rescaling: the reference maximum M of a lane moves only when a tile's maximum exceeds
   // it by more than 2^RESCALE_LOG2 (log2 units), so weights exp2(x - M) stay below 2^8 and most
@@ -147,17 +150,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
   // DMA: block i of a stage (i < NBLK/2: K, else V) is filled by wave i % 4; lane l lands at
   // byte 16 l, i.e. row RPB * (i mod NBLK/2) + l / CPR, physical chunk l % CPR. The byte
   // offset of a lane's source within a tile is fixed; tiles advance by BKV rows.
-  uint32_t dma_off[C::NDMA];
-  int dma_row[C::NDMA], dma_lc[C::NDMA];
-#pragma unroll
-  for (int n = 0; n < C::NDMA; ++n) {
+  auto dma_row = [&](int n) {
     const int i = C::NW * n + wv;
-    const bool is_v = i >= C::NBLK / 2;
-    const int blk = is_v ? i - C::NBLK / 2 : i;
-    dma_row[n] = C::RPB * blk + lane / C::CPR;
-    dma_lc[n] = (lane % C::CPR) ^ (is_v ? C::vswz(dma_row[n]) : C::kswz(dma_row[n]));
-    dma_off[n] = (uint32_t)dma_row[n] * (uint32_t)ldk * 2u + (uint32_t)dma_lc[n] * 16u;
-  }
+    const int blk = i >= C::NBLK / 2 ? i - C::NBLK / 2 : i;
+    return C::RPB * blk + lane / C::CPR;
+  };
+  auto dma_lc = [&](int n) {
+    const int i = C::NW * n + wv, row = dma_row(n);
+    return (lane % C::CPR) ^ (i >= C::NBLK / 2 ? C::vswz(row) : C::kswz(row));
+  };
   auto issue_tile = [&](int jt, int stage) {
     const size_t tile_bytes = (size_t)jt * BKV * ldk * 2;
     const bool ragged = jt * BKV + BKV > kvlen;  // rows past the sequence read its last row
@@ -166,11 +167,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
       const int i = C::NW * n + wv;
       const bool is_v = i >= C::NBLK / 2;
       const int blk = is_v ? i - C::NBLK / 2 : i;
-      uint32_t off = dma_off[n];
-      if (ragged) {
-        const int row = min(dma_row[n], kvlen - 1 - jt * BKV);
-        off = (uint32_t)row * (uint32_t)ldk * 2u + (uint32_t)dma_lc[n] * 16u;
-      }
+      int row = dma_row(n);
+      if (ragged) row = min(row, kvlen - 1 - jt * BKV);
+      const uint32_t off = (uint32_t)row * (uint32_t)ldk * 2u + (uint32_t)dma_lc(n) * 16u;
       attn_dma16((is_v ? vbase : kbase) + tile_bytes + off,
                  lds + stage + (is_v ? C::TILE : 0) + C::RPB * blk * HD);
     }
@@ -225,19 +224,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
     if (key0 <= q_last_wave) {
       // S^T[key, query] for 64 keys x this wave's 32 queries. The K fragments of the second
       // 32-key block are read while the first block's MFMAs run.
-      f32x16 sacc[2];
+      f32x16 sacc[NB];
       bf16x8 kf[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) kf[s] = *(const bf16x8 *)(Ks + k_off[s]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NB; ++t) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[t][e] = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc[t], 0, 0, 0);
-          if (t == 0) kf[s] = *(const bf16x8 *)(Ks + 32 * HD + k_off[s]);
+          if (t + 1 < NB) kf[s] = *(const bf16x8 *)(Ks + (t + 1) * 32 * HD + k_off[s]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -260,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
       // causal mask only where the tile reaches past the wave's first query or the sequence
       if (key0 + BKV - 1 > q_first_wave || key0 + BKV > kvlen) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NB; ++t)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = key0 + t * 32 + 8 * (e >> 2) + 4 * gq + (e & 3);
@@ -270,7 +269,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
       // online softmax in log2 units (statistics shared by lanes l and l^32)
       float mt = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NB; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[t][e]);
       mt = max_with_xor32(mt) * scale_log2;
@@ -286,7 +285,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
       }
       float psum = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NB; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], scale_log2, -m_ref));
@@ -385,13 +384,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(const uint16_t *__rest
 
 constexpr int ATTN_CUS = 256;  // MI355X
 
-template <int HD, bool FULLKV, int NW>
+template <int HD, bool FULLKV, int NW, int BKV>
 static void launch_nw(dim3 grid, hipStream_t s, const uint16_t *qkv, int ld_qkv, uint16_t *o,
                       int ld_o, int k, int Hq, int Hkv, float scale_log2, const int32_t *seq_off,
                       const int32_t *seq_len, const FullKV &fkv, float *lse, int paired) {
-  hipLaunchKernelGGL((attn_kernel<HD, FULLKV, NW>), grid, dim3(64 * NW), 0, s, qkv, ld_qkv, o,
+  hipLaunchKernelGGL((attn_kernel<HD, FULLKV, NW, BKV>), grid, dim3(64 * NW), 0, s, qkv, ld_qkv, o,
                      ld_o, k, Hq, Hkv, scale_log2, seq_off, seq_len, fkv, lse, paired);
 }
+
+// Key tiles of 128 rows for sequences of at least this many packed rows (half the barriers
+// and per-tile softmax bookkeeping of 64-row tiles: 1 x 8192 rows, 32/8 heads 536 -> 517 us,
+// 1 x 16384, 16/4 heads 1058 -> 1017 us, 2 x 4100, 32/8 heads 298 -> 291 us; at 8 x 512 rows
+// they were 5 % slower). Chosen by the sequence length alone, so that a sequence's result
+// does not depend on the batch it runs in. The Selected-Q/full-KV form keeps 64-row tiles (at
+// 128 its register allocation spills), and so do per-sequence lengths (the host knows only
+// their bound).
+constexpr int ATTN_LONG_KEYS = 2048;
 
 template <bool FULLKV>
 static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, int B, int k,
@@ -408,20 +416,30 @@ static void launch_attn(const uint16_t *qkv, int ld_qkv, uint16_t *o, int ld_o, 
   // as many of them on the CUs. 1024 routed rows, 8 heads: 15.1 -> 12.3 us; 2048 rows, 12 heads
   // 20.9 -> 18.8 us; identical results (each wave's rows see the same key tiles in the same
   // order). At 256 workgroups of eight waves (4096 rows, 16 heads) it gains nothing.
-  if (t256 <= 128) nw = 4;
+  // fixed-length sequences of at least ATTN_LONG_KEYS rows take 128-row key tiles (with
+  // per-sequence lengths k is only their bound, and the tiles stay 64 rows)
+  const bool long_keys = !FULLKV && !seq_len && k >= ATTN_LONG_KEYS;
+  if (t256 <= 128 && !long_keys) nw = 4;
   const int bq = 32 * nw;
   const int units = paired ? ((k + bq / 2 - 1) / (bq / 2) + 1) / 2 : (k + bq - 1) / bq;
   const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)(seq_len ? (units + 3) / 4 : units));
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
-#define XMOD_ATTN_NW(HD_, NW_)                                                                \
-  launch_nw<HD_, FULLKV, NW_>(grid, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv, scale_log2, seq_off, \
-                              seq_len, fkv, lse, paired)
+#define XMOD_ATTN_NW(HD_, NW_, BKV_)                                                          \
+  launch_nw<HD_, FULLKV, NW_, BKV_>(grid, s, qkv, ld_qkv, o, ld_o, k, Hq, Hkv, scale_log2,    \
+                                    seq_off, seq_len, fkv, lse, paired)
+  if constexpr (!FULLKV) {
+    if (long_keys) {  // eight-wave workgroups only (the wave count does not change the bits)
+      if (hd == 128) XMOD_ATTN_NW(128, 8, 128);
+      else XMOD_ATTN_NW(64, 8, 128);
+      return;
+    }
+  }
   if (hd == 128) {
-    if (nw == 8) XMOD_ATTN_NW(128, 8);
-    else XMOD_ATTN_NW(128, 4);
+    if (nw == 8) XMOD_ATTN_NW(128, 8, 64);
+    else XMOD_ATTN_NW(128, 4, 64);
   } else {
-    if (nw == 8) XMOD_ATTN_NW(64, 8);
-    else XMOD_ATTN_NW(64, 4);
+    if (nw == 8) XMOD_ATTN_NW(64, 8, 64);
+    else XMOD_ATTN_NW(64, 4, 64);
   }
 #undef XMOD_ATTN_NW
 }

@@ -299,7 +299,12 @@ def test_gemm_layouts(x, layout, M, N, K, f32, pad):
                                            (1, 64, 2, 2, 64),
                                            # more workgroups than CUs: one 256-row q-tile per
                                            # workgroup, ragged last tiles
-                                           (1, 1100, 64, 8, 64), (2, 700, 48, 6, 128)])
+                                           (1, 1100, 64, 8, 64), (2, 700, 48, 6, 128),
+                                           # sequences of 2048 rows and more: 128-row key
+                                           # tiles (pair split on a small grid, one-tile split
+                                           # on a large one; ragged and exact last tiles)
+                                           (1, 2100, 8, 2, 128), (2, 2048, 4, 4, 64),
+                                           (1, 2500, 48, 8, 128)])
 def test_attention(x, B, k, Hq, Hkv, hd):
     say(f"[attention] B{B} k{k} Hq{Hq} Hkv{Hkv} hd{hd}")
     rng = np.random.default_rng(13)
