@@ -51,7 +51,10 @@ def _attn_terms(Q, Kt, Vt, dO, Hq, Hkv, hd):
                                            (1, 129, 2, 2, 128), (1, 700, 8, 2, 128),
                                            # more dQ workgroups than CUs: one 256-row q-tile
                                            # per workgroup, ragged last tiles
-                                           (1, 600, 96, 8, 64), (2, 300, 96, 12, 128)])
+                                           (1, 600, 96, 8, 64), (2, 300, 96, 12, 128),
+                                           # a forward with 128-row key tiles (2048 rows or
+                                           # more) hands the backward its normaliser
+                                           (1, 2100, 4, 2, 128)])
 def test_attention_backward(x, B, k, Hq, Hkv, hd):
     say(f"[attention bwd] B{B} k{k} Hq{Hq} Hkv{Hkv} hd{hd}")
     rng = np.random.default_rng(21)
