@@ -50,6 +50,10 @@ CASES = {
     "all options, B2 T512 K2 d256": (
         wl.Workload("opt_d", 113, 2, 512, 256, 4, 4, 64, 1024, 2, bias_std=0.1),
         dict(qk=True, theta=500.0, residual=1)),
+    # 2048 routed rows per sequence: the attention's 128-row key tiles after QK-norm and RoPE
+    "QK-norm + RoPE 1e4 + Eq. (6), B1 T8192 K4 d512 GQA 8/2 hd128": (
+        wl.Workload("opt_e", 114, 1, 8192, 512, 8, 2, 128, 1536, 4, bias_std=0.1),
+        dict(qk=True, theta=1e4, residual=1)),
 }
 
 
