@@ -529,7 +529,8 @@ def routing_diagnostics(xmod, w, Ls, dims, x, x0, bias, ws):
 def measured_ceilings(w, reps=10):
     """What this GPU sustains on plain work, beside the vendor peaks the fractions use: HBM copy
     bandwidth (read + write of a 1 GiB buffer by torch's copy kernel), the library's ceiling
-    probes (a streaming read of the same 1 GiB; back-to-back bf16 MFMAs on every SIMD, no memory
+    probes (a streaming read of the same 1 GiB, grid-stride and in per-workgroup chunks with
+    non-temporal loads; back-to-back bf16 MFMAs on every SIMD, no memory
     traffic) and the vendor GEMM library
     (torch.matmul, i.e. hipBLASLt) on the layer's gate/up shape and on 8192^3, bf16. Context
     for the roofline fractions; no part of the layer runs here."""
@@ -555,6 +556,7 @@ def measured_ceilings(w, reps=10):
     # the library's own probes: a streaming read of the same 1 GiB, back-to-back MFMAs
     sums = torch.empty(xmod.PROBE_THREADS, dtype=torch.int32, device="cuda")
     t_reads = {dep: timed(lambda: xmod.probe_read(src, sums, dep)) for dep in (4, 8, 16)}
+    t_chunked = timed(lambda: xmod.probe_read_chunked(src, sums))
     del src
     acc = torch.empty(xmod.PROBE_THREADS, dtype=torch.float32, device="cuda")
     iters = 4096
@@ -565,6 +567,7 @@ def measured_ceilings(w, reps=10):
            "hbm_read_gbs": round(n / min(t_reads.values()) / 1e9, 1),
            "hbm_read_gbs_by_loads_in_flight": {str(dep): round(n / t / 1e9, 1)
                                                for dep, t in t_reads.items()},
+           "hbm_read_chunked_nt_gbs": round(n / t_chunked / 1e9, 1),
            "mfma_bf16_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
     # the same products by the vendor library and by this library's GEMM (xmod_gemm_bf16_nt,
     # plain bf16 store), one after the other on the same operands (N(0, 1), so the matrix

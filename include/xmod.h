@@ -412,10 +412,16 @@ xmod_status xmod_phase_times(float *ms, int32_t n_slots, int32_t *n_calls);
  *   a grid-stride pass, loads_in_flight (4, 8 or 16) independent loads outstanding per thread
  *   (16 * loads_in_flight KB per CU); out[t] = the 32-bit wrap-around sum of the words thread t
  *   read, so the sum over t equals that of every 32-bit word of src. INVALID_ARG: NULL pointer,
- *   bytes 0 or not a multiple of 16, loads_in_flight not 4, 8 or 16. */
+ *   bytes 0 or not a multiple of 16, loads_in_flight not 4, 8 or 16.
+ * xmod_probe_read_chunked: the same read and the same out, but each of the 1024 workgroups reads
+ *   its own contiguous 1/1024 share of src with non-temporal 16-byte loads (four 4 KB blocks of
+ *   the share in flight), the faster way to stream a buffer larger than the last-level cache.
+ *   Its lines are not kept by the caches, so unlike xmod_probe_read it does not flush them.
+ *   INVALID_ARG: NULL pointer, bytes 0 or not a multiple of 16, src not 16-byte aligned. */
 xmod_status xmod_probe_mfma(float *out, int32_t iters, void *stream);
 xmod_status xmod_probe_read(const void *src, size_t bytes, int32_t loads_in_flight, uint32_t *out,
                             void *stream);
+xmod_status xmod_probe_read_chunked(const void *src, size_t bytes, uint32_t *out, void *stream);
 
 const char *xmod_status_string(xmod_status st);
 int32_t xmod_last_hip_error(void);

@@ -5,6 +5,11 @@
 //  * HBM read: a grid-stride pass of 16-byte loads over a buffer, 4, 8 or 16 of them in flight
 //    per thread, every 32-bit word added into a per-thread sum (kept, so that nothing is
 //    skipped; the sums are checkable on the host).
+//  * HBM read, chunked: every workgroup reads its own contiguous share of the buffer with
+//    non-temporal 16-byte loads (the nt bit: the caches do not keep the lines), four 4 KB
+//    blocks of the share in flight per workgroup. This is the faster way to stream a buffer
+//    larger than the last-level cache; the grid-stride form is the one a cache flush uses,
+//    since its lines do displace what the caches held.
 #include "common.h"
 
 namespace xmod {
@@ -56,6 +61,32 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const uint4 *__restrict
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef unsigned int probe_u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void probe_read_chunked_kernel(const uint4 *__restrict__ src,
+                                                                 int64_t n16,
+                                                                 uint32_t *__restrict__ out) {
+  constexpr int D = 4;
+  const probe_u32x4 *p = (const probe_u32x4 *)src;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  uint32_t s = 0;
+  int64_t i = lo + threadIdx.x;
+  for (; i + (D - 1) * 256 < hi; i += D * 256) {
+    probe_u32x4 v[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) v[j] = __builtin_nontemporal_load(p + i + j * 256);
+#pragma unroll
+    for (int j = 0; j < D; ++j) s += v[j][0] + v[j][1] + v[j][2] + v[j][3];
+  }
+  for (; i < hi; i += 256) {
+    const probe_u32x4 v = __builtin_nontemporal_load(p + i);
+    s += v[0] + v[1] + v[2] + v[3];
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 hipError_t launch_probe_mfma(float *out, int iters, hipStream_t s) {
   hipLaunchKernelGGL(probe_mfma_kernel, dim3(PROBE_WGS), dim3(256), 0, s, out, iters);
   return hipGetLastError();
@@ -71,6 +102,12 @@ hipError_t launch_probe_read(const void *src, size_t bytes, int depth, uint32_t 
     hipLaunchKernelGGL(probe_read_kernel<8>, dim3(PROBE_WGS), dim3(256), 0, s, p, n16, out);
   else
     hipLaunchKernelGGL(probe_read_kernel<4>, dim3(PROBE_WGS), dim3(256), 0, s, p, n16, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_read_chunked(const void *src, size_t bytes, uint32_t *out, hipStream_t s) {
+  hipLaunchKernelGGL(probe_read_chunked_kernel, dim3(PROBE_WGS), dim3(256), 0, s,
+                     (const uint4 *)src, (int64_t)(bytes / 16), out);
   return hipGetLastError();
 }
 

@@ -333,6 +333,7 @@ xmod_status route_topk_into(const void *x, const xmod_layer *L, const xmod_dims 
 namespace xmod {
 // ceiling probes (probe.hip)
 hipError_t launch_probe_mfma(float *out, int iters, hipStream_t s);
+hipError_t launch_probe_read_chunked(const void *src, size_t bytes, uint32_t *out, hipStream_t s);
 hipError_t launch_probe_read(const void *src, size_t bytes, int depth, uint32_t *out,
                              hipStream_t s);
 }  // namespace xmod
@@ -683,6 +684,13 @@ xmod_status xmod_probe_read(const void *src, size_t bytes, int32_t loads_in_flig
   if (loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16)
     return XMOD_ERR_INVALID_ARG;
   XMOD_HIP(launch_probe_read(src, bytes, loads_in_flight, out, (hipStream_t)stream));
+  return XMOD_OK;
+}
+
+xmod_status xmod_probe_read_chunked(const void *src, size_t bytes, uint32_t *out, void *stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0)
+    return XMOD_ERR_INVALID_ARG;
+  XMOD_HIP(launch_probe_read_chunked(src, bytes, out, (hipStream_t)stream));
   return XMOD_OK;
 }
 

@@ -34,7 +34,7 @@ EXPORTED = ["xmod_workspace_bytes", "xmod_route_topk", "xmod_topk_workspace_byte
             "xmod_rmsnorm_rows", "xmod_gemm_bf16_nt", "xmod_gemm_bf16", "xmod_attention_fwd",
             "xmod_attention_fwd_lse", "xmod_attention_bwd",
             "xmod_phase_timing_enable", "xmod_phase_timing_slots", "xmod_phase_times",
-            "xmod_probe_mfma", "xmod_probe_read",
+            "xmod_probe_mfma", "xmod_probe_read", "xmod_probe_read_chunked",
             "xmod_status_string",
             "xmod_last_hip_error"]
 
@@ -103,6 +103,7 @@ _sig = {
                               _vp]),
     "xmod_attention_fwd": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "xmod_probe_read": (_i32, [_vp, _sz, _i32, _vp, _vp]),
+    "xmod_probe_read_chunked": (_i32, [_vp, _sz, _vp, _vp]),
     "xmod_phase_timing_enable": (None, [_i32]),
     "xmod_phase_timing_slots": (None, [ctypes.c_uint32]),
     "xmod_phase_times": (_i32, [_P(_f32), _i32, _P(_i32)]),
@@ -563,6 +564,17 @@ def probe_read(src, out, loads_in_flight=4, stream=None):
     op = _arg(out, "out", _I32, at_least=PROBE_THREADS)
     _check(lib.xmod_probe_read(sp, nbytes, int(loads_in_flight), op, _stream(stream)),
            "xmod_probe_read")
+    return nbytes
+
+
+def probe_read_chunked(src, out, stream=None):
+    """The same read as probe_read (same sums in out), each workgroup streaming its own
+    contiguous share of src with non-temporal loads. Returns the bytes read."""
+    nbytes = src.numel() * src.element_size()
+    sp = _arg(src, "src", src.dtype)
+    op = _arg(out, "out", _I32, at_least=PROBE_THREADS)
+    _check(lib.xmod_probe_read_chunked(sp, nbytes, op, _stream(stream)),
+           "xmod_probe_read_chunked")
     return nbytes
 
 

@@ -258,6 +258,10 @@ def test_probes_reject_before_launch(x):
     assert L.xmod_probe_read(FAKE, 24, 4, FAKE, None) == x.ERR_INVALID_ARG
     assert L.xmod_probe_read(FAKE, 64, 4, None, None) == x.ERR_INVALID_ARG
     assert L.xmod_probe_read(FAKE, 64, 5, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read_chunked(None, 64, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read_chunked(FAKE, 0, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read_chunked(FAKE, 24, FAKE, None) == x.ERR_INVALID_ARG
+    assert L.xmod_probe_read_chunked(FAKE, 64, None, None) == x.ERR_INVALID_ARG
 
 
 def test_operand_size_limits_reject_before_launch(x):
