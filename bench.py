@@ -558,6 +558,22 @@ def measured_ceilings(w, reps=10):
     t_reads = {dep: timed(lambda: xmod.probe_read(src, sums, dep)) for dep in (4, 8, 16)}
     t_chunked = timed(lambda: xmod.probe_read_chunked(src, sums))
     del src
+    # the same chunked read over a buffer of the layer's hidden-state size, each rep after the
+    # cold-step flush: the bare-read time of exactly the bytes the router streams
+    xb = w.B * w.T * w.d * 2
+    xsrc = torch.ones(xb, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    t_x = []
+    for _ in range(reps + 1):
+        xmod.probe_read(flush, sums)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        xmod.probe_read_chunked(xsrc, sums)
+        e1.record()
+        torch.cuda.synchronize()
+        t_x.append(e0.elapsed_time(e1) * 1e-3)
+    t_x = sorted(t_x[1:])[reps // 2]
+    del xsrc, flush
     acc = torch.empty(xmod.PROBE_THREADS, dtype=torch.float32, device="cuda")
     iters = 4096
     t_mfma = timed(lambda: xmod.probe_mfma(acc, iters))
@@ -568,6 +584,8 @@ def measured_ceilings(w, reps=10):
            "hbm_read_gbs_by_loads_in_flight": {str(dep): round(n / t / 1e9, 1)
                                                for dep, t in t_reads.items()},
            "hbm_read_chunked_nt_gbs": round(n / t_chunked / 1e9, 1),
+           "hbm_read_chunked_nt_x_bytes": {"bytes": xb, "us": round(t_x * 1e6, 1),
+                                           "gbs": round(xb / t_x / 1e9, 1)},
            "mfma_bf16_tflops": round(mfma_flops / t_mfma / 1e12, 1)}
     # the same products by the vendor library and by this library's GEMM (xmod_gemm_bf16_nt,
     # plain bf16 store), one after the other on the same operands (N(0, 1), so the matrix
@@ -590,7 +608,9 @@ def measured_ceilings(w, reps=10):
     out["this_library_gemm_tflops"] = ours
     out["note"] = ("torch copy (read + write), the library's streaming-read probe (4, 8 or 16 "
                    "16-byte loads in flight per thread, 1024 threads per CU; the best is "
-                   "hbm_read_gbs) and back-to-back MFMA probe, and torch.matmul (vendor library) "
+                   "hbm_read_gbs), the chunked non-temporal read of 1 GiB and of the hidden "
+                   "state's bytes after the cold-step flush (hbm_read_chunked_nt_*), the "
+                   "back-to-back MFMA probe, and torch.matmul (vendor library) "
                    "beside this library's plain GEMM on the same operands, on this GPU; the "
                    "roofline fractions use the vendor peaks (8 TB/s, 2.5 PFLOP/s)")
     return out
